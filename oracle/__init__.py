@@ -1,0 +1,181 @@
+"""CPU oracle of the fused multi-column embedding stage -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  The product path (the HIP library and its binding) never touches it.
+
+`oracle.c` holds the arithmetic (plain scalar loops, fp64 accumulation); this
+module marshals numpy arrays into it with ctypes.  `table.py` holds the keyed
+table model (frequency-filtered admission) in numpy.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+
+ROW_DROPPED = -1
+ROW_DEFAULT = -2
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (plain C, no fused multiply-add contraction)."""
+    if os.environ.get("ORACLE_LIB"):
+        return _LIB                      # a prebuilt variant (mutation tests)
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-std=c11", "-Wall",
+                               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Col(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("pool", C.c_int32), ("dtype", C.c_int32),
+                ("dim", C.c_int32), ("rows", C.c_int64), ("id_lo", C.c_int64),
+                ("id_hi", C.c_int64), ("boundaries", C.c_void_p), ("n_boundaries", C.c_int64),
+                ("weights", C.c_void_p), ("state", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = C.CDLL(_LIB)
+        L.oracle_splitmix64.restype = C.c_uint64
+        L.oracle_splitmix64.argtypes = [C.c_uint64]
+        L.oracle_splitmix64_array.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+        L.oracle_hash_mod.restype = C.c_int64
+        L.oracle_hash_mod.argtypes = [C.c_uint64, C.c_int64]
+        L.oracle_bucketize.restype = C.c_int64
+        L.oracle_bucketize.argtypes = [C.c_void_p, C.c_int64, C.c_float]
+        L.oracle_double_to_bf16.restype = C.c_uint16
+        L.oracle_double_to_bf16.argtypes = [C.c_double]
+        L.oracle_adagrad_elem.restype = C.c_double
+        L.oracle_adagrad_elem.argtypes = [C.c_double] * 5 + [C.POINTER(C.c_double)]
+        L.oracle_row.restype = C.c_int64
+        L.oracle_row.argtypes = [C.POINTER(_Col), C.c_int64, C.c_float, C.c_int32]
+        L.oracle_forward.restype = C.c_int64
+        L.oracle_forward.argtypes = [C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 8
+        L.oracle_backward.restype = C.c_int64
+        L.oracle_backward.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 5
+                                      + [C.c_int32, C.c_double, C.c_double]
+                                      + [C.c_void_p] * 4 + [C.c_int64])
+        L.oracle_init_row.argtypes = [C.c_int64, C.c_int32, C.c_double, C.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+# ------------------------------------------------------------------ scalars
+
+def splitmix64(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x).astype(np.uint64))
+    out = np.empty_like(x)
+    lib().oracle_splitmix64_array(_p(x), _p(out), x.size)
+    return out
+
+
+def hash_mod(id_bits: int, rows: int) -> int:
+    return int(lib().oracle_hash_mod(C.c_uint64(id_bits & (2**64 - 1)), rows))
+
+
+def bucketize(boundaries: np.ndarray, x: float) -> int:
+    b = np.ascontiguousarray(boundaries, dtype=np.float32)
+    return int(lib().oracle_bucketize(_p(b), b.size, C.c_float(x)))
+
+
+def double_to_bf16(v: float) -> int:
+    return int(lib().oracle_double_to_bf16(float(v)))
+
+
+def adagrad_elem(e, a, g, lr, eps):
+    a_out = C.c_double()
+    e2 = lib().oracle_adagrad_elem(e, a, g, lr, eps, C.byref(a_out))
+    return e2, a_out.value
+
+
+def init_row(key: int, dim: int, std: float) -> np.ndarray:
+    out = np.empty(dim, dtype=np.float32)
+    lib().oracle_init_row(int(key), dim, float(std), _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ columns
+
+class Columns:
+    """Column descriptors + host tables (numpy) in the oracle's C layout.
+
+    weights[c]: float32 [rows, dim] or uint16 (bf16 bits) [rows, dim]; states[c]:
+    float32 [rows, dim] Adagrad accumulator or None.  Arrays are used in place."""
+
+    def __init__(self, cols, weights, states=None):
+        self.cols = cols
+        self.weights = [None if w is None else np.ascontiguousarray(w) for w in weights]
+        self.states = [None if (states is None or s is None) else np.ascontiguousarray(s)
+                       for s in (states or [None] * len(cols))]
+        self.bounds = [None if c.boundaries is None else
+                       np.ascontiguousarray(c.boundaries, dtype=np.float32) for c in cols]
+        arr = (_Col * len(cols))()
+        for i, c in enumerate(cols):
+            w = self.weights[i]
+            if w is not None:
+                assert w.shape == (c.rows, c.dim), (w.shape, c.rows, c.dim)
+                assert w.dtype == (np.uint16 if c.dtype == 1 else np.float32)
+            arr[i] = _Col(c.kind, c.pool, c.dtype, c.dim, c.rows, c.id_lo, c.id_hi,
+                          _p(self.bounds[i]), 0 if self.bounds[i] is None else self.bounds[i].size,
+                          _p(w), _p(self.states[i]))
+        self.arr = arr
+        self.sum_dim = int(sum(c.dim for c in cols))
+        self.max_dim = int(max(c.dim for c in cols))
+
+
+def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=None):
+    """Returns (Y fp32 [B, sumD], Ybound fp64 [B, sumD], bag_n int32 [C*B], rows int32 [N])."""
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = int(offsets[-1])
+    ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int64)
+    fvals = None if fvals is None else np.ascontiguousarray(fvals, dtype=np.float32)
+    keyed_rows = None if keyed_rows is None else np.ascontiguousarray(keyed_rows, dtype=np.int32)
+    Y = np.zeros((B, cols.sum_dim), dtype=np.float32)
+    Yb = np.zeros((B, cols.sum_dim), dtype=np.float64)
+    bag_n = np.zeros(len(cols.cols) * B, dtype=np.int32)
+    rows = np.zeros(max(n, 1), dtype=np.int32)
+    lib().oracle_forward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
+                         _p(keyed_rows), _p(Y), _p(Yb), _p(bag_n), _p(rows))
+    return Y, Yb, bag_n, rows[:n]
+
+
+def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows=None,
+             opt: int = 0, lr: float = 0.0, eps: float = 0.0):
+    """Gradient w.r.t. touched rows and the row update `opt` (applied in place to
+    cols.weights / cols.states).  Returns (ucol int32 [U], urow int64 [U],
+    ugrad fp64 [U, maxD], ubound fp64 [U, maxD])."""
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = int(offsets[-1])
+    ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int64)
+    fvals = None if fvals is None else np.ascontiguousarray(fvals, dtype=np.float32)
+    keyed_rows = None if keyed_rows is None else np.ascontiguousarray(keyed_rows, dtype=np.int32)
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    assert G.shape == (B, cols.sum_dim)
+    cap = max(n, 1)
+    ucol = np.zeros(cap, dtype=np.int32)
+    urow = np.zeros(cap, dtype=np.int64)
+    ug = np.zeros((cap, cols.max_dim), dtype=np.float64)
+    ub = np.zeros((cap, cols.max_dim), dtype=np.float64)
+    U = lib().oracle_backward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
+                              _p(keyed_rows), _p(G), opt, lr, eps, _p(ucol), _p(urow), _p(ug),
+                              _p(ub), cap)
+    assert U >= 0
+    return ucol[:U], urow[:U], ug[:U], ub[:U]

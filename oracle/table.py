@@ -1,0 +1,129 @@
+"""Keyed-table model of the oracle -- TEST INFRASTRUCTURE ONLY.
+
+Collisionless int64-keyed embedding table with a frequency filter, after the
+Monolith paper, Sec. 2.1 "Hash Table": distinct IDs never share an embedding, and
+an ID is admitted only once its occurrence count reaches a tunable threshold.
+
+The model keeps what the method defines and nothing about slot placement:
+  key -> (occurrence count, admitted?, row values).
+Step rule (batch-level, independent of thread order):
+  m_k  = occurrences of valid key k (k >= 1) in the step, repeats included;
+  present keys: count += m_k; absent keys: inserted with count = m_k;
+  a key without a row whose count reaches the threshold is admitted now and gets
+  a fresh row (oracle_init_row); every occurrence of an admitted key returns its
+  row, the others return DEFAULT (a zero row that counts in a mean).
+  Keys < 1 are dropped.  Prepopulated keys are admitted with count 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import ROW_DEFAULT, ROW_DROPPED, init_row
+
+
+class TableFull(RuntimeError):
+    pass
+
+
+class OracleTable:
+    def __init__(self, capacity: int, dim: int, threshold: int, init_std: float,
+                 prepop_keys=None, prepop_rows=None):
+        """prepop_rows: array-like [n, dim] or a callable idx -> rows (lazy, so a
+        large prepopulated pool can stay wherever it lives)."""
+        self.capacity, self.dim, self.threshold, self.init_std = capacity, dim, threshold, init_std
+        if prepop_keys is None:
+            prepop_keys = np.empty(0, dtype=np.int64)
+        pk = np.asarray(prepop_keys, dtype=np.int64)
+        order = np.argsort(pk, kind="stable")
+        self.keys = pk[order]
+        if self.keys.size and np.any(self.keys[1:] == self.keys[:-1]):
+            raise ValueError("duplicate prepopulated keys")
+        self.count = np.zeros(self.keys.size, dtype=np.int64)
+        self.admitted = np.ones(self.keys.size, dtype=bool)
+        self.prepop_idx = order.astype(np.int64)         # index into the prepop rows
+        self._prepop_rows = prepop_rows
+        self.vals = {}                                    # key -> row values (new or updated)
+        if self.keys.size > capacity:
+            raise TableFull("prepopulation exceeds capacity")
+
+    # ------------------------------------------------------------- queries
+    def _find(self, k: np.ndarray):
+        i = np.searchsorted(self.keys, k)
+        i = np.minimum(i, max(self.keys.size - 1, 0))
+        hit = (self.keys.size > 0) & (self.keys[i] == k) if self.keys.size else np.zeros(k.shape, bool)
+        return i, hit
+
+    def row_values(self, keys) -> np.ndarray:
+        keys = np.asarray(keys, dtype=np.int64)
+        out = np.zeros((keys.size, self.dim), dtype=np.float32)
+        idx, hit = self._find(keys)
+        need = []
+        for j, k in enumerate(keys.tolist()):
+            if k in self.vals:
+                out[j] = self.vals[k]
+            elif hit[j] and self.admitted[idx[j]]:
+                need.append(j)
+        if need:
+            src = self.prepop_idx[idx[need]]
+            pr = self._prepop_rows
+            vals = pr(src) if callable(pr) else np.asarray(pr)[src]
+            out[need] = np.asarray(vals, dtype=np.float32)
+        return out
+
+    def state(self, keys):
+        """(present, count, admitted) for each key."""
+        keys = np.asarray(keys, dtype=np.int64)
+        idx, hit = self._find(keys)
+        cnt = np.where(hit, self.count[idx] if self.keys.size else 0, 0)
+        adm = np.where(hit, self.admitted[idx] if self.keys.size else False, False)
+        return hit, cnt, adm
+
+    # ---------------------------------------------------------------- step
+    def step(self, keys):
+        """One lookup-or-insert over a batch of keys.  Returns (uk, admitted_uk):
+        the step's distinct valid keys and whether each is admitted after it."""
+        keys = np.asarray(keys, dtype=np.int64)
+        valid = keys >= 1
+        uk, m = np.unique(keys[valid], return_counts=True)
+        idx, hit = self._find(uk)
+        new = uk[~hit]
+        if self.keys.size + new.size > self.capacity:
+            raise TableFull(f"{new.size} new keys, {self.capacity - self.keys.size} free slots")
+        # count the present keys
+        if self.keys.size:
+            np.add.at(self.count, idx[hit], m[hit])
+        # insert the absent keys with their counts
+        if new.size:
+            keys2 = np.concatenate([self.keys, new])
+            cnt2 = np.concatenate([self.count, m[~hit]])
+            adm2 = np.concatenate([self.admitted, np.zeros(new.size, dtype=bool)])
+            pidx2 = np.concatenate([self.prepop_idx, np.full(new.size, -1, dtype=np.int64)])
+            order = np.argsort(keys2, kind="stable")
+            self.keys, self.count = keys2[order], cnt2[order]
+            self.admitted, self.prepop_idx = adm2[order], pidx2[order]
+        # admit whatever reached the threshold and has no row yet
+        idx, hit = self._find(uk)
+        assert hit.all()
+        fresh = (~self.admitted[idx]) & (self.count[idx] >= self.threshold)
+        for k in uk[fresh].tolist():
+            self.vals[k] = init_row(k, self.dim, self.init_std)
+        self.admitted[idx[fresh]] = True
+        return uk, self.admitted[idx]
+
+    def resolve(self, keys):
+        """Per-position rows into a compact local pool for the oracle's forward:
+        returns (keyed_rows int32 [n], pool_keys int64 [P], pool fp32 [P, dim])."""
+        keys = np.asarray(keys, dtype=np.int64)
+        valid = keys >= 1
+        _, _, adm = self.state(keys)
+        use = valid & adm
+        pool_keys, inv = np.unique(keys[use], return_inverse=True)
+        rows = np.full(keys.size, ROW_DROPPED, dtype=np.int32)
+        rows[valid & ~adm] = ROW_DEFAULT
+        rows[use] = inv.astype(np.int32)
+        return rows, pool_keys, self.row_values(pool_keys)
+
+    def store(self, pool_keys, pool_rows):
+        """Write updated row values back (after an oracle row update)."""
+        for k, r in zip(np.asarray(pool_keys).tolist(), np.asarray(pool_rows)):
+            self.vals[int(k)] = np.array(r, dtype=np.float32)
