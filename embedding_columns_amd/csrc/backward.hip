@@ -1,0 +1,623 @@
+// backward.hip -- deduplicate touched rows, segment-sum their gradients, update rows.
+//
+// The gradient of the pooled output with respect to a table row u is the sum
+// over the positions r that looked u up of w_r * G[s(r), :] (RecIS Sec. 3.2,
+// Algorithm 1, backward half).  Instead of RecIS's wave-merge + global atomics,
+// the contributions are grouped by a stable LSD radix sort of their 32-bit row
+// keys (key = row_base_c + row), which yields the distinct touched rows (the
+// "Reduce-ID" of RecIS Fig. 3) in ascending order and a fixed summation order,
+// so gradients and updated weights are deterministic run to run.
+//
+//   pass p (ceil(key_bits / 8) passes):
+//     rs_hist     per-block digit histograms
+//     rs_scan     per-digit exclusive scan over blocks (+ digit totals)
+//     rs_scatter  per-wavefront stable ranking by ballot matching, LDS-local
+//                 digit sort, coalesced scatter of each digit run
+//   uq_count / uq_scan / uq_write   segment heads -> unique keys + segment starts
+//   seg_apply   one tile of sorted contributors per wavefront: gather fp32
+//               G slices scaled by the pooling weight, sum per segment in
+//               registers (split segments through LDS / last-arriver tickets
+//               as in the forward), then EMIT, SGD or Adagrad on the row.
+#include <algorithm>
+#include <string>
+
+#include "device.h"
+
+namespace emb {
+
+// ---------------------------------------------------------------- radix sort
+
+__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
+                                                 int shift, uint32_t *__restrict__ hist,
+                                                 int64_t nblk)
+{
+    __shared__ uint32_t h[kRadix];
+    const int t = threadIdx.x;
+    h[t] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+#pragma unroll 4
+    for (int i = 0; i < kSortItems; i++) {
+        const int64_t idx = base + (int64_t)i * kBlock + t;
+        if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & (kRadix - 1)], 1u);
+    }
+    __syncthreads();
+    hist[(int64_t)t * nblk + blockIdx.x] = h[t];
+}
+
+// exclusive scan of 256 values held one per thread; returns the total
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t &excl)
+{
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) tmp[w] = x;
+    __syncthreads();
+    uint32_t wpre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; i++) {
+        const uint32_t s = tmp[i];
+        wpre += (i < w) ? s : 0u;
+        tot += s;
+    }
+    excl = wpre + x - v;
+    __syncthreads();
+    return tot;
+}
+
+// one block per digit: exclusive scan of hist[d][0..nblk) in place, total -> dtot[d]
+__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
+                                                 uint32_t *__restrict__ dtot)
+{
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    uint32_t *h = hist + (int64_t)blockIdx.x * nblk;
+    uint32_t carry = 0;
+    for (int64_t s = 0; s < nblk; s += kBlock) {
+        const int64_t i = s + threadIdx.x;
+        const uint32_t v = i < nblk ? h[i] : 0u;
+        uint32_t ex;
+        const uint32_t tot = block_exclusive_scan(v, tmp, ex);
+        if (i < nblk) h[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) dtot[blockIdx.x] = carry;
+}
+
+struct SortLds {
+    uint32_t skey[kSortTile];
+    uint32_t sval[kSortTile];
+    uint32_t run[kWavesPerBlock][kRadix];   // per-wave running digit counts
+    uint32_t lpre[kRadix];                  // block-local digit prefix
+    uint32_t gbase[kRadix];                 // global destination of digit runs
+    uint32_t tmp[kWavesPerBlock];
+};
+
+__global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict__ kin,
+                                                    const uint32_t *__restrict__ vin,
+                                                    uint32_t *__restrict__ kout,
+                                                    uint32_t *__restrict__ vout, int64_t n,
+                                                    int shift, const uint32_t *__restrict__ hist,
+                                                    const uint32_t *__restrict__ dtot, int64_t nblk)
+{
+    __shared__ SortLds S;
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int cnt = (int)min<int64_t>(kSortTile, n - base);
+
+    // digit offsets: global prefix over digits + this block's offset within each digit
+    uint32_t dex;
+    block_exclusive_scan(dtot[t], S.tmp, dex);
+    S.gbase[t] = dex + hist[(int64_t)t * nblk + blockIdx.x];
+    for (int i = 0; i < kWavesPerBlock; i++) S.run[i][t] = 0;
+    __syncthreads();
+
+    // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
+    // so (wave, j, lane) order is index order and the ranking below is stable
+    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kSortItems; j++) {
+        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
+        const bool in = li < cnt;
+        key[j] = in ? kin[base + li] : 0u;
+        val[j] = in ? vin[base + li] : 0u;
+        const uint32_t d = (key[j] >> shift) & (kRadix - 1);
+        uint64_t peers = __ballot(in);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; b++) {
+            const uint64_t m = __ballot((d >> b) & 1u);
+            peers &= ((d >> b) & 1u) ? m : ~m;
+        }
+        const uint32_t before = S.run[w][d];
+        rank[j] = before + (uint32_t)__popcll(peers & lt_mask);
+        const bool leader = in && (peers >> lane) == 1ull;   // highest lane of its digit group
+        wave_sync();
+        if (leader) S.run[w][d] = before + (uint32_t)__popcll(peers);
+        wave_sync();
+    }
+    __syncthreads();
+    // block-local digit histogram -> local prefix; per-wave offsets inside each digit
+    {
+        uint32_t tot = 0, woff[kWavesPerBlock];
+#pragma unroll
+        for (int i = 0; i < kWavesPerBlock; i++) {
+            woff[i] = tot;
+            tot += S.run[i][t];
+        }
+        uint32_t lex;
+        block_exclusive_scan(tot, S.tmp, lex);
+        S.lpre[t] = lex;
+#pragma unroll
+        for (int i = 0; i < kWavesPerBlock; i++) S.run[i][t] = lex + woff[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSortItems; j++) {
+        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
+        if (li < cnt) {
+            const uint32_t d = (key[j] >> shift) & (kRadix - 1);
+            const uint32_t lp = S.run[w][d] + rank[j];
+            S.skey[lp] = key[j];
+            S.sval[lp] = val[j];
+        }
+    }
+    __syncthreads();
+    // write each digit run contiguously
+    for (int lp = t; lp < cnt; lp += kBlock) {
+        const uint32_t k = S.skey[lp];
+        const uint32_t d = (k >> shift) & (kRadix - 1);
+        const uint32_t dst = S.gbase[d] + (uint32_t)lp - S.lpre[d];
+        kout[dst] = k;
+        vout[dst] = S.sval[lp];
+    }
+}
+
+// -------------------------------------------------------------- unique rows
+
+__global__ __launch_bounds__(kBlock) void uq_count(const uint32_t *__restrict__ k, int64_t n,
+                                                  uint32_t total_rows, uint32_t *__restrict__ ucnt,
+                                                  uint32_t *__restrict__ misc)
+{
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
+    uint32_t c = 0;
+    for (int j = 0; j < kSortItems; j++) {
+        const int64_t i = base + j;
+        if (i >= n) break;
+        const uint32_t x = k[i];
+        const uint32_t p = i > 0 ? k[i - 1] : 0xFFFFFFFFu;
+        c += (x < total_rows) && (i == 0 || p != x);
+        // the first sentinel key marks the end of the valid contributors
+        if (x >= total_rows && (i == 0 || p < total_rows)) misc[0] = (uint32_t)i;
+        if (i == n - 1 && x < total_rows) misc[0] = (uint32_t)n;
+    }
+    uint32_t ex;
+    const uint32_t tot = block_exclusive_scan(c, tmp, ex);
+    if (t == 0) ucnt[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kBlock) void uq_scan(const uint32_t *__restrict__ ucnt, int64_t nblk,
+                                                 uint32_t *__restrict__ uscan,
+                                                 uint32_t *__restrict__ misc, int64_t *n_uniq,
+                                                 int64_t *stats)
+{
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    uint32_t carry = 0;
+    for (int64_t s = 0; s < nblk; s += kBlock) {
+        const int64_t i = s + threadIdx.x;
+        const uint32_t v = i < nblk ? ucnt[i] : 0u;
+        uint32_t ex;
+        const uint32_t tot = block_exclusive_scan(v, tmp, ex);
+        if (i < nblk) uscan[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        misc[1] = carry;
+        if (n_uniq) *n_uniq = carry;
+        if (stats) atomicAdd((unsigned long long *)&stats[EMB_STAT_UNIQUE], (unsigned long long)carry);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void uq_write(const uint32_t *__restrict__ k, int64_t n,
+                                                  uint32_t total_rows,
+                                                  const uint32_t *__restrict__ uscan,
+                                                  const uint32_t *__restrict__ misc,
+                                                  uint32_t *__restrict__ seg,
+                                                  uint32_t *__restrict__ ukeys,
+                                                  uint32_t *__restrict__ user_keys)
+{
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
+    uint32_t c = 0;
+    for (int j = 0; j < kSortItems; j++) {
+        const int64_t i = base + j;
+        if (i >= n) break;
+        const uint32_t x = k[i];
+        c += (x < total_rows) && (i == 0 || k[i - 1] != x);
+    }
+    uint32_t ex;
+    block_exclusive_scan(c, tmp, ex);
+    uint32_t u = uscan[blockIdx.x] + ex;
+    for (int j = 0; j < kSortItems; j++) {
+        const int64_t i = base + j;
+        if (i >= n) break;
+        const uint32_t x = k[i];
+        if ((x < total_rows) && (i == 0 || k[i - 1] != x)) {
+            seg[u] = (uint32_t)i;
+            ukeys[u] = x;
+            if (user_keys) user_keys[u] = x;
+            u++;
+        }
+    }
+    if (blockIdx.x == 0 && t == 0) seg[misc[1]] = misc[0];   // seg[U] = number of valid contributors
+}
+
+// ------------------------------------------------------- segment-sum + apply
+
+struct BwdArgs {
+    const DevCol *cols;
+    const uint32_t *row_base;   // [C + 1]
+    int32_t C, B, sumD, maxD, T, opt;
+    float lr, eps;
+    int64_t ntiles;
+    const float *G;
+    const uint32_t *sval;       // sorted bags
+    const int32_t *bag_n;
+    const uint32_t *seg;        // [U + 1]
+    const uint32_t *ukeys;      // [U]
+    const uint32_t *misc;       // [0] = valid contributors, [1] = U
+    float *ugrads;              // EMIT output or NULL
+    float *part;
+    int32_t *pcnt;
+    uint32_t *tick;
+};
+
+struct BwdLds {
+    int32_t smp[kTileMax];      // sample of each contributor
+    float wt[kTileMax];         // pooling weight of each contributor
+    uint32_t seg[kOffCap];      // window of segment starts
+    float part[2][kWave][4];
+    int32_t hseg[kWave], hpass[kWave], tseg[kWave];
+};
+
+struct BTile {
+    int64_t k;
+    int t0, t1, uf, ul, wb, wn;
+};
+
+__device__ __forceinline__ int segat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
+{
+    const unsigned i = (unsigned)(u - t.wb);
+    return (int)(i < (unsigned)t.wn ? L.seg[i] : a.seg[u]);
+}
+
+__device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const BTile &t, int p)
+{
+    int lo = t.uf, hi = t.ul + 1;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (segat(a, L, t, mid) <= p) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// the finished gradient g (4 fp32 per lane) of unique row u: emit or update
+__device__ __forceinline__ void seg_out(const BwdArgs &a, const DevCol &col, int c, int u,
+                                       const float (&g)[4], int q, bool qa)
+{
+    if (!qa) return;
+    if (a.opt == EMB_OPT_EMIT) {
+        if (a.ugrads)
+            *reinterpret_cast<float4 *>(a.ugrads + (int64_t)u * a.maxD + q * 4) =
+                make_float4(g[0], g[1], g[2], g[3]);
+        return;
+    }
+    const int64_t r = (int64_t)(a.ukeys[u] - col.row_base);
+    const int64_t e = r * col.dim + q * 4;
+    float w[4];
+    if (col.dtype == EMB_BF16) {
+        const uint2 raw = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(col.weights) + e);
+        w[0] = bf16_lo(raw.x); w[1] = bf16_hi(raw.x); w[2] = bf16_lo(raw.y); w[3] = bf16_hi(raw.y);
+    } else {
+        const float4 raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e);
+        w[0] = raw.x; w[1] = raw.y; w[2] = raw.z; w[3] = raw.w;
+    }
+    if (a.opt == EMB_OPT_SGD) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) w[v] = w[v] - a.lr * g[v];
+    } else {
+        float4 *sp = reinterpret_cast<float4 *>(col.state + e);
+        float4 s = *sp;
+        float acc[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            acc[v] = acc[v] + g[v] * g[v];
+            w[v] = w[v] - a.lr * g[v] / (sqrtf(acc[v]) + a.eps);
+        }
+        *sp = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    if (col.dtype == EMB_BF16) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16);
+        o.y = f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(col.weights) + e) = o;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e) =
+            make_float4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+template <int P>
+__device__ void bwd_piece(const BwdArgs &a, const BwdLds &L, const BTile &t, const DevCol &col,
+                          int c, int side, int u, const float (&sum)[4], int g, int q, bool qa)
+{
+    const int64_t T = a.T;
+    const int ss = segat(a, L, t, u), se = segat(a, L, t, u + 1);
+    const int64_t k0 = ss / T, k1 = (se - 1) / T;
+    const int64_t slot = t.k * 2 + side;
+    if (qa)
+        *reinterpret_cast<float4 *>(a.part + slot * a.maxD + q * 4) =
+            make_float4(sum[0], sum[1], sum[2], sum[3]);
+    __threadfence();
+    uint32_t old = 0;
+    if (q == 0) old = atomicAdd(&a.tick[k0], 1u);
+    old = __shfl(old, g * P, kWave);
+    if (old == (uint32_t)(k1 - k0)) {
+        __threadfence();
+        float tot[4] = {0.f, 0.f, 0.f, 0.f};
+        if (qa) {
+            const float *p0 = a.part + (k0 * 2 + 1) * a.maxD + q * 4;
+#pragma unroll
+            for (int v = 0; v < 4; v++) tot[v] = p0[v];
+            for (int64_t kk = k0 + 1; kk <= k1; kk++) {
+                const float *pk = a.part + (kk * 2) * a.maxD + q * 4;
+#pragma unroll
+                for (int v = 0; v < 4; v++) tot[v] += pk[v];
+            }
+        }
+        seg_out(a, col, c, u, tot, q, qa);
+        if (q == 0) a.tick[k0] = 0;
+    }
+}
+
+template <int P>
+__device__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t, const DevCol &col, int c,
+                            int s0, int s1)
+{
+    constexpr int G = kWave / P;
+    constexpr int U = 8;
+    const int lane = lane_id(), g = lane / P, q = lane % P;
+    const bool qa = q < col.dim / 4;
+    const int len = s1 - s0, Lg = (len + G - 1) / G;
+    const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
+    const float *gbase = a.G + col.out_off + q * 4;
+
+    float acc[4] = {0.f, 0.f, 0.f, 0.f}, hacc[4] = {0.f, 0.f, 0.f, 0.f};
+    int hseg = -1, tseg = -1;
+    bool hpass = false;
+    if (ga < ge) {
+        int u = seg_of(a, L, t, ga);
+        int uend = segat(a, L, t, u + 1);
+        bool before = segat(a, L, t, u) < ga;
+        for (int p = ga; p < ge; p += U) {
+            float4 x[U];
+            float wt[U];
+#pragma unroll
+            for (int u2 = 0; u2 < U; u2++) {
+                const int pp = p + u2;
+                x[u2] = make_float4(0.f, 0.f, 0.f, 0.f);
+                wt[u2] = 0.f;
+                if (pp < ge) {
+                    wt[u2] = L.wt[pp - t.t0];
+                    if (qa) x[u2] = *reinterpret_cast<const float4 *>(gbase + (int64_t)L.smp[pp - t.t0] * a.sumD);
+                }
+            }
+#pragma unroll
+            for (int u2 = 0; u2 < U; u2++) {
+                const int pp = p + u2;
+                if (pp < ge) {
+                    if (pp == uend) {
+                        if (before) {
+#pragma unroll
+                            for (int v = 0; v < 4; v++) hacc[v] = acc[v];
+                            hseg = u; hpass = false;
+                        } else {
+                            seg_out(a, col, c, u, acc, q, qa);
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[v] = 0.f;
+                        u++;
+                        uend = segat(a, L, t, u + 1);
+                        before = false;
+                    }
+                    acc[0] += wt[u2] * x[u2].x;
+                    acc[1] += wt[u2] * x[u2].y;
+                    acc[2] += wt[u2] * x[u2].z;
+                    acc[3] += wt[u2] * x[u2].w;
+                }
+            }
+        }
+        if (uend == ge) {
+            if (before) {
+#pragma unroll
+                for (int v = 0; v < 4; v++) hacc[v] = acc[v];
+                hseg = u; hpass = false;
+            } else {
+                seg_out(a, col, c, u, acc, q, qa);
+            }
+        } else if (before) {
+#pragma unroll
+            for (int v = 0; v < 4; v++) hacc[v] = acc[v];
+            hseg = u; hpass = true;
+        } else {
+            tseg = u;
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        L.part[0][lane][v] = hacc[v];
+        L.part[1][lane][v] = acc[v];
+    }
+    if (q == 0) {
+        L.hseg[g] = hseg; L.hpass[g] = hpass; L.tseg[g] = tseg;
+    }
+    wave_sync();
+    if (tseg >= 0) {
+        float sum[4] = {acc[0], acc[1], acc[2], acc[3]};
+        bool ended = false;
+        for (int g2 = g + 1; g2 < G; g2++) {
+            if (L.hseg[g2] != tseg) break;
+#pragma unroll
+            for (int v = 0; v < 4; v++) sum[v] += L.part[0][g2 * P + q][v];
+            if (!L.hpass[g2]) { ended = true; break; }
+        }
+        if (ended) seg_out(a, col, c, tseg, sum, q, qa);
+        else bwd_piece<P>(a, L, t, col, c, 1, tseg, sum, g, q, qa);
+    }
+    if (g == 0 && hseg >= 0) {
+        float sum[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
+        bool pass = hpass;
+        for (int g2 = 1; pass && g2 < G; g2++) {
+            if (L.hseg[g2] != hseg) break;
+#pragma unroll
+            for (int v = 0; v < 4; v++) sum[v] += L.part[0][g2 * P + q][v];
+            pass = L.hpass[g2];
+        }
+        bwd_piece<P>(a, L, t, col, c, 0, hseg, sum, g, q, qa);
+    }
+    wave_sync();
+}
+
+__global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
+{
+    __shared__ BwdLds lds[kWavesPerBlock];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    BwdLds &L = lds[w];
+    BTile t;
+    t.k = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    if (t.k >= a.ntiles) return;
+    const int nv = (int)a.misc[0], U = (int)a.misc[1];
+    t.t0 = (int)min<int64_t>(t.k * a.T, nv);
+    t.t1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
+    if (t.t0 >= t.t1) return;
+    t.uf = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)t.t0) - 1;
+    t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
+    t.wb = t.uf;
+    t.wn = min(t.ul + 2 - t.uf, kOffCap);
+    for (int i = lane; i < t.wn; i += kWave) L.seg[i] = a.seg[t.wb + i];
+    wave_sync();
+    int u = t.uf;
+    while (u <= t.ul) {
+        const int uu = uniform(u);
+        const uint32_t key = a.ukeys[uu];
+        const int c = uniform((int)wave_upper_bound(a.row_base, (int64_t)a.C + 1, key) - 1);
+        const DevCol col = a.cols[c];
+        // uniques of column c inside [uu, ul]
+        const uint32_t lim = a.row_base[c + 1];
+        const int uend = uu + (int)wave_lower_bound(a.ukeys + uu, (int64_t)(t.ul + 1 - uu), lim);
+        const int s0 = max(t.t0, segat(a, L, t, uu)), s1 = min(t.t1, segat(a, L, t, uend));
+        // stage each contributor's sample and pooling weight
+        for (int p = s0 + lane; p < s1; p += kWave) {
+            const int b = (int)a.sval[p];
+            L.smp[p - t.t0] = b - c * a.B;
+            L.wt[p - t.t0] = col.pool == EMB_POOL_MEAN ? 1.0f / (float)a.bag_n[b] : 1.0f;
+        }
+        wave_sync();
+        switch (col.glanes) {
+        case 1: bwd_segment<1>(a, L, t, col, c, s0, s1); break;
+        case 2: bwd_segment<2>(a, L, t, col, c, s0, s1); break;
+        case 4: bwd_segment<4>(a, L, t, col, c, s0, s1); break;
+        case 8: bwd_segment<8>(a, L, t, col, c, s0, s1); break;
+        case 16: bwd_segment<16>(a, L, t, col, c, s0, s1); break;
+        case 32: bwd_segment<32>(a, L, t, col, c, s0, s1); break;
+        default: bwd_segment<64>(a, L, t, col, c, s0, s1); break;
+        }
+        u = uend;
+    }
+}
+
+}  // namespace emb
+
+using namespace emb;
+
+extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *workspace,
+                                   uint32_t *uniq_keys, float *uniq_grads, int64_t *n_uniq,
+                                   int64_t *stats, void *stream)
+{
+    if (!plan || !grad_out || !workspace) return fail(EMB_ERR_INVALID_ARG, "plan, grad_out and workspace are required");
+    if (!aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned");
+    if (!aligned(workspace, 256)) return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (uniq_grads && (plan->opt != EMB_OPT_EMIT || !aligned(uniq_grads, 16)))
+        return fail(EMB_ERR_INVALID_ARG, "uniq_grads needs the EMIT optimizer and 16-byte alignment");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const int64_t n = plan->last_n;
+    if (n < 0) return fail(EMB_ERR_INVALID_ARG, "no training forward ran on this plan");
+    const WsLayout &W = plan->ws;
+    uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + W.keys);
+    uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + W.bags);
+    uint32_t *k1 = reinterpret_cast<uint32_t *>(ws + W.keys2);
+    uint32_t *v1 = reinterpret_cast<uint32_t *>(ws + W.vals2);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + W.hist);
+    uint32_t *dtot = reinterpret_cast<uint32_t *>(ws + W.dtot);
+    uint32_t *misc = reinterpret_cast<uint32_t *>(ws + W.misc);
+    const int64_t nblk = std::max<int64_t>(1, (n + kSortTile - 1) / kSortTile);
+    const int passes = (plan->key_bits + kRadixBits - 1) / kRadixBits;
+    hipError_t e = hipSuccess;
+    if (n > 0) {
+        for (int p = 0; p < passes; p++) {
+            const int shift = p * kRadixBits;
+            hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk);
+            hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
+            hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
+                               shift, hist, dtot, nblk);
+            std::swap(k0, k1);
+            std::swap(v0, v1);
+        }
+    }
+    uint32_t *ucnt = reinterpret_cast<uint32_t *>(ws + W.ucnt);
+    uint32_t *uscan = reinterpret_cast<uint32_t *>(ws + W.uscan);
+    uint32_t *seg = reinterpret_cast<uint32_t *>(ws + W.seg);
+    uint32_t *ukeys = reinterpret_cast<uint32_t *>(ws + W.ukeys);
+    if (n > 0) {
+        hipLaunchKernelGGL(uq_count, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
+        hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, nblk, uscan, misc, n_uniq, stats);
+        hipLaunchKernelGGL(uq_write, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
+                           uscan, misc, seg, ukeys, uniq_keys);
+        BwdArgs a{};
+        a.cols = plan->dcols;
+        a.row_base = plan->drow_base;
+        a.C = plan->n_cols;
+        a.B = plan->batch;
+        a.sumD = plan->sum_dim;
+        a.maxD = plan->max_dim;
+        a.T = plan->tile;
+        a.opt = plan->opt;
+        a.lr = plan->lr;
+        a.eps = plan->eps;
+        a.ntiles = std::max<int64_t>(1, (n + plan->tile - 1) / plan->tile);
+        a.G = grad_out;
+        a.sval = v0;
+        a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
+        a.seg = seg;
+        a.ukeys = ukeys;
+        a.misc = misc;
+        a.ugrads = uniq_grads;
+        a.part = reinterpret_cast<float *>(ws + W.bpart);
+        a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
+        a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
+        const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+        hipLaunchKernelGGL(seg_apply, dim3((unsigned)blocks), dim3(kBlock), 0, st, a);
+    } else if (n_uniq) {
+        e = hipMemsetAsync(n_uniq, 0, sizeof(int64_t), st);
+    }
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+    return EMB_OK;
+}

@@ -1,0 +1,130 @@
+// device.h -- gfx950 device helpers: ID hashing, exact 64-bit remainder, wavefront
+// searches and reductions, bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace emb {
+
+// SplitMix64 output function of x + golden gamma (the first output of a SplitMix64
+// generator seeded with x; Steele, Lea & Flood 2014).
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x)
+{
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// h mod d for any 64-bit h and d >= 1, with magic = floor((2^64-1)/d): the
+// multiply-high quotient is q or q-1, so one conditional subtraction is exact
+// (the second is a guard).  CDNA has no 64-bit integer divide.
+__device__ __forceinline__ uint64_t mod_magic(uint64_t h, uint64_t d, uint64_t magic)
+{
+    uint64_t q = __umul64hi(h, magic);
+    uint64_t r = h - q * d;
+    if (r >= d) r -= d;
+    if (r >= d) r -= d;
+    return r;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wavefront-level fence + barrier: makes one wavefront's LDS writes visible to
+// all its lanes (all waves of a block run independent tiles, so no s_barrier).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// First index i in [0, n) with a[i] > x (a non-decreasing), n if none, searched
+// by the whole wavefront: 64 probes per step, so ~log64(n) dependent loads.
+template <typename T>
+__device__ __forceinline__ int64_t wave_upper_bound(const T *a, int64_t n, T x)
+{
+    int64_t lo = 0, hi = n;   // answer in [lo, hi]
+    const int l = lane_id();
+    while (hi - lo > 64) {
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t i = lo + (int64_t)l * step;
+        const bool le = (i < hi) ? (a[i] <= x) : false;
+        const uint64_t m = __ballot(le);
+        const int cnt = __popcll(m);          // probes with a[i] <= x (a prefix of lanes)
+        if (cnt == 0) { hi = lo; break; }     // a[lo] > x
+        const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;   // a[nlo-1] <= x
+        const int64_t nhi = (lo + (int64_t)cnt * step < hi) ? lo + (int64_t)cnt * step : hi;
+        lo = nlo;
+        hi = nhi;
+    }
+    if (hi > lo) {
+        const int64_t i = lo + l;
+        const bool le = (i < hi) ? (a[i] <= x) : false;
+        lo += __popcll(__ballot(le));
+    }
+    return lo;
+}
+
+// First index i in [0, n) with a[i] >= x, n if none.
+template <typename T>
+__device__ __forceinline__ int64_t wave_lower_bound(const T *a, int64_t n, T x)
+{
+    int64_t lo = 0, hi = n;
+    const int l = lane_id();
+    while (hi - lo > 64) {
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t i = lo + (int64_t)l * step;
+        const bool lt = (i < hi) ? (a[i] < x) : false;
+        const int cnt = __popcll(__ballot(lt));
+        if (cnt == 0) { hi = lo; break; }
+        const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;
+        const int64_t nhi = (lo + (int64_t)cnt * step < hi) ? lo + (int64_t)cnt * step : hi;
+        lo = nlo;
+        hi = nhi;
+    }
+    if (hi > lo) {
+        const int64_t i = lo + l;
+        const bool lt = (i < hi) ? (a[i] < x) : false;
+        lo += __popcll(__ballot(lt));
+    }
+    return lo;
+}
+
+// Sum over the wavefront with DPP row shifts / swizzles (via shfl_xor).
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// XCD-aware block order: consecutive hardware block ids go round-robin over
+// the 8 XCDs; map them so each XCD walks one contiguous range of tiles (its own
+// L2 then caches the rows of fewer columns).
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
+{
+    const int64_t x = b & 7, i = b >> 3;
+    const int64_t base = nb >> 3, rem = nb & 7;
+    return x * base + (x < rem ? x : rem) + i;
+}
+
+}  // namespace emb

@@ -1,0 +1,479 @@
+// forward.hip -- the fused multi-column forward: transform, filter, gather, pool.
+//
+// ONE launch covers every column.  Work follows element count, not column count
+// (RecIS Sec. 3.1, "Thread mapping for skewed inputs"): all columns' positions
+// form one flat index space (column-major bags), cut into equal tiles of T
+// positions, one tile per wavefront.  Inside a tile:
+//   1. three wavefront-parallel searches over the CSR offsets find the bags the
+//      tile touches; their offsets are staged in LDS;
+//   2. per column segment, each lane transforms positions (hash + exact mod,
+//      identity, bucketize on LDS-staged boundaries, keyed rows), with the
+//      validity filter of an embedding column (RECom explainer: out-of-range
+//      indices dropped), into LDS; a training step also records the row key and
+//      bag of every position for the backward;
+//   3. the wavefront splits into groups of P lanes (P * 16 bytes = one table row);
+//      each group walks a contiguous run of positions, issuing 8 independent
+//      16-byte row loads per lane before accumulating them in fp32 registers, and
+//      a bag that ends inside the run is written by that group alone -- the
+//      unique-writer forward of RecIS Sec. 3.2 / Algorithm 1, no atomics on Y,
+//      empty bags produce zero;
+//   4. bags cut by group boundaries are combined in LDS; bags cut by tile
+//      boundaries leave fp32 partials in the workspace and the last tile to
+//      arrive (atomic ticket) sums the pieces in tile order, so the result does
+//      not depend on arrival order.
+#include <algorithm>
+#include <string>
+
+#include "device.h"
+
+namespace emb {
+
+struct FwdArgs {
+    const DevCol *cols;
+    int32_t C, B, sumD, maxD, T, training;
+    int64_t N, ntiles;
+    const int32_t *off;
+    const int64_t *ids;
+    const float *fvals;
+    const int32_t *krows;
+    float *Y;
+    uint32_t *keys;
+    int32_t *bags;
+    int32_t *bag_n;
+    float *part;
+    int32_t *pcnt;
+    uint32_t *tick;
+    int64_t *stats;
+    uint32_t total_rows;
+};
+
+struct WaveLds {
+    int32_t rows[kTileMax];          // transformed row of each tile position
+    int32_t off[kOffCap];            // window of CSR offsets
+    union {
+        float part[2][kWave][8];     // per-lane head / tail partial sums
+        float bnd[kBndCap];          // bucket boundaries of the current column
+    } x;
+    int32_t hbag[kWave], hcnt[kWave], hpass[kWave];
+    int32_t tbag[kWave], tcnt[kWave];
+};
+
+struct TileCtx {
+    int64_t k;
+    int t0, t1;      // positions of this tile
+    int bf, bl;      // first / last non-empty bag touching the tile
+    int wb, wn;      // LDS window: offsets[wb .. wb+wn)
+};
+
+__device__ __forceinline__ int offat(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+{
+    const unsigned i = (unsigned)(b - t.wb);
+    return i < (unsigned)t.wn ? L.off[i] : a.off[b];
+}
+
+// the non-empty bag containing position p (p inside the tile)
+__device__ __forceinline__ int bag_of(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int p)
+{
+    int lo = t.bf, hi = t.bl + 1;   // off[lo] <= p < off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offat(a, L, t, mid) <= p) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// the next non-empty bag after b (a later position exists)
+__device__ __forceinline__ int next_bag(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+{
+    int nb = b + 1;
+    while (offat(a, L, t, nb + 1) == offat(a, L, t, nb)) nb++;
+    return nb;
+}
+
+template <int V>
+__device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int c, int bag,
+                                        const float (&acc)[V], int n, int q, bool qa,
+                                        int64_t &zero_bags)
+{
+    const int s = bag - c * a.B;
+    if (qa) {
+        float o[V];
+        const bool mean = col.pool == EMB_POOL_MEAN;
+#pragma unroll
+        for (int v = 0; v < V; v++) o[v] = n == 0 ? 0.f : (mean ? acc[v] / (float)n : acc[v]);
+        float4 *y = reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V);
+#pragma unroll
+        for (int v = 0; v < V; v += 4) y[v / 4] = make_float4(o[v], o[v + 1], o[v + 2], o[v + 3]);
+    }
+    if (q == 0) {
+        if (a.training) a.bag_n[bag] = n;
+        zero_bags += (n == 0);
+    }
+}
+
+template <int V, bool BF>
+__device__ __forceinline__ void accum(float (&acc)[V], const uint4 &w)
+{
+    if constexpr (BF) {
+        acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+        acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+        acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+        acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+    } else {
+        acc[0] += __uint_as_float(w.x); acc[1] += __uint_as_float(w.y);
+        acc[2] += __uint_as_float(w.z); acc[3] += __uint_as_float(w.w);
+    }
+}
+
+// a piece of a bag that crosses a tile boundary: publish it, and if this is the
+// last piece to arrive, sum all pieces in tile order and write the bag
+template <int P, int V>
+__device__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t, const DevCol &col,
+                           int c, int side, int bag, const float (&sum)[V], int n, int g, int q,
+                           bool qa, int64_t &zero_bags)
+{
+    const int64_t T = a.T;
+    const int bs = offat(a, L, t, bag), be = offat(a, L, t, bag + 1);
+    const int64_t k0 = bs / T, k1 = (be - 1) / T;
+    const int64_t slot = t.k * 2 + side;
+    float *pp = a.part + slot * a.maxD + q * V;
+    if (qa) {
+#pragma unroll
+        for (int v = 0; v < V; v += 4)
+            reinterpret_cast<float4 *>(pp)[v / 4] = make_float4(sum[v], sum[v + 1], sum[v + 2], sum[v + 3]);
+    }
+    if (q == 0) a.pcnt[slot] = n;
+    __threadfence();
+    uint32_t old = 0;
+    if (q == 0) old = atomicAdd(&a.tick[k0], 1u);
+    old = __shfl(old, g * P, kWave);
+    if (old == (uint32_t)(k1 - k0)) {
+        __threadfence();
+        float tot[V];
+        const float *p0 = a.part + (k0 * 2 + 1) * a.maxD + q * V;
+        int tn = a.pcnt[k0 * 2 + 1];
+#pragma unroll
+        for (int v = 0; v < V; v++) tot[v] = qa ? p0[v] : 0.f;
+        for (int64_t kk = k0 + 1; kk <= k1; kk++) {
+            const float *pk = a.part + (kk * 2) * a.maxD + q * V;
+            tn += a.pcnt[kk * 2];
+#pragma unroll
+            for (int v = 0; v < V; v++) tot[v] += qa ? pk[v] : 0.f;
+        }
+        bag_out<V>(a, col, c, bag, tot, tn, q, qa, zero_bags);
+        if (q == 0) a.tick[k0] = 0;   // ready for the next call
+    }
+}
+
+template <int P, int V, bool BF>
+__device__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
+                            int c, int s0, int s1, int64_t &zero_bags)
+{
+    constexpr int G = kWave / P;
+    constexpr int U = 8;
+    constexpr int ESZ = BF ? 2 : 4;
+    const int lane = lane_id(), g = lane / P, q = lane % P;
+    const int D = col.dim;
+    const bool qa = q < D / V;
+    const int len = s1 - s0, Lg = (len + G - 1) / G;
+    const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
+    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)q * V * ESZ;
+
+    float acc[V], hacc[V];
+#pragma unroll
+    for (int v = 0; v < V; v++) acc[v] = hacc[v] = 0.f;
+    int cnt = 0, hcnt = 0, hbag = -1, tbag = -1;
+    bool hpass = false;
+
+    if (ga < ge) {
+        int b = bag_of(a, L, t, ga);
+        int bend = offat(a, L, t, b + 1);
+        bool before = offat(a, L, t, b) < ga;
+        for (int p = ga; p < ge; p += U) {
+            int r[U];
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) r[u] = (p + u < ge) ? L.rows[p + u - t.t0] : -1;
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                w[u] = make_uint4(0, 0, 0, 0);
+                if (r[u] >= 0 && qa)
+                    w[u] = *reinterpret_cast<const uint4 *>(wbase + (int64_t)r[u] * D * ESZ);
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int pp = p + u;
+                if (pp < ge) {
+                    if (pp == bend) {              // bag b ended just before pp
+                        if (before) {
+#pragma unroll
+                            for (int v = 0; v < V; v++) hacc[v] = acc[v];
+                            hcnt = cnt; hbag = b; hpass = false;
+                        } else {
+                            bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
+                        }
+#pragma unroll
+                        for (int v = 0; v < V; v++) acc[v] = 0.f;
+                        cnt = 0;
+                        b = next_bag(a, L, t, b);
+                        bend = offat(a, L, t, b + 1);
+                        before = false;
+                    }
+                    accum<V, BF>(acc, w[u]);
+                    cnt += (r[u] != -1);
+                }
+            }
+        }
+        // the piece holding the run's last position
+        if (bend == ge) {
+            if (before) {
+#pragma unroll
+                for (int v = 0; v < V; v++) hacc[v] = acc[v];
+                hcnt = cnt; hbag = b; hpass = false;
+            } else {
+                bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
+            }
+        } else if (before) {
+#pragma unroll
+            for (int v = 0; v < V; v++) hacc[v] = acc[v];
+            hcnt = cnt; hbag = b; hpass = true;
+        } else {
+            tbag = b;
+        }
+    }
+
+    // publish the run's boundary pieces
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+        L.x.part[0][lane][v] = hacc[v];
+        L.x.part[1][lane][v] = acc[v];
+    }
+    if (q == 0) {
+        L.hbag[g] = hbag; L.hcnt[g] = hcnt; L.hpass[g] = hpass;
+        L.tbag[g] = tbag; L.tcnt[g] = cnt;
+    }
+    wave_sync();
+
+    // bags that start in this run and continue into the next runs
+    if (tbag >= 0) {
+        float sum[V];
+#pragma unroll
+        for (int v = 0; v < V; v++) sum[v] = acc[v];
+        int n = cnt;
+        bool ended = false;
+        for (int g2 = g + 1; g2 < G; g2++) {
+            if (L.hbag[g2] != tbag) break;
+#pragma unroll
+            for (int v = 0; v < V; v++) sum[v] += L.x.part[0][g2 * P + q][v];
+            n += L.hcnt[g2];
+            if (!L.hpass[g2]) { ended = true; break; }
+        }
+        if (ended) bag_out<V>(a, col, c, tbag, sum, n, q, qa, zero_bags);
+        else tile_piece<P, V>(a, L, t, col, c, 1, tbag, sum, n, g, q, qa, zero_bags);
+    }
+    // the bag that came in from the previous tile
+    if (g == 0 && hbag >= 0) {
+        float sum[V];
+#pragma unroll
+        for (int v = 0; v < V; v++) sum[v] = hacc[v];
+        int n = hcnt;
+        bool pass = hpass;
+        for (int g2 = 1; pass && g2 < G; g2++) {
+            if (L.hbag[g2] != hbag) break;
+#pragma unroll
+            for (int v = 0; v < V; v++) sum[v] += L.x.part[0][g2 * P + q][v];
+            n += L.hcnt[g2];
+            pass = L.hpass[g2];
+        }
+        tile_piece<P, V>(a, L, t, col, c, 0, hbag, sum, n, g, q, qa, zero_bags);
+    }
+    wave_sync();
+}
+
+__device__ __forceinline__ int bucket_count(const float *b, int nb, float x)
+{
+    int k = 0;
+    int step = nb ? (1 << (31 - __clz(nb))) : 0;
+    for (; step > 0; step >>= 1)
+        if (k + step <= nb && b[k + step - 1] <= x) k += step;
+    return k;
+}
+
+__device__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
+                              int s0, int s1, int64_t (&cnt)[4])
+{
+    const int lane = lane_id();
+    const float *bp = col.boundaries;
+    const int nbd = col.n_bnd;
+    if (col.kind == EMB_COL_BUCKET && nbd <= kBndCap) {
+        for (int i = lane; i < nbd; i += kWave) L.x.bnd[i] = col.boundaries[i];
+        wave_sync();
+        bp = L.x.bnd;
+    }
+    const uint64_t rows = (uint64_t)col.rows;
+    for (int p = s0 + lane; p < s1; p += kWave) {
+        int r;
+        if (col.kind == EMB_COL_HASH) {
+            const int64_t id = a.ids[p];
+            r = (id >= col.id_lo && id < col.id_hi)
+                    ? (int)mod_magic(splitmix64((uint64_t)id), rows, col.magic) : -1;
+        } else if (col.kind == EMB_COL_IDENTITY) {
+            const int64_t id = a.ids[p];
+            r = (id >= 0 && (uint64_t)id < rows) ? (int)id : -1;
+        } else if (col.kind == EMB_COL_BUCKET) {
+            const float x = a.fvals[p];
+            r = (x != x) ? -1 : bucket_count(bp, nbd, x);
+        } else {
+            const int kr = a.krows[p];
+            r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
+        }
+        L.rows[p - t.t0] = r;
+        cnt[0] += 1;
+        cnt[1] += (r >= 0);
+        cnt[2] += (r == -1);
+        cnt[3] += (r == -2);
+        if (a.training) {
+            a.keys[p] = r >= 0 ? col.row_base + (uint32_t)r
+                               : (r == -2 ? a.total_rows + 1u : a.total_rows);
+            a.bags[p] = bag_of(a, L, t, p);
+        }
+    }
+    wave_sync();
+}
+
+__global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
+{
+    __shared__ WaveLds lds[kWavesPerBlock];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    WaveLds &L = lds[w];
+    TileCtx t;
+    t.k = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    if (t.k >= a.ntiles) return;
+    const int N = (int)a.N, T = a.T, nbag = a.C * a.B;
+    t.t0 = (int)min<int64_t>(t.k * T, N);
+    t.t1 = (int)min<int64_t>((t.k + 1) * T, N);
+    const bool last = t.k == a.ntiles - 1;
+    if (t.t0 < t.t1) {
+        t.bf = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t0) - 1;
+        t.bl = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t1 - 1) - 1;
+    } else {
+        t.bf = nbag;
+        t.bl = nbag - 1;
+    }
+    const int own_lo = (int)wave_lower_bound(a.off, (int64_t)nbag + 1, t.t0);
+    const int own_hi = last ? nbag : min((int)wave_lower_bound(a.off, (int64_t)nbag + 1, t.t1), nbag);
+    t.wb = min(t.bf, own_lo);
+    const int we = min(max(t.bl + 2, own_hi + 1), nbag + 1);
+    t.wn = min(we - t.wb, kOffCap);
+    for (int i = lane; i < t.wn; i += kWave) L.off[i] = a.off[t.wb + i];
+    wave_sync();
+
+    int64_t cnt[4] = {0, 0, 0, 0};
+    int64_t zero_bags = 0;
+    if (t.t0 < t.t1) {
+        const int c_first = t.bf / a.B, c_last = t.bl / a.B;
+        for (int c = c_first; c <= c_last; c++) {
+            const int cu = uniform(c);
+            const int s0 = max(t.t0, offat(a, L, t, cu * a.B));
+            const int s1 = min(t.t1, offat(a, L, t, (cu + 1) * a.B));
+            if (s0 >= s1) continue;
+            const DevCol col = a.cols[cu];
+            fwd_transform(a, L, t, col, s0, s1, cnt);
+            if (col.dtype == EMB_BF16) {
+                switch (col.lanes) {
+                case 1: fwd_segment<1, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 2: fwd_segment<2, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 4: fwd_segment<4, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 8: fwd_segment<8, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 16: fwd_segment<16, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                default: fwd_segment<32, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                }
+            } else {
+                switch (col.lanes) {
+                case 1: fwd_segment<1, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 2: fwd_segment<2, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 4: fwd_segment<4, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 8: fwd_segment<8, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 16: fwd_segment<16, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                case 32: fwd_segment<32, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                default: fwd_segment<64, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
+                }
+            }
+        }
+    }
+
+    // bags with no position that this tile owns: the zero default
+    for (int b = own_lo + lane; b < own_hi; b += kWave) {
+        if (offat(a, L, t, b) != offat(a, L, t, b + 1)) continue;
+        const int c = b / a.B;
+        const DevCol &col = a.cols[c];
+        float4 *y = reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD + col.out_off);
+        for (int d = 0; d < col.dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.training) a.bag_n[b] = 0;
+        zero_bags++;
+    }
+
+    if (a.stats) {
+        const int64_t s0 = wave_sum_i64(cnt[0]), s1 = wave_sum_i64(cnt[1]);
+        const int64_t s2 = wave_sum_i64(cnt[2]), s3 = wave_sum_i64(cnt[3]);
+        const int64_t s4 = wave_sum_i64(zero_bags);
+        if (lane == 0) {
+            if (s0) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_IDS], (unsigned long long)s0);
+            if (s1) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_VALID], (unsigned long long)s1);
+            if (s2) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_DROPPED], (unsigned long long)s2);
+            if (s3) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_DEFAULT], (unsigned long long)s3);
+            if (s4) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_ZERO_BAGS], (unsigned long long)s4);
+        }
+    }
+}
+
+}  // namespace emb
+
+using namespace emb;
+
+extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                  const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
+                                  float *out, void *workspace, int32_t training, int64_t *stats,
+                                  void *stream)
+{
+    if (!plan) return fail(EMB_ERR_INVALID_ARG, "plan is NULL");
+    if (!offsets || !out || !workspace) return fail(EMB_ERR_INVALID_ARG, "offsets, out and workspace are required");
+    if (n_ids < 0 || n_ids > plan->max_ids)
+        return fail(EMB_ERR_WORKSPACE, "n_ids exceeds the plan's max_ids");
+    if (plan->has_hash && n_ids > 0 && !ids) return fail(EMB_ERR_INVALID_ARG, "ids required (hash/identity columns)");
+    if (plan->has_bucket && n_ids > 0 && !fvals) return fail(EMB_ERR_INVALID_ARG, "fvals required (bucket columns)");
+    if (plan->has_keyed && n_ids > 0 && !keyed_rows) return fail(EMB_ERR_INVALID_ARG, "keyed_rows required (keyed columns)");
+    if (!aligned(out, 16)) return fail(EMB_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (!aligned(workspace, 256)) return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    FwdArgs a{};
+    char *ws = static_cast<char *>(workspace);
+    a.cols = plan->dcols;
+    a.C = plan->n_cols;
+    a.B = plan->batch;
+    a.sumD = plan->sum_dim;
+    a.maxD = plan->max_dim;
+    a.T = plan->tile;
+    a.training = training ? 1 : 0;
+    a.N = n_ids;
+    a.ntiles = std::max<int64_t>(1, (n_ids + plan->tile - 1) / plan->tile);
+    a.off = offsets;
+    a.ids = ids;
+    a.fvals = fvals;
+    a.krows = keyed_rows;
+    a.Y = out;
+    a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
+    a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
+    a.bag_n = reinterpret_cast<int32_t *>(ws + plan->ws.bag_n);
+    a.part = reinterpret_cast<float *>(ws + plan->ws.fpart);
+    a.pcnt = reinterpret_cast<int32_t *>(ws + plan->ws.fcnt);
+    a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
+    a.stats = stats;
+    a.total_rows = plan->total_rows;
+    if (training) plan->last_n = n_ids;
+    const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));
+    return EMB_OK;
+}

@@ -1,0 +1,99 @@
+// internal.h -- layouts shared by the host entry points and the gfx950 kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "emb.h"
+
+namespace emb {
+
+constexpr int kWave = 64;            // CDNA wavefront
+constexpr int kWavesPerBlock = 4;    // each wavefront owns one tile; no block-wide barriers
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kTileMax = 512;        // positions (or sorted contributors) per wavefront tile
+constexpr int kTileDefault = 512;
+constexpr int kOffCap = kTileMax + 64;   // LDS window of segment offsets per wavefront
+constexpr int kBndCap = 1024;            // bucket boundaries staged in LDS
+constexpr int kMaxDimF32 = 256;
+constexpr int kMaxDimBF16 = 512;
+
+// radix sort of (key, value) pairs
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortItems = 16;                       // keys per thread
+constexpr int kSortTile = kBlock * kSortItems;       // 4096 keys per block
+
+// One column as the kernels read it (plan device memory), 96 bytes.
+struct DevCol {
+    int32_t kind, pool, dtype, dim;
+    int64_t rows;
+    int64_t id_lo, id_hi;
+    uint64_t magic;          // floor((2^64 - 1) / rows): exact 64-bit remainder by multiply-high
+    void *weights;
+    float *state;
+    const float *boundaries;
+    int32_t n_bnd;
+    int32_t out_off;         // first output column of this embedding column
+    uint32_t row_base;       // sum of rows of the columns before this one
+    int32_t lanes;           // lanes per row: pow2 >= dim / vec
+    int32_t vec;             // elements per lane per 16-byte load: 4 (fp32) or 8 (bf16)
+    int32_t glanes;          // lanes per gradient row (fp32, 4 per lane): pow2 >= dim / 4
+};
+static_assert(sizeof(DevCol) == 96, "DevCol layout");
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct WsLayout {
+    size_t keys, bags, bag_n;                 // forward -> backward
+    size_t fpart, fcnt, ftick;                // forward split-bag partials and tickets
+    size_t keys2, vals2;                      // radix sort ping-pong
+    size_t hist, dtot;                        // radix histograms, digit totals
+    size_t seg, ukeys, ucnt, uscan, misc;     // unique rows: segment starts, keys, block counts
+    size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
+    size_t total;
+};
+
+}  // namespace emb
+
+struct emb_plan {
+    int32_t n_cols = 0, batch = 0;
+    int64_t max_ids = 0;
+    int32_t sum_dim = 0, max_dim = 0;
+    int32_t tile = emb::kTileDefault;
+    int32_t opt = EMB_OPT_EMIT;
+    float lr = 0.f, eps = 0.f;
+    uint32_t total_rows = 0;       // sum of rows: keys >= this are sentinels
+    int32_t key_bits = 0;          // bits needed for keys up to total_rows + 1
+    int64_t max_tiles = 0;         // tiles of the largest batch
+    int64_t sort_blocks = 0;       // radix blocks of the largest batch
+    bool has_hash = false, has_bucket = false, has_keyed = false;
+    int64_t last_n = -1;           // positions of the last training forward (read by the backward)
+    emb::DevCol *dcols = nullptr;  // device copy of the column metadata
+    uint32_t *drow_base = nullptr; // device [n_cols + 1] row bases (after dcols)
+    uint32_t *hrow_base = nullptr; // host copy
+    emb::DevCol *hcols = nullptr;  // host copy
+    emb::WsLayout ws{};
+};
+
+struct emb_table {
+    int64_t capacity = 0, row_capacity = 0;
+    int32_t dim = 0, threshold = 0;
+    float init_a = 0.f;            // fp32(init_std * sqrt(3)); 0 = zero rows
+    int64_t *slot_keys = nullptr;  // [capacity], 0 = empty
+    int32_t *slot_count = nullptr; // [capacity]
+    int32_t *slot_row = nullptr;   // [capacity], -1 = not admitted
+    float *pool = nullptr;         // [row_capacity, dim]
+    int32_t *next_row = nullptr;   // device counter of allocated rows
+    size_t bytes = 0;
+};
+
+namespace emb {
+// host helpers (plan.cpp)
+emb_status fail(emb_status s, const std::string &msg);
+emb_status ok();
+bool aligned(const void *p, size_t a);
+emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t batch,
+                         int64_t max_ids, const emb_plan_opts *opts);
+void plan_layout(emb_plan &P);
+}  // namespace emb

@@ -1,0 +1,238 @@
+/*
+ * emb.h -- C ABI of the fused multi-column embedding stage for AMD MI355X (gfx950).
+ *
+ * The stage turns many embedding columns into one pass over a jagged batch:
+ * raw ID or float transform (hash, bucketize), safety filtering (out-of-range IDs
+ * dropped, empty bags given the zero default), row lookup (hash-mod, identity, or
+ * a collisionless keyed table), gather with sum/mean pooling into one
+ * concatenated [B, sum(dim)] output, and the backward that deduplicates the
+ * touched rows, segment-reduces their gradients and applies a sparse row update.
+ *
+ * Sources of the definitions (the web pages this library implements):
+ *  - RECom explainer, "Why this problem is worth solving": an embedding column
+ *    maps a raw feature to an index by hashing or bucketing, drops out-of-range
+ *    indices, fills a default when the feature is missing, looks up table rows
+ *    and reduces them to one vector; one column owns one table.
+ *  - RecIS, Sec. 3.2 "Index-aware segment reduction" and Algorithm 1: CSR
+ *    offsets define segments; forward Y[s,:] = sum_r w_r E[i_r,:] over segment s,
+ *    empty segments produce zero; backward dE[u] = sum over contributors r with
+ *    i_r = u of w_r G[s(r),:].
+ *  - RecIS, Sec. 3.1 "Fused and Vectorized Feature Processing": all fields'
+ *    elements are flattened into one index space cut into equal tiles, so work
+ *    follows element count rather than field count.
+ *  - Monolith, Sec. 2.1 "Hash Table": a collisionless key-value table (distinct
+ *    IDs never share an embedding) that admits an ID only after its occurrence
+ *    count reaches a tunable threshold; lookup and update are native ops.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE memory owned by the caller unless marked (host).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it; none synchronizes the host and none
+ *    allocates device memory.  The caller keeps every buffer alive until the
+ *    stream work that uses it has completed.
+ *  - Host-detectable argument problems return a status before anything is
+ *    enqueued; emb_last_error() then holds a message.  A failed kernel launch
+ *    returns EMB_ERR_HIP.
+ *  - Data conditions are not errors: out-of-range IDs and NaN values are
+ *    dropped, empty bags give zero, keys not (yet) admitted read the DEFAULT
+ *    (zero) row; all are counted in the optional stats array.
+ */
+#ifndef EMB_H
+#define EMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EMB_OK = 0,
+    EMB_ERR_INVALID_ARG = 1,   /* bad descriptor, pointer, size or alignment */
+    EMB_ERR_UNSUPPORTED = 2,   /* a valid request this build does not handle (e.g. dim) */
+    EMB_ERR_WORKSPACE = 3,     /* a caller buffer is smaller than the query returned */
+    EMB_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} emb_status;
+
+/* column kinds: how a raw input becomes a row index (RECom: "by hashing or bucketing") */
+#define EMB_COL_HASH     0  /* ids int64; valid iff id_lo <= id < id_hi; row = splitmix64(id) mod rows */
+#define EMB_COL_IDENTITY 1  /* ids int64; valid iff 0 <= id < rows;      row = id                    */
+#define EMB_COL_BUCKET   2  /* fvals fp32; valid iff not NaN;            row = #{j : boundaries[j] <= x} */
+#define EMB_COL_KEYED    3  /* keyed_rows int32 from emb_table_lookup_or_insert                      */
+
+#define EMB_POOL_SUM  0     /* w_r = 1                                                  */
+#define EMB_POOL_MEAN 1     /* w_r = 1/n, n = valid positions of the bag, DEFAULT included */
+
+#define EMB_F32  0
+#define EMB_BF16 1          /* weights bf16, accumulation fp32, updated weights rounded to nearest even */
+
+#define EMB_OPT_EMIT    0   /* backward writes (unique key, gradient) and leaves tables alone */
+#define EMB_OPT_SGD     1   /* E <- E - lr g                                                  */
+#define EMB_OPT_ADAGRAD 2   /* A <- A + g^2 ; E <- E - lr g / (sqrt(A) + eps), element-wise   */
+
+#define EMB_ROW_DROPPED (-1) /* keyed row code: the position is dropped                       */
+#define EMB_ROW_DEFAULT (-2) /* keyed row code: the zero DEFAULT row (counted in a mean)        */
+
+/* stats[] indices: int64 device counters, accumulated (the caller zeroes them) */
+#define EMB_STAT_IDS            0  /* positions transformed by emb_forward           */
+#define EMB_STAT_VALID          1  /* positions with a table row                     */
+#define EMB_STAT_DROPPED        2  /* positions dropped (out of range, NaN, key < 1) */
+#define EMB_STAT_DEFAULT        3  /* positions reading the DEFAULT row              */
+#define EMB_STAT_ZERO_BAGS      4  /* bags whose output is the zero default          */
+#define EMB_STAT_UNIQUE         5  /* distinct (column, row) pairs in emb_backward   */
+#define EMB_STAT_TABLE_INSERTED 6  /* keys newly placed in a keyed table             */
+#define EMB_STAT_TABLE_ADMITTED 7  /* keys that received a row (admission)           */
+#define EMB_STAT_TABLE_FULL     8  /* key occurrences refused: no free slot or row   */
+#define EMB_STAT_MAX_PROBE      9  /* longest probe sequence seen (max, not sum)     */
+#define EMB_STAT_COUNT         16
+
+/* One embedding column (host struct), in output order.  Row-major tables. */
+typedef struct emb_column_desc {
+    int32_t kind;              /* EMB_COL_*                                             */
+    int32_t pool;              /* EMB_POOL_*                                            */
+    int32_t dtype;             /* EMB_F32 | EMB_BF16 (KEYED: EMB_F32)                    */
+    int32_t dim;               /* D: fp32 multiple of 4, <= 256; bf16 multiple of 8, <= 512 */
+    int64_t rows;              /* table rows, 1 .. 2^31-1                               */
+    int64_t id_lo, id_hi;      /* HASH: valid raw IDs are [id_lo, id_hi)                  */
+    const float *boundaries;   /* BUCKET: device, sorted ascending fp32                 */
+    int64_t n_boundaries;      /* BUCKET: rows >= n_boundaries + 1                      */
+    void *weights;             /* device [rows, dim] in dtype; updated in place by emb_backward */
+    float *opt_state;          /* ADAGRAD: device fp32 [rows, dim], zero before the first step  */
+} emb_column_desc;
+
+typedef struct emb_plan_opts {
+    int32_t opt;               /* EMB_OPT_*                                            */
+    float lr;                  /* learning rate (SGD, ADAGRAD)                          */
+    float eps;                 /* ADAGRAD epsilon, outside the square root              */
+    int32_t tile;              /* positions per wavefront tile: 0 = default, else a multiple of 64 <= 1024 */
+} emb_plan_opts;
+
+typedef struct emb_plan emb_plan;    /* host object owned by the library */
+typedef struct emb_table emb_table;  /* host object owned by the library */
+
+/* Sizes of the device buffers a plan needs: `plan_bytes` of column metadata and
+ * `workspace_bytes` of per-step workspace for batches of `batch` samples with at
+ * most `max_ids` positions.  Host only; validates the descriptors. */
+emb_status emb_plan_query(const emb_column_desc *cols /* host [n_cols] */, int32_t n_cols,
+                          int32_t batch, int64_t max_ids, const emb_plan_opts *opts /* host */,
+                          size_t *plan_bytes /* host */, size_t *workspace_bytes /* host */);
+
+/* Creates a plan.  Copies the column metadata into `plan_mem` (>= plan_bytes,
+ * 256-byte aligned) on `stream`.  The plan keeps pointers to the caller's tables. */
+emb_status emb_plan_create(const emb_column_desc *cols, int32_t n_cols, int32_t batch,
+                           int64_t max_ids, const emb_plan_opts *opts, void *plan_mem,
+                           void *stream, emb_plan **out /* host */);
+
+emb_status emb_plan_destroy(emb_plan *plan);
+
+/*
+ * Forward of all columns in ONE kernel launch.
+ *   offsets  int32 [n_cols*batch + 1]: bag (c, s) is positions [offsets[c*B+s], offsets[c*B+s+1]),
+ *            column-major (all bags of column 0, then column 1, ...); offsets[0] = 0,
+ *            non-decreasing, offsets[n_cols*batch] = n_ids.
+ *   ids      int64 [n_ids] raw IDs (HASH, IDENTITY positions), or NULL if no such column.
+ *   fvals    fp32  [n_ids] raw values (BUCKET positions), or NULL if no such column.
+ *   keyed_rows int32 [n_ids] rows from emb_table_lookup_or_insert (KEYED positions), or NULL.
+ *   out      fp32 [batch, sum(dim)]: every element is written (zero for empty bags).
+ *   workspace >= workspace_bytes, 256-byte aligned, ZERO-FILLED once before the
+ *            plan's first call; it holds per-step state that the library
+ *            restores before each call returns.  With training != 0 the forward
+ *            records what the matching emb_backward needs in it, so the same
+ *            workspace must reach that backward unmodified.  A workspace serves
+ *            one call at a time.
+ *   stats    int64 [EMB_STAT_COUNT] or NULL.
+ */
+emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                       const float *fvals, const int32_t *keyed_rows, int64_t n_ids, float *out,
+                       void *workspace, int32_t training, int64_t *stats, void *stream);
+
+/*
+ * Backward of the last training forward on this workspace: deduplicates the
+ * touched (column, row) pairs by a radix sort of their keys, sums each pair's
+ * contributions w_r * grad_out[s(r), off_c:off_c+dim] and applies opts->opt.
+ *   grad_out   fp32 [batch, sum(dim)].
+ *   uniq_keys  uint32 [n_ids] or NULL: the distinct keys, ascending, key = row_base_c + row
+ *              with row_base_c = sum of rows of the columns before c.
+ *   uniq_grads fp32 [n_ids, max(dim)] or NULL (EMIT only): gradient of uniq_keys[u] in row u.
+ *   n_uniq     int64 device scalar or NULL: number of distinct keys.
+ * SGD / ADAGRAD update the columns' weights (and opt_state) in place; rows that
+ * no position touched are left bit-identical.
+ */
+emb_status emb_backward(emb_plan *plan, const float *grad_out, void *workspace,
+                        uint32_t *uniq_keys, float *uniq_grads, int64_t *n_uniq, int64_t *stats,
+                        void *stream);
+
+/* Device views into a workspace after a training forward (parity checks):
+ * keys uint32 [n_ids] (row_base_c + row; sum(rows) for a dropped position,
+ * sum(rows)+1 for a DEFAULT one), bags int32 [n_ids] (bag index c*B+s),
+ * bag_n int32 [n_cols*batch] (valid positions per bag). */
+typedef struct emb_workspace_view {
+    uint32_t *keys;
+    int32_t *bags;
+    int32_t *bag_n;
+} emb_workspace_view;
+emb_status emb_plan_workspace_view(emb_plan *plan, void *workspace, emb_workspace_view *out /* host */);
+
+/* ------------------------------------------------------------------------
+ * Collisionless keyed table (Monolith, Sec. 2.1): open addressing over a
+ * power-of-two slot array, linear probing from splitmix64(key) & (capacity-1),
+ * insertion by atomic compare-and-swap on the slot key, an occurrence count per
+ * slot and a frequency filter: a key gets a row from the row pool once its count
+ * reaches `threshold`.  Distinct keys never share a row.  Valid keys are >= 1.
+ * Rows are fp32 [row_capacity, dim]; emb_table_rows() gives the pool, which a
+ * KEYED column uses as its weights (rows = row_capacity).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device memory for a table. */
+emb_status emb_table_query(int64_t capacity /* power of two, <= 2^30 */, int64_t row_capacity,
+                           int32_t dim, size_t *table_bytes /* host */);
+
+/* Creates an empty table in `table_mem` (>= table_bytes, 256-byte aligned; cleared
+ * on `stream`).  New rows start as fp32(init_std*sqrt(3)) * (2u - 1) with
+ * u = (splitmix64(splitmix64(key) + d) >> 40) * 2^-24 (uniform, std init_std),
+ * or zero if init_std == 0. */
+emb_status emb_table_create(int64_t capacity, int64_t row_capacity, int32_t dim,
+                            int32_t threshold, float init_std, void *table_mem, void *stream,
+                            emb_table **out /* host */);
+
+emb_status emb_table_destroy(emb_table *table);
+
+/* Device pointer to the row pool, fp32 [row_capacity, dim]. */
+float *emb_table_rows(emb_table *table);
+
+/* Inserts distinct keys as already admitted (count 0) with row values `rows`
+ * fp32 [n, dim] (or the initializer above if rows is NULL).  Keys already
+ * present keep their row; keys < 1 are skipped. */
+emb_status emb_table_bulk_insert(emb_table *table, const int64_t *keys, const float *rows,
+                                 int64_t n, int64_t *stats, void *stream);
+
+/*
+ * One step's lookup-or-insert.  Every occurrence of a valid key adds one to its
+ * count (absent keys are inserted first); afterwards a key without a row whose
+ * count reached the threshold is admitted.  The rule is batch-level: all
+ * occurrences in the step see the same outcome, whatever the thread order.
+ *   rows_out int32 [n]: the key's row, EMB_ROW_DEFAULT (not admitted, or refused
+ *            because the table or row pool is full) or EMB_ROW_DROPPED (key < 1).
+ */
+emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int64_t n,
+                                      int32_t *rows_out, int64_t *stats, void *stream);
+
+/* Read-only lookup: rows_out int32 [n] (row, EMB_ROW_DEFAULT if present but not
+ * admitted, EMB_ROW_DROPPED if absent); counts_out int32 [n] or NULL. */
+emb_status emb_table_find(emb_table *table, const int64_t *keys, int64_t n, int32_t *rows_out,
+                          int32_t *counts_out, void *stream);
+
+/* Writes every occupied slot (in unspecified order): keys int64, counts int32,
+ * rows int32 (-1 if not admitted), each [capacity]; n_out int64 device scalar. */
+emb_status emb_table_export(emb_table *table, int64_t *keys, int32_t *counts, int32_t *rows,
+                            int64_t *n_out, void *stream);
+
+/* Message for the last non-OK status on this host thread. */
+const char *emb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMB_H */

@@ -70,6 +70,9 @@ def lib():
                                       + [C.c_int32, C.c_double, C.c_double]
                                       + [C.c_void_p] * 4 + [C.c_int64])
         L.oracle_init_row.argtypes = [C.c_int64, C.c_int32, C.c_double, C.c_void_p]
+        L.oracle_adagrad_array.argtypes = [C.c_void_p] * 3 + [C.c_int64, C.c_double, C.c_double,
+                                                                C.c_void_p, C.c_void_p]
+        L.oracle_to_bf16_array.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
         _lib = L
     return _lib
 
@@ -104,6 +107,22 @@ def adagrad_elem(e, a, g, lr, eps):
     a_out = C.c_double()
     e2 = lib().oracle_adagrad_elem(e, a, g, lr, eps, C.byref(a_out))
     return e2, a_out.value
+
+
+def adagrad_array(e, a, g, lr, eps):
+    e = np.ascontiguousarray(e, dtype=np.float64)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    eo, ao = np.empty_like(e), np.empty_like(e)
+    lib().oracle_adagrad_array(_p(e), _p(a), _p(g), e.size, lr, eps, _p(eo), _p(ao))
+    return eo, ao
+
+
+def to_bf16_array(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_to_bf16_array(_p(v), v.size, _p(out))
+    return out
 
 
 def init_row(key: int, dim: int, std: float) -> np.ndarray:

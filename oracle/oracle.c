@@ -360,3 +360,17 @@ void oracle_init_row(int64_t key, int32_t dim, double std, float *out)
         out[d] = (float)((double)a * (2.0 * u - 1.0));
     }
 }
+
+/* ------------------------------------------------------- array helpers */
+
+/* oracle_adagrad_elem over arrays (used to bound a reordered-sum result) */
+void oracle_adagrad_array(const double *e, const double *a, const double *g, int64_t n, double lr,
+                          double eps, double *e_out, double *a_out)
+{
+    for (int64_t i = 0; i < n; i++) e_out[i] = oracle_adagrad_elem(e[i], a[i], g[i], lr, eps, &a_out[i]);
+}
+
+void oracle_to_bf16_array(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_double_to_bf16(v[i]);
+}

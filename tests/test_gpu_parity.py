@@ -1,0 +1,181 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Integer results (transformed rows, bag of each position, valid counts per bag,
+the distinct touched rows) must match bit-exactly; pooled outputs and gradients
+within 1e-5 of sum |term| (fp32 accumulation in another order); updated rows
+within the interval the oracle's update takes over that gradient error.
+Sizes span many tiles with ragged tails; tiles of 64 positions force most bags
+across tile boundaries (the split-bag combine)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_harness import run_dense_case, Step, to_np, check_forward, oracle_columns
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("tile", [64, 512])
+def test_tiny_fused_bag_emit(tile):
+    # 8 hashed columns, B=256, 1000 x 16 fp32 tables, bags of 1..4, EMIT of row grads
+    run_dense_case(W.config(1), seed=1001, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [64, 192, 512])
+def test_training_front_end_sgd(tile):
+    # Poisson(3) bags, 5 % forced empty, 2 % invalid IDs, sum/mean, dims 8..64, SGD
+    w = W.config(2, n_cols=24, batch=512, rows_range=(1e2, 1e4))
+    run_dense_case(w, seed=2002, tile=tile)
+
+
+def test_training_front_end_emit_mean_and_sum():
+    w = W.config(2, n_cols=16, batch=300, rows_range=(30, 3000), opt=W.OPT_EMIT)
+    run_dense_case(w, seed=2003, tile=128)
+
+
+@pytest.mark.parametrize("training", [False, True])
+def test_many_tiny_columns_inference(training):
+    # 100 columns (70 hashed, 30 bucketized floats), dims 4..16, forward
+    w = W.config(3, n_cols=100, batch=128, rows_range=(100, 1e4))
+    run_dense_case(w, seed=3003, tile=256, training=training, check_bwd=False)
+
+
+def test_many_tiny_columns_backward():
+    w = W.config(3, n_cols=60, batch=96, rows_range=(100, 5000), opt=W.OPT_SGD, lr=0.01,
+                 training=True)
+    run_dense_case(w, seed=3004, tile=64)
+
+
+@pytest.mark.parametrize("tile", [128, 512])
+def test_long_sequences_bf16_adagrad(tile):
+    # bags of 200..2000 IDs over 4 identity columns, bf16 tables, mean, Adagrad
+    w = W.config(4, n_cols=4, batch=40, rows=100_000)
+    run_dense_case(w, seed=4004, tile=tile)
+
+
+def test_deterministic_across_runs():
+    w = W.config(2, n_cols=12, batch=256, rows_range=(50, 2000), opt=W.OPT_EMIT)
+    a = run_dense_case(w, seed=5, tile=64)
+    b = run_dense_case(w, seed=5, tile=64)
+    assert torch.equal(a["Y"], b["Y"])
+    n = int(a["nu"].item())
+    assert torch.equal(a["ukeys"][:n], b["ukeys"][:n])
+    # gradient rows are padded to the widest column; compare each row's own dims
+    rb = np.concatenate([[0], np.cumsum([c.rows for c in w.cols])])
+    keys = to_np(a["ukeys"][:n]).astype(np.int64)
+    dims = np.array([c.dim for c in w.cols])[np.searchsorted(rb, keys, side="right") - 1]
+    ga, gb = to_np(a["ugrads"][:n]), to_np(b["ugrads"][:n])
+    for u in range(n):
+        assert np.array_equal(ga[u, :dims[u]], gb[u, :dims[u]])
+
+
+# ------------------------------------------------------------------ edges
+
+def _custom(cols, lens, ids=None, fvals=None, B=None, opt=W.OPT_EMIT, lr=0.0):
+    C = len(cols)
+    B = B or len(lens) // C
+    off = np.zeros(C * B + 1, dtype=np.int32)
+    off[1:] = np.cumsum(lens)
+    n = int(off[-1])
+    rng = np.random.default_rng(n + C)
+    ids = ids if ids is not None else rng.integers(0, 1 << 40, size=n, dtype=np.int64)
+    fvals = fvals if fvals is not None else rng.normal(size=n).astype(np.float32)
+    w = W.Workload("edge", cols, B, "fixed", opt=opt, lr=lr)
+    b = W.Batch(off, ids, fvals, np.zeros(n, bool), np.zeros(C * B, bool), n)
+    return w, b
+
+
+def _run_custom(w, b, tile, seed=0):
+    wts, sts = W.make_tables(w, seed=seed, device="cpu")
+    G = W.make_grad(w, seed=seed, device="cpu")
+    st = Step(w, b, wts, sts, tile=tile)
+    Y = st.forward(training=True)
+    ws = st.cols.workspace_view(max(b.n, 1))
+    host_w = [to_np(t) for t in wts]
+    oc = oracle_columns(w, [x.copy() for x in host_w])
+    ref = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals)
+    torch.cuda.synchronize()
+    check_forward(w, b, Y, (ws[0][:b.n], ws[1][:b.n], ws[2]), ref)
+    ukeys, ugrads, nu = st.backward(G)
+    torch.cuda.synchronize()
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals)
+    n = int(nu.item())
+    assert n == ucol.size
+    rb = np.concatenate([[0], np.cumsum([c.rows for c in w.cols])])
+    assert np.array_equal(to_np(ukeys[:n]).astype(np.int64), rb[ucol] + urow)
+    g = to_np(ugrads[:n]).astype(np.float64)
+    for u in range(n):
+        D = w.cols[ucol[u]].dim
+        assert np.all(np.abs(g[u, :D] - ug[u, :D]) <= 1e-5 * ub[u, :D])
+    return Y
+
+
+def _hash_cols(n, dim=16, rows=97, pool=W.SUM):
+    return [W.Column(W.HASH, pool, W.F32, rows, dim, 0, 1 << 40) for _ in range(n)]
+
+
+def test_all_bags_empty():
+    w, b = _custom(_hash_cols(3), [0] * 30)
+    Y = _run_custom(w, b, 64)
+    assert torch.count_nonzero(Y) == 0
+
+
+@pytest.mark.parametrize("tile", [64, 512])
+def test_one_bag_spanning_many_tiles(tile):
+    # one 5000-position bag between empty bags: pieces from ~80 tiles combine
+    lens = [0, 5000, 0, 3, 0, 0]
+    w, b = _custom(_hash_cols(2, dim=32, pool=W.MEAN), lens)
+    _run_custom(w, b, tile)
+
+
+def test_single_position_and_all_invalid():
+    cols = _hash_cols(2, dim=8)
+    w, b = _custom(cols, [1, 0, 0, 4], ids=np.array([5, -1, -7, 1 << 41, -2], dtype=np.int64))
+    Y = _run_custom(w, b, 64)
+    assert torch.count_nonzero(Y[1]) == 0
+
+
+@pytest.mark.parametrize("dtype,dim", [(W.F32, 256), (W.F32, 4), (W.BF16, 256), (W.BF16, 8),
+                                       (W.F32, 12), (W.BF16, 24)])
+def test_dims_and_dtypes(dtype, dim):
+    cols = [W.Column(W.IDENTITY, W.MEAN, dtype, 50, dim), W.Column(W.HASH, W.SUM, dtype, 31, dim, 0, 1 << 40)]
+    rng = np.random.default_rng(dim)
+    lens = rng.integers(0, 40, size=2 * 70)
+    n = int(lens.sum())
+    ids = rng.integers(-3, 60, size=n).astype(np.int64)
+    w, b = _custom(cols, lens, ids=ids)
+    _run_custom(w, b, 128)
+
+
+def test_many_columns_tiny_batch():
+    # 300 columns with B=1: a tile spans many column segments
+    cols = [W.Column(W.HASH, W.SUM if c % 3 else W.MEAN, W.F32, 7 + c, 4 * (1 + c % 4), 0, 1 << 40)
+            for c in range(300)]
+    rng = np.random.default_rng(9)
+    w, b = _custom(cols, rng.integers(0, 4, size=300), B=1)
+    _run_custom(w, b, 64)
+
+
+def test_bucket_edges():
+    bnd = np.array([-1.0, 0.0, 0.0, 2.5], dtype=np.float32)
+    cols = [W.Column(W.BUCKET, W.SUM, W.F32, 5, 8, boundaries=bnd),
+            W.Column(W.BUCKET, W.MEAN, W.F32, 9, 4, boundaries=bnd)]
+    fv = np.array([np.nan, -1.0, 0.0, -0.0, 2.5, np.inf, -np.inf, 1e-45, 3.0, -1.0000001, np.nan,
+                   0.5], dtype=np.float32)
+    w, b = _custom(cols, [3, 3, 0, 2, 4, 0], fvals=fv)
+    _run_custom(w, b, 64)
+
+
+def test_stats_counts():
+    w = W.config(2, n_cols=10, batch=200, rows_range=(100, 1000), opt=W.OPT_EMIT)
+    out = run_dense_case(w, seed=77, tile=128)
+    st, b = out["step"], out["batch"]
+    s = to_np(st.stats)
+    assert s[0] == b.n
+    assert s[2] == int(b.invalid_mask.sum())          # dropped = generator's invalid IDs
+    assert s[1] == b.n - s[2]
+    lens = np.diff(b.offsets)
+    assert s[4] >= int((lens == 0).sum())             # at least the empty bags are zero
+    assert s[5] == int(out["nu"].item())
