@@ -1,0 +1,280 @@
+"""Throughput of the fused multi-column embedding stage on one MI355X.
+
+Default workload: the training sparse front end -- 200 hashed columns, batch
+4096, tables of 1e4..1e6 rows (log-uniform) and dims 8..64 in fp32, Poisson(3)
+bags with 5 % forced-empty bags and 2 % out-of-range IDs, Zipf(1.1) raw IDs over
+2^40, alternating sum/mean pooling, one SGD step (lr 0.01).  A step is one
+forward launch plus the backward (sort, unique rows, segment-sum + SGD) over
+one batch already resident in HBM; steps cycle a pool of pre-generated batches.
+
+Prints one JSON line: lookups/s (valid (column, sample, ID) positions per
+second), the roofline of the dominant kernel (algorithmic bytes / its average
+launch time, timed with HIP events on the launch stream), and the CPU oracle
+timed on one batch on the host.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"tiny": 1, "front-end": 2, "inference": 3, "long-seq": 4, "keyed": 5}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def elem_size(col):
+    return 2 if col.dtype == 1 else 4
+
+
+def fwd_bytes(w, b, valid_per_col, gathers_per_col, training):
+    """Algorithmic bytes of one forward: raw inputs, CSR offsets, one row read
+    per valid non-default position, the pooled output, and (training) one 4-byte
+    row index per valid position kept for the backward."""
+    C, B = len(w.cols), w.batch
+    n_int = sum(int(b.offsets[(c + 1) * B] - b.offsets[c * B]) for c, col in enumerate(w.cols)
+                if col.kind != 2)
+    n_flt = b.n - n_int
+    byts = 8 * n_int + 4 * n_flt + 4 * (C * B + 1)
+    byts += sum(gathers_per_col[c] * col.dim * elem_size(col) for c, col in enumerate(w.cols))
+    byts += 4 * B * w.sum_dim
+    if training:
+        byts += 4 * sum(valid_per_col)
+    return byts
+
+
+def bwd_bytes(w, valid_total, uniq_per_col):
+    """Saved row indices + upstream gradient read once + the row update of each
+    distinct touched row (EMIT: key + gradient; SGD: row read + write; Adagrad:
+    row read + write and the fp32 accumulator read + write)."""
+    byts = 4 * valid_total + 4 * w.batch * w.sum_dim
+    for c, col in enumerate(w.cols):
+        u, d, e = uniq_per_col[c], col.dim, elem_size(col)
+        if w.opt == 0:
+            byts += u * (4 + 4 * d)
+        elif w.opt == 1:
+            byts += u * 2 * d * e
+        else:
+            byts += u * (2 * d * e + 8 * d)
+    return byts
+
+
+def per_col_counts(w, b):
+    C, B = len(w.cols), w.batch
+    valid, gathers = [], []
+    for c, col in enumerate(w.cols):
+        a, e = int(b.offsets[c * B]), int(b.offsets[(c + 1) * B])
+        v = (e - a) - int(b.invalid_mask[a:e].sum())
+        if col.kind == 2:
+            v = (e - a) - int(np.isnan(b.fvals[a:e]).sum())
+        valid.append(v)
+        gathers.append(v)
+    return valid, gathers
+
+
+def run(args):
+    import torch
+
+    import embedding_columns_amd as E
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    w = W.config(cfg)
+    keyed = cfg == 5
+    training = w.training
+    t0 = time.time()
+    n_pool = args.batches if not keyed else args.warmup + args.steps
+    batches = [W.make_batch(w, seed=1000 * cfg + i) for i in range(n_pool)]
+    log(f"[bench] {w.name}: {n_pool} batches generated in {time.time() - t0:.1f}s, "
+        f"positions/batch {np.mean([b.n for b in batches]):.0f}")
+    dbat = []
+    for b in batches:
+        dbat.append(dict(off=torch.from_numpy(b.offsets).to(dev), ids=torch.from_numpy(b.ids).to(dev),
+                         fv=torch.from_numpy(b.fvals).to(dev), n=b.n))
+    max_ids = max(b.n for b in batches)
+
+    table = None
+    if keyed:
+        table = E.KeyedTable(w.capacity, w.row_capacity, 32, threshold=w.threshold,
+                             init_std=w.init_std, device=dev)
+        t0 = time.time()
+        chunk = 10_000_000
+        for s in range(0, w.prepop, chunk):
+            k = torch.from_numpy(W.key_of_rank(np.arange(s + 1, min(s + chunk, w.prepop) + 1,
+                                                         dtype=np.uint64))).to(dev)
+            rows = W.make_prepop_rows(k.numel(), 32, w.init_std, seed=s, device=dev)
+            table.bulk_insert(k, rows)
+            del rows
+        torch.cuda.synchronize()
+        log(f"[bench] prepopulated {w.prepop} keys in {time.time() - t0:.1f}s")
+        weights, states = [table.rows], [None]
+    else:
+        weights, states = W.make_tables(w, seed=cfg, device=dev)
+    plan = E.EmbeddingColumns(w.cols, weights, states, batch=w.batch, max_ids=max_ids, opt=w.opt,
+                              lr=w.lr, eps=w.eps, tile=args.tile, device=dev)
+    G = W.make_grad(w, seed=cfg, device=dev)
+    stats = torch.zeros(E.STAT_COUNT, dtype=torch.int64, device=dev)
+    Y = torch.empty(w.batch, w.sum_dim, dtype=torch.float32, device=dev)
+    krows = torch.empty(max_ids, dtype=torch.int32, device=dev) if keyed else None
+    kinds = {c.kind for c in w.cols}
+
+    def step(i, ev=None):
+        d = dbat[i % len(dbat)]
+        n = d["n"]
+        if keyed:
+            table.lookup_or_insert(d["ids"], rows_out=krows[:n], stats=stats)
+        if ev is not None:
+            ev[0].record()
+        E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
+                      d["fv"] if 2 in kinds else None, krows[:n] if keyed else None, n, Y,
+                      plan.workspace, training, stats)
+        if ev is not None:
+            ev[1].record()
+        if training:
+            E.emb_backward(plan.plan, G, plan.workspace, None, None, None, stats)
+        if ev is not None:
+            ev[2].record()
+
+    # per-batch algorithmic bytes (dense workloads: valid counts from the generator's
+    # masks, distinct rows from one untimed backward per batch)
+    counts = [per_col_counts(w, b) for b in batches]
+    uniq = []
+    if training and not keyed:
+        for i, b in enumerate(batches):
+            E.emb_forward(plan.plan, dbat[i]["off"], dbat[i]["ids"] if kinds & {0, 1} else None,
+                          dbat[i]["fv"] if 2 in kinds else None, None, b.n, Y, plan.workspace,
+                          True, None)
+            keys = torch.empty(max(b.n, 1), dtype=torch.int32, device=dev)
+            nu = torch.zeros(1, dtype=torch.int64, device=dev)
+            E.emb_backward(plan.plan, G, plan.workspace, keys, None, nu, None)
+            k = keys[:int(nu.item())].cpu().numpy().view(np.uint32).astype(np.int64)
+            rb = np.array(plan.row_base)
+            uniq.append(np.bincount(np.searchsorted(rb, k, side="right") - 1, minlength=len(w.cols)))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stats.zero_()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = stats.cpu().numpy()
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    idx = [(args.warmup + i) % len(dbat) for i in range(args.steps)]
+    if keyed:
+        lookups = int(st[1] + st[3])                     # admitted rows + DEFAULT reads
+        n_steps = args.steps
+        fb = np.mean([fwd_bytes(w, batches[j], [counts[j][0][0]], [st[1] / n_steps], True)
+                      for j in idx])
+        valid = lookups / n_steps
+        ub = bwd_bytes(w, st[1] / n_steps, [st[5] / n_steps])
+        table_bytes = 8 * batches[0].n + 16 * batches[0].n + 4 * batches[0].n
+        step_bytes = fb + ub + table_bytes
+    else:
+        lookups = sum(sum(counts[j][0]) for j in idx)
+        fb = np.mean([fwd_bytes(w, batches[j], counts[j][0], counts[j][1], training) for j in idx])
+        ub = (np.mean([bwd_bytes(w, sum(counts[j][0]), uniq[j]) for j in idx]) if training else 0.0)
+        step_bytes = fb + ub
+    value = lookups / wall
+    ms_step = 1000.0 * wall / args.steps
+    fwd_avg = float(np.mean(fwd_ms))
+    achieved = fb / (fwd_avg * 1e-3) / 1e9
+    out = {
+        "metric": "pooled embedding lookups/sec (fwd+bwd) at 1 GPU; achieved HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if any(c.dtype == 1 for c in w.cols) else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "columns": len(w.cols), "batch": w.batch,
+                   "positions_per_step": int(np.mean([batches[j].n for j in idx])),
+                   "valid_lookups_per_step": int(lookups / args.steps),
+                   "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
+                   "tile": plan.opts.tile or 512, "fwd_launches_per_step": 1},
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "fwd_ms": round(fwd_avg, 4),
+        "bwd_ms": round(float(np.mean(bwd_ms)), 4) if training else 0.0,
+        "roofline": {"kernel": "fwd_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": int(fb)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, batches[0], plan, G, weights, states)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, b, plan, G, weights, states):
+    """The oracle (single-threaded C, fp64) on one batch of the same workload,
+    forward + backward + the row update, on the host cores of this machine."""
+    import torch
+
+    import oracle
+    import workloads as W
+    if any(c.kind == W.KEYED for c in w.cols):
+        return None
+    t0 = time.time()
+    host_w = []
+    for t in weights:
+        h = t.cpu()
+        host_w.append(h.view(torch.int16).numpy().view(np.uint16) if h.dtype == torch.bfloat16
+                      else h.numpy())
+    host_s = [None if s is None else s.cpu().numpy() for s in states]
+    oc = oracle.Columns(w.cols, host_w, host_s)
+    Gh = G.cpu().numpy()
+    log(f"[bench] oracle inputs copied to host in {time.time() - t0:.1f}s")
+    t0 = time.perf_counter()
+    oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals)
+    if w.training:
+        oracle.backward(oc, w.batch, b.offsets, Gh, b.ids, b.fvals, opt=w.opt, lr=w.lr, eps=w.eps)
+    dt = time.perf_counter() - t0
+    valid = sum(per_col_counts(w, b)[0])
+    return {"value": round(valid / dt, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"one batch of the same workload ({b.n} positions, {valid} valid lookups, "
+                      f"all {len(w.cols)} columns), forward + backward + update, fp64 C, "
+                      f"1 thread: {dt:.2f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="front-end", choices=sorted(WORKLOADS))
+    ap.add_argument("--batches", type=int, default=4)
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(column-wise sharding with one all-to-all is designed, not built).", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

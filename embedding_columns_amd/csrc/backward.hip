@@ -353,46 +353,47 @@ __device__ __forceinline__ void seg_out(const BwdArgs &a, const DevCol &col, int
     }
 }
 
-template <int P>
-__device__ void bwd_piece(const BwdArgs &a, const BwdLds &L, const BTile &t, const DevCol &col,
-                          int c, int side, int u, const float (&sum)[4], int g, int q, bool qa)
+__device__ __forceinline__ void bwd_piece(const BwdArgs &a, const BwdLds &L, const BTile &t,
+                                          const DevCol &col, int c, int side, int u,
+                                          const float (&sum)[4], int leader, int q, bool qa)
 {
     const int64_t T = a.T;
     const int ss = segat(a, L, t, u), se = segat(a, L, t, u + 1);
     const int64_t k0 = ss / T, k1 = (se - 1) / T;
     const int64_t slot = t.k * 2 + side;
-    if (qa)
-        *reinterpret_cast<float4 *>(a.part + slot * a.maxD + q * 4) =
-            make_float4(sum[0], sum[1], sum[2], sum[3]);
-    __threadfence();
+    if (qa) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) st_agent(a.part + slot * a.maxD + q * 4 + v, sum[v]);
+    }
+    wait_vm();
     uint32_t old = 0;
-    if (q == 0) old = atomicAdd(&a.tick[k0], 1u);
-    old = __shfl(old, g * P, kWave);
+    if (q == 0) old = ticket_add(&a.tick[k0]);
+    old = __shfl(old, leader, kWave);
     if (old == (uint32_t)(k1 - k0)) {
-        __threadfence();
         float tot[4] = {0.f, 0.f, 0.f, 0.f};
         if (qa) {
             const float *p0 = a.part + (k0 * 2 + 1) * a.maxD + q * 4;
 #pragma unroll
-            for (int v = 0; v < 4; v++) tot[v] = p0[v];
+            for (int v = 0; v < 4; v++) tot[v] = ld_agent(p0 + v);
             for (int64_t kk = k0 + 1; kk <= k1; kk++) {
                 const float *pk = a.part + (kk * 2) * a.maxD + q * 4;
 #pragma unroll
-                for (int v = 0; v < 4; v++) tot[v] += pk[v];
+                for (int v = 0; v < 4; v++) tot[v] += ld_agent(pk + v);
             }
         }
         seg_out(a, col, c, u, tot, q, qa);
-        if (q == 0) a.tick[k0] = 0;
+        if (q == 0) st_agent(&a.tick[k0], 0u);
     }
 }
 
-template <int P>
-__device__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t, const DevCol &col, int c,
-                            int s0, int s1)
+// one column segment [s0, s1) of sorted contributors; P = lanes per gradient row
+__device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t,
+                                            const DevCol &col, int c, int s0, int s1)
 {
-    constexpr int G = kWave / P;
     constexpr int U = 8;
-    const int lane = lane_id(), g = lane / P, q = lane % P;
+    const int P = col.glanes, lp = __ffs(P) - 1;
+    const int G = kWave >> lp;
+    const int lane = lane_id(), g = lane >> lp, q = lane & (P - 1);
     const bool qa = q < col.dim / 4;
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
@@ -478,7 +479,7 @@ __device__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t, const D
             if (!L.hpass[g2]) { ended = true; break; }
         }
         if (ended) seg_out(a, col, c, tseg, sum, q, qa);
-        else bwd_piece<P>(a, L, t, col, c, 1, tseg, sum, g, q, qa);
+        else bwd_piece(a, L, t, col, c, 1, tseg, sum, g * P, q, qa);
     }
     if (g == 0 && hseg >= 0) {
         float sum[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
@@ -489,7 +490,7 @@ __device__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t, const D
             for (int v = 0; v < 4; v++) sum[v] += L.part[0][g2 * P + q][v];
             pass = L.hpass[g2];
         }
-        bwd_piece<P>(a, L, t, col, c, 0, hseg, sum, g, q, qa);
+        bwd_piece(a, L, t, col, c, 0, hseg, sum, 0, q, qa);
     }
     wave_sync();
 }
@@ -529,15 +530,7 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
             L.wt[p - t.t0] = col.pool == EMB_POOL_MEAN ? 1.0f / (float)a.bag_n[b] : 1.0f;
         }
         wave_sync();
-        switch (col.glanes) {
-        case 1: bwd_segment<1>(a, L, t, col, c, s0, s1); break;
-        case 2: bwd_segment<2>(a, L, t, col, c, s0, s1); break;
-        case 4: bwd_segment<4>(a, L, t, col, c, s0, s1); break;
-        case 8: bwd_segment<8>(a, L, t, col, c, s0, s1); break;
-        case 16: bwd_segment<16>(a, L, t, col, c, s0, s1); break;
-        case 32: bwd_segment<32>(a, L, t, col, c, s0, s1); break;
-        default: bwd_segment<64>(a, L, t, col, c, s0, s1); break;
-        }
+        bwd_segment(a, L, t, col, c, s0, s1);
         u = uend;
     }
 }

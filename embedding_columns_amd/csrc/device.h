@@ -34,6 +34,42 @@ __device__ __forceinline__ uint64_t mod_magic(uint64_t h, uint64_t d, uint64_t m
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Cross-workgroup exchange without cache flushes.  Stores and loads at agent
+// scope go to the device-coherent level (past the per-XCD L2) for these words
+// only; a full __threadfence() would write back and invalidate the whole L2.
+__device__ __forceinline__ void st_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t *p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t *p)
+{
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this wavefront's outstanding memory operations (stores included)
+// have completed, i.e. reached their coherence point
+__device__ __forceinline__ void wait_vm()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ uint32_t ticket_add(uint32_t *p)
+{
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Wavefront-level fence + barrier: makes one wavefront's LDS writes visible to

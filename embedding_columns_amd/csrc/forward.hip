@@ -127,10 +127,11 @@ __device__ __forceinline__ void accum(float (&acc)[V], const uint4 &w)
 
 // a piece of a bag that crosses a tile boundary: publish it, and if this is the
 // last piece to arrive, sum all pieces in tile order and write the bag
-template <int P, int V>
-__device__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t, const DevCol &col,
-                           int c, int side, int bag, const float (&sum)[V], int n, int g, int q,
-                           bool qa, int64_t &zero_bags)
+template <int V>
+__device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t,
+                                           const DevCol &col, int c, int side, int bag,
+                                           const float (&sum)[V], int n, int leader, int q, bool qa,
+                                           int64_t &zero_bags)
 {
     const int64_t T = a.T;
     const int bs = offat(a, L, t, bag), be = offat(a, L, t, bag + 1);
@@ -139,40 +140,41 @@ __device__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t,
     float *pp = a.part + slot * a.maxD + q * V;
     if (qa) {
 #pragma unroll
-        for (int v = 0; v < V; v += 4)
-            reinterpret_cast<float4 *>(pp)[v / 4] = make_float4(sum[v], sum[v + 1], sum[v + 2], sum[v + 3]);
+        for (int v = 0; v < V; v++) st_agent(pp + v, sum[v]);
     }
-    if (q == 0) a.pcnt[slot] = n;
-    __threadfence();
+    if (q == 0) st_agent(a.pcnt + slot, n);
+    wait_vm();                                   // the piece is visible before the ticket
     uint32_t old = 0;
-    if (q == 0) old = atomicAdd(&a.tick[k0], 1u);
-    old = __shfl(old, g * P, kWave);
+    if (q == 0) old = ticket_add(&a.tick[k0]);
+    old = __shfl(old, leader, kWave);
     if (old == (uint32_t)(k1 - k0)) {
-        __threadfence();
         float tot[V];
         const float *p0 = a.part + (k0 * 2 + 1) * a.maxD + q * V;
-        int tn = a.pcnt[k0 * 2 + 1];
+        int tn = ld_agent(a.pcnt + k0 * 2 + 1);
 #pragma unroll
-        for (int v = 0; v < V; v++) tot[v] = qa ? p0[v] : 0.f;
+        for (int v = 0; v < V; v++) tot[v] = qa ? ld_agent(p0 + v) : 0.f;
         for (int64_t kk = k0 + 1; kk <= k1; kk++) {
             const float *pk = a.part + (kk * 2) * a.maxD + q * V;
-            tn += a.pcnt[kk * 2];
+            tn += ld_agent(a.pcnt + kk * 2);
 #pragma unroll
-            for (int v = 0; v < V; v++) tot[v] += qa ? pk[v] : 0.f;
+            for (int v = 0; v < V; v++) tot[v] += qa ? ld_agent(pk + v) : 0.f;
         }
         bag_out<V>(a, col, c, bag, tot, tn, q, qa, zero_bags);
-        if (q == 0) a.tick[k0] = 0;   // ready for the next call
+        if (q == 0) st_agent(&a.tick[k0], 0u);   // ready for the next call
     }
 }
 
-template <int P, int V, bool BF>
-__device__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
-                            int c, int s0, int s1, int64_t &zero_bags)
+// one column segment [s0, s1) of the tile; P = lanes per row (a power of two)
+template <int V, bool BF>
+__device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
+                                            const DevCol &col, int c, int s0, int s1,
+                                            int64_t &zero_bags)
 {
-    constexpr int G = kWave / P;
     constexpr int U = 8;
     constexpr int ESZ = BF ? 2 : 4;
-    const int lane = lane_id(), g = lane / P, q = lane % P;
+    const int P = col.lanes, lp = __ffs(P) - 1;
+    const int G = kWave >> lp;
+    const int lane = lane_id(), g = lane >> lp, q = lane & (P - 1);
     const int D = col.dim;
     const bool qa = q < D / V;
     const int len = s1 - s0, Lg = (len + G - 1) / G;
@@ -269,7 +271,7 @@ __device__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t, cons
             if (!L.hpass[g2]) { ended = true; break; }
         }
         if (ended) bag_out<V>(a, col, c, tbag, sum, n, q, qa, zero_bags);
-        else tile_piece<P, V>(a, L, t, col, c, 1, tbag, sum, n, g, q, qa, zero_bags);
+        else tile_piece<V>(a, L, t, col, c, 1, tbag, sum, n, g * P, q, qa, zero_bags);
     }
     // the bag that came in from the previous tile
     if (g == 0 && hbag >= 0) {
@@ -285,7 +287,7 @@ __device__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t, cons
             n += L.hcnt[g2];
             pass = L.hpass[g2];
         }
-        tile_piece<P, V>(a, L, t, col, c, 0, hbag, sum, n, g, q, qa, zero_bags);
+        tile_piece<V>(a, L, t, col, c, 0, hbag, sum, n, 0, q, qa, zero_bags);
     }
     wave_sync();
 }
@@ -299,7 +301,7 @@ __device__ __forceinline__ int bucket_count(const float *b, int nb, float x)
     return k;
 }
 
-__device__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
+__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
                               int s0, int s1, int64_t (&cnt)[4])
 {
     const int lane = lane_id();
@@ -379,26 +381,8 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
             fwd_transform(a, L, t, col, s0, s1, cnt);
-            if (col.dtype == EMB_BF16) {
-                switch (col.lanes) {
-                case 1: fwd_segment<1, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 2: fwd_segment<2, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 4: fwd_segment<4, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 8: fwd_segment<8, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 16: fwd_segment<16, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                default: fwd_segment<32, 8, true>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                }
-            } else {
-                switch (col.lanes) {
-                case 1: fwd_segment<1, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 2: fwd_segment<2, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 4: fwd_segment<4, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 8: fwd_segment<8, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 16: fwd_segment<16, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                case 32: fwd_segment<32, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                default: fwd_segment<64, 4, false>(a, L, t, col, cu, s0, s1, zero_bags); break;
-                }
-            }
+            if (col.dtype == EMB_BF16) fwd_segment<8, true>(a, L, t, col, cu, s0, s1, zero_bags);
+            else fwd_segment<4, false>(a, L, t, col, cu, s0, s1, zero_bags);
         }
     }
 
