@@ -94,7 +94,7 @@ def run(args):
     cfg = WORKLOADS[args.workload]
     w = W.config(cfg)
     keyed = cfg == 5
-    training = w.training
+    training = w.training and not args.inference
     t0 = time.time()
     n_pool = args.batches if not keyed else args.warmup + args.steps
     batches = [W.make_batch(w, seed=1000 * cfg + i) for i in range(n_pool)]
@@ -131,20 +131,22 @@ def run(args):
     krows = torch.empty(max_ids, dtype=torch.int32, device=dev) if keyed else None
     kinds = {c.kind for c in w.cols}
 
+    tstats = stats if (args.stats or keyed) else None
+
     def step(i, ev=None):
         d = dbat[i % len(dbat)]
         n = d["n"]
         if keyed:
-            table.lookup_or_insert(d["ids"], rows_out=krows[:n], stats=stats)
+            table.lookup_or_insert(d["ids"], rows_out=krows[:n], stats=tstats)
         if ev is not None:
             ev[0].record()
         E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
                       d["fv"] if 2 in kinds else None, krows[:n] if keyed else None, n, Y,
-                      plan.workspace, training, stats)
+                      plan.workspace, training, tstats)
         if ev is not None:
             ev[1].record()
         if training:
-            E.emb_backward(plan.plan, G, plan.workspace, None, None, None, stats)
+            E.emb_backward(plan.plan, G, plan.workspace, None, None, None, tstats)
         if ev is not None:
             ev[2].record()
 
@@ -215,7 +217,7 @@ def run(args):
                    "positions_per_step": int(np.mean([batches[j].n for j in idx])),
                    "valid_lookups_per_step": int(lookups / args.steps),
                    "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
-                   "tile": plan.opts.tile or 512, "fwd_launches_per_step": 1},
+                   "tile": plan.opts.tile or 256, "fwd_launches_per_step": 1},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4) if training else 0.0,
@@ -223,6 +225,13 @@ def run(args):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None, "algorithmic_bytes": int(fb)},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, batches[0], plan, G, weights, states)
     print(json.dumps(out), flush=True)
@@ -268,6 +277,10 @@ def main():
     ap.add_argument("--batches", type=int, default=4)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats", action="store_true", help="collect the device counters while timing")
+    ap.add_argument("--inference", action="store_true", help="forward only (no backward)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

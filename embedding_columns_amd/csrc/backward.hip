@@ -282,8 +282,8 @@ struct BwdLds {
     int32_t smp[kTileMax];      // sample of each contributor
     float wt[kTileMax];         // pooling weight of each contributor
     uint32_t seg[kOffCap];      // window of segment starts
-    float part[2][kWave][4];
-    int32_t hseg[kWave], hpass[kWave], tseg[kWave];
+    float part[kWave][4];
+    int32_t hseg[kWave], hpass[kWave];
 };
 
 struct BTile {
@@ -294,7 +294,7 @@ struct BTile {
 __device__ __forceinline__ int segat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
 {
     const unsigned i = (unsigned)(u - t.wb);
-    return (int)(i < (unsigned)t.wn ? L.seg[i] : a.seg[u]);
+    return (int)(i < (unsigned)t.wn ? L.seg[i] : *gp(a.seg + u));
 }
 
 __device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const BTile &t, int p)
@@ -314,25 +314,26 @@ __device__ __forceinline__ void seg_out(const BwdArgs &a, const DevCol &col, int
     if (!qa) return;
     if (a.opt == EMB_OPT_EMIT) {
         if (a.ugrads)
-            *reinterpret_cast<float4 *>(a.ugrads + (int64_t)u * a.maxD + q * 4) =
+            *gp(reinterpret_cast<float4 *>(a.ugrads + (int64_t)u * a.maxD + q * 4)) =
                 make_float4(g[0], g[1], g[2], g[3]);
         return;
     }
-    const int64_t r = (int64_t)(a.ukeys[u] - col.row_base);
+    const int64_t r = (int64_t)(*gp(a.ukeys + u) - col.row_base);
     const int64_t e = r * col.dim + q * 4;
     float w[4];
     if (col.dtype == EMB_BF16) {
-        const uint2 raw = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(col.weights) + e);
-        w[0] = bf16_lo(raw.x); w[1] = bf16_hi(raw.x); w[2] = bf16_lo(raw.y); w[3] = bf16_hi(raw.y);
+        const uint64_t raw = *gp(reinterpret_cast<const uint64_t *>(static_cast<const uint16_t *>(col.weights) + e));
+        const uint32_t lo = (uint32_t)raw, hi = (uint32_t)(raw >> 32);
+        w[0] = bf16_lo(lo); w[1] = bf16_hi(lo); w[2] = bf16_lo(hi); w[3] = bf16_hi(hi);
     } else {
-        const float4 raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e);
+        const float4 raw = *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e));
         w[0] = raw.x; w[1] = raw.y; w[2] = raw.z; w[3] = raw.w;
     }
     if (a.opt == EMB_OPT_SGD) {
 #pragma unroll
         for (int v = 0; v < 4; v++) w[v] = w[v] - a.lr * g[v];
     } else {
-        float4 *sp = reinterpret_cast<float4 *>(col.state + e);
+        EMB_GLOBAL float4 *sp = gp(reinterpret_cast<float4 *>(col.state + e));
         float4 s = *sp;
         float acc[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
@@ -343,12 +344,11 @@ __device__ __forceinline__ void seg_out(const BwdArgs &a, const DevCol &col, int
         *sp = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
     if (col.dtype == EMB_BF16) {
-        uint2 o;
-        o.x = f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16);
-        o.y = f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(col.weights) + e) = o;
+        const uint64_t o = (uint64_t)(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16)) |
+                           ((uint64_t)(f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)) << 32);
+        *gp(reinterpret_cast<uint64_t *>(static_cast<uint16_t *>(col.weights) + e)) = o;
     } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e) =
+        *gp(reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e)) =
             make_float4(w[0], w[1], w[2], w[3]);
     }
 }
@@ -416,7 +416,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 wt[u2] = 0.f;
                 if (pp < ge) {
                     wt[u2] = L.wt[pp - t.t0];
-                    if (qa) x[u2] = *reinterpret_cast<const float4 *>(gbase + (int64_t)L.smp[pp - t.t0] * a.sumD);
+                    if (qa) x[u2] = *gp(reinterpret_cast<const float4 *>(gbase + (int64_t)L.smp[pp - t.t0] * a.sumD));
                 }
             }
 #pragma unroll
@@ -462,11 +462,10 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     }
 #pragma unroll
     for (int v = 0; v < 4; v++) {
-        L.part[0][lane][v] = hacc[v];
-        L.part[1][lane][v] = acc[v];
+        L.part[lane][v] = hacc[v];
     }
     if (q == 0) {
-        L.hseg[g] = hseg; L.hpass[g] = hpass; L.tseg[g] = tseg;
+        L.hseg[g] = hseg; L.hpass[g] = hpass;
     }
     wave_sync();
     if (tseg >= 0) {
@@ -475,7 +474,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
         for (int g2 = g + 1; g2 < G; g2++) {
             if (L.hseg[g2] != tseg) break;
 #pragma unroll
-            for (int v = 0; v < 4; v++) sum[v] += L.part[0][g2 * P + q][v];
+            for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             if (!L.hpass[g2]) { ended = true; break; }
         }
         if (ended) seg_out(a, col, c, tseg, sum, q, qa);
@@ -487,7 +486,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
         for (int g2 = 1; pass && g2 < G; g2++) {
             if (L.hseg[g2] != hseg) break;
 #pragma unroll
-            for (int v = 0; v < 4; v++) sum[v] += L.part[0][g2 * P + q][v];
+            for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             pass = L.hpass[g2];
         }
         bwd_piece(a, L, t, col, c, 0, hseg, sum, 0, q, qa);
@@ -511,7 +510,7 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
     t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
     t.wb = t.uf;
     t.wn = min(t.ul + 2 - t.uf, kOffCap);
-    for (int i = lane; i < t.wn; i += kWave) L.seg[i] = a.seg[t.wb + i];
+    for (int i = lane; i < t.wn; i += kWave) L.seg[i] = *gp(a.seg + t.wb + i);
     wave_sync();
     int u = t.uf;
     while (u <= t.ul) {
@@ -525,9 +524,9 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
         const int s0 = max(t.t0, segat(a, L, t, uu)), s1 = min(t.t1, segat(a, L, t, uend));
         // stage each contributor's sample and pooling weight
         for (int p = s0 + lane; p < s1; p += kWave) {
-            const int b = (int)a.sval[p];
+            const int b = (int)*gp(a.sval + p);
             L.smp[p - t.t0] = b - c * a.B;
-            L.wt[p - t.t0] = col.pool == EMB_POOL_MEAN ? 1.0f / (float)a.bag_n[b] : 1.0f;
+            L.wt[p - t.t0] = col.pool == EMB_POOL_MEAN ? 1.0f / (float)*gp(a.bag_n + b) : 1.0f;
         }
         wave_sync();
         bwd_segment(a, L, t, col, c, s0, s1);

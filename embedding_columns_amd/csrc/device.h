@@ -34,6 +34,25 @@ __device__ __forceinline__ uint64_t mod_magic(uint64_t h, uint64_t d, uint64_t m
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Pointers read from memory (column metadata) have no known address space, so
+// the compiler would emit flat loads, which also count against the LDS wait
+// counter and stall every later LDS access; these casts make them global.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define EMB_GLOBAL __attribute__((address_space(1)))
+#else
+#define EMB_GLOBAL   /* the host pass only type-checks device code */
+#endif
+template <typename T>
+__device__ __forceinline__ const EMB_GLOBAL T *gp(const T *p)
+{
+    return (const EMB_GLOBAL T *)p;
+}
+template <typename T>
+__device__ __forceinline__ EMB_GLOBAL T *gp(T *p)
+{
+    return (EMB_GLOBAL T *)p;
+}
+
 // Cross-workgroup exchange without cache flushes.  Stores and loads at agent
 // scope go to the device-coherent level (past the per-XCD L2) for these words
 // only; a full __threadfence() would write back and invalidate the whole L2.

@@ -51,11 +51,10 @@ struct WaveLds {
     int32_t rows[kTileMax];          // transformed row of each tile position
     int32_t off[kOffCap];            // window of CSR offsets
     union {
-        float part[2][kWave][8];     // per-lane head / tail partial sums
+        float part[kWave][4];        // per-lane partial sum of each run's first bag
         float bnd[kBndCap];          // bucket boundaries of the current column
     } x;
     int32_t hbag[kWave], hcnt[kWave], hpass[kWave];
-    int32_t tbag[kWave], tcnt[kWave];
 };
 
 struct TileCtx {
@@ -68,7 +67,7 @@ struct TileCtx {
 __device__ __forceinline__ int offat(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
 {
     const unsigned i = (unsigned)(b - t.wb);
-    return i < (unsigned)t.wn ? L.off[i] : a.off[b];
+    return i < (unsigned)t.wn ? L.off[i] : *gp(a.off + b);
 }
 
 // the non-empty bag containing position p (p inside the tile)
@@ -98,30 +97,16 @@ __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int
     const int s = bag - c * a.B;
     if (qa) {
         float o[V];
-        const bool mean = col.pool == EMB_POOL_MEAN;
+        const float sc = n == 0 ? 0.f : (col.pool == EMB_POOL_MEAN ? 1.0f / (float)n : 1.0f);
 #pragma unroll
-        for (int v = 0; v < V; v++) o[v] = n == 0 ? 0.f : (mean ? acc[v] / (float)n : acc[v]);
-        float4 *y = reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V);
+        for (int v = 0; v < V; v++) o[v] = acc[v] * sc;
+        EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V));
 #pragma unroll
         for (int v = 0; v < V; v += 4) y[v / 4] = make_float4(o[v], o[v + 1], o[v + 2], o[v + 3]);
     }
     if (q == 0) {
-        if (a.training) a.bag_n[bag] = n;
+        if (a.training) *gp(a.bag_n + bag) = n;
         zero_bags += (n == 0);
-    }
-}
-
-template <int V, bool BF>
-__device__ __forceinline__ void accum(float (&acc)[V], const uint4 &w)
-{
-    if constexpr (BF) {
-        acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
-        acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
-        acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
-        acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
-    } else {
-        acc[0] += __uint_as_float(w.x); acc[1] += __uint_as_float(w.y);
-        acc[2] += __uint_as_float(w.z); acc[3] += __uint_as_float(w.w);
     }
 }
 
@@ -164,14 +149,16 @@ __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, c
     }
 }
 
-// one column segment [s0, s1) of the tile; P = lanes per row (a power of two)
-template <int V, bool BF>
+// one column segment [s0, s1) of the tile.  A row is read by P lanes (a power
+// of two), 4 elements per lane: 16-byte loads for fp32 rows, 8-byte for bf16.
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
                                             int64_t &zero_bags)
 {
-    constexpr int U = 8;
-    constexpr int ESZ = BF ? 2 : 4;
+    constexpr int V = 4;
+    constexpr int U = 8;                       // row loads in flight per lane
+    const bool bf = col.dtype == EMB_BF16;
+    const int esz = bf ? 2 : 4;
     const int P = col.lanes, lp = __ffs(P) - 1;
     const int G = kWave >> lp;
     const int lane = lane_id(), g = lane >> lp, q = lane & (P - 1);
@@ -179,7 +166,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     const bool qa = q < D / V;
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
-    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)q * V * ESZ;
+    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)q * V * esz;
+    const int64_t rstride = (int64_t)D * esz;
 
     float acc[V], hacc[V];
 #pragma unroll
@@ -193,14 +181,23 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
         bool before = offat(a, L, t, b) < ga;
         for (int p = ga; p < ge; p += U) {
             int r[U];
-            uint4 w[U];
+            float4 w[U];
 #pragma unroll
             for (int u = 0; u < U; u++) r[u] = (p + u < ge) ? L.rows[p + u - t.t0] : -1;
+            if (bf) {
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                w[u] = make_uint4(0, 0, 0, 0);
-                if (r[u] >= 0 && qa)
-                    w[u] = *reinterpret_cast<const uint4 *>(wbase + (int64_t)r[u] * D * ESZ);
+                for (int u = 0; u < U; u++) {
+                    uint64_t h = 0;
+                    if (r[u] >= 0 && qa) h = *gp(reinterpret_cast<const uint64_t *>(wbase + r[u] * rstride));
+                    const uint32_t lo = (uint32_t)h, hi = (uint32_t)(h >> 32);
+                    w[u] = make_float4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi));
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    w[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (r[u] >= 0 && qa) w[u] = *gp(reinterpret_cast<const float4 *>(wbase + r[u] * rstride));
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {
@@ -221,7 +218,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                         bend = offat(a, L, t, b + 1);
                         before = false;
                     }
-                    accum<V, BF>(acc, w[u]);
+                    acc[0] += w[u].x; acc[1] += w[u].y; acc[2] += w[u].z; acc[3] += w[u].w;
                     cnt += (r[u] != -1);
                 }
             }
@@ -247,12 +244,10 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     // publish the run's boundary pieces
 #pragma unroll
     for (int v = 0; v < V; v++) {
-        L.x.part[0][lane][v] = hacc[v];
-        L.x.part[1][lane][v] = acc[v];
+        L.x.part[lane][v] = hacc[v];
     }
     if (q == 0) {
         L.hbag[g] = hbag; L.hcnt[g] = hcnt; L.hpass[g] = hpass;
-        L.tbag[g] = tbag; L.tcnt[g] = cnt;
     }
     wave_sync();
 
@@ -266,7 +261,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
         for (int g2 = g + 1; g2 < G; g2++) {
             if (L.hbag[g2] != tbag) break;
 #pragma unroll
-            for (int v = 0; v < V; v++) sum[v] += L.x.part[0][g2 * P + q][v];
+            for (int v = 0; v < V; v++) sum[v] += L.x.part[g2 * P + q][v];
             n += L.hcnt[g2];
             if (!L.hpass[g2]) { ended = true; break; }
         }
@@ -283,7 +278,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
         for (int g2 = 1; pass && g2 < G; g2++) {
             if (L.hbag[g2] != hbag) break;
 #pragma unroll
-            for (int v = 0; v < V; v++) sum[v] += L.x.part[0][g2 * P + q][v];
+            for (int v = 0; v < V; v++) sum[v] += L.x.part[g2 * P + q][v];
             n += L.hcnt[g2];
             pass = L.hpass[g2];
         }
@@ -292,7 +287,9 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     wave_sync();
 }
 
-__device__ __forceinline__ int bucket_count(const float *b, int nb, float x)
+// #{j : b[j] <= x} for sorted b, by binary lifting (B is an LDS or a global array)
+template <typename B>
+__device__ __forceinline__ int bucket_count(B b, int nb, float x)
 {
     int k = 0;
     int step = nb ? (1 << (31 - __clz(nb))) : 0;
@@ -301,32 +298,35 @@ __device__ __forceinline__ int bucket_count(const float *b, int nb, float x)
     return k;
 }
 
-__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t, const DevCol &col,
-                              int s0, int s1, int64_t (&cnt)[4])
+constexpr int kMargin = 64;             // offsets staged before the tile's first bag
+
+__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
+                                              const DevCol &col, int s0, int s1,
+                                              int64_t (&cnt)[4])
 {
     const int lane = lane_id();
-    const float *bp = col.boundaries;
     const int nbd = col.n_bnd;
-    if (col.kind == EMB_COL_BUCKET && nbd <= kBndCap) {
-        for (int i = lane; i < nbd; i += kWave) L.x.bnd[i] = col.boundaries[i];
+    const bool staged = col.kind == EMB_COL_BUCKET && nbd <= kBndCap;
+    if (staged) {
+        for (int i = lane; i < nbd; i += kWave) L.x.bnd[i] = *gp(col.boundaries + i);
         wave_sync();
-        bp = L.x.bnd;
     }
     const uint64_t rows = (uint64_t)col.rows;
     for (int p = s0 + lane; p < s1; p += kWave) {
         int r;
         if (col.kind == EMB_COL_HASH) {
-            const int64_t id = a.ids[p];
+            const int64_t id = *gp(a.ids + p);
             r = (id >= col.id_lo && id < col.id_hi)
                     ? (int)mod_magic(splitmix64((uint64_t)id), rows, col.magic) : -1;
         } else if (col.kind == EMB_COL_IDENTITY) {
-            const int64_t id = a.ids[p];
+            const int64_t id = *gp(a.ids + p);
             r = (id >= 0 && (uint64_t)id < rows) ? (int)id : -1;
         } else if (col.kind == EMB_COL_BUCKET) {
-            const float x = a.fvals[p];
-            r = (x != x) ? -1 : bucket_count(bp, nbd, x);
+            const float x = *gp(a.fvals + p);
+            r = (x != x) ? -1 : (staged ? bucket_count(L.x.bnd, nbd, x)
+                                        : bucket_count(gp(col.boundaries), nbd, x));
         } else {
-            const int kr = a.krows[p];
+            const int kr = *gp(a.krows + p);
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
         L.rows[p - t.t0] = r;
@@ -335,9 +335,9 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
         cnt[2] += (r == -1);
         cnt[3] += (r == -2);
         if (a.training) {
-            a.keys[p] = r >= 0 ? col.row_base + (uint32_t)r
-                               : (r == -2 ? a.total_rows + 1u : a.total_rows);
-            a.bags[p] = bag_of(a, L, t, p);
+            *gp(a.keys + p) = r >= 0 ? col.row_base + (uint32_t)r
+                                     : (r == -2 ? a.total_rows + 1u : a.total_rows);
+            *gp(a.bags + p) = bag_of(a, L, t, p);
         }
     }
     wave_sync();
@@ -355,25 +355,44 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
     t.t0 = (int)min<int64_t>(t.k * T, N);
     t.t1 = (int)min<int64_t>((t.k + 1) * T, N);
     const bool last = t.k == a.ntiles - 1;
+
+    // the bags this tile touches: one global search for the first, then the
+    // offsets window in LDS answers the rest
+    int own_lo, own_hi;
     if (t.t0 < t.t1) {
         t.bf = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t0) - 1;
-        t.bl = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t1 - 1) - 1;
+        t.wb = max(0, t.bf - kMargin);
     } else {
         t.bf = nbag;
-        t.bl = nbag - 1;
+        t.wb = 0;
     }
-    const int own_lo = (int)wave_lower_bound(a.off, (int64_t)nbag + 1, t.t0);
-    const int own_hi = last ? nbag : min((int)wave_lower_bound(a.off, (int64_t)nbag + 1, t.t1), nbag);
-    t.wb = min(t.bf, own_lo);
-    const int we = min(max(t.bl + 2, own_hi + 1), nbag + 1);
-    t.wn = min(we - t.wb, kOffCap);
-    for (int i = lane; i < t.wn; i += kWave) L.off[i] = a.off[t.wb + i];
+    t.wn = min(nbag + 1 - t.wb, kOffCap);
+    for (int i = lane; i < t.wn; i += kWave) L.off[i] = *gp(a.off + t.wb + i);
     wave_sync();
+    if (t.t0 < t.t1) {
+        const int f = t.bf - t.wb;
+        if (L.off[t.wn - 1] > t.t1 - 1)
+            t.bl = t.bf + (int)wave_upper_bound(L.off + f, (int64_t)(t.wn - f), t.t1 - 1) - 1;
+        else
+            t.bl = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t1 - 1) - 1;
+        // owned bags start in [t0, t1): empty bags sitting exactly at t0 come first
+        own_lo = t.bf + 1;
+        if (offat(a, L, t, t.bf) == t.t0) {
+            own_lo = t.bf;
+            while (own_lo > 0 && offat(a, L, t, own_lo - 1) == t.t0) own_lo--;
+        }
+        own_hi = last ? nbag : t.bl + 1;
+    } else {
+        t.bl = nbag - 1;
+        own_lo = 0;
+        own_hi = nbag;
+    }
 
     int64_t cnt[4] = {0, 0, 0, 0};
     int64_t zero_bags = 0;
     if (t.t0 < t.t1) {
         const int c_first = t.bf / a.B, c_last = t.bl / a.B;
+        // transform every position of the tile, then walk each column segment
         for (int c = c_first; c <= c_last; c++) {
             const int cu = uniform(c);
             const int s0 = max(t.t0, offat(a, L, t, cu * a.B));
@@ -381,8 +400,14 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
             fwd_transform(a, L, t, col, s0, s1, cnt);
-            if (col.dtype == EMB_BF16) fwd_segment<8, true>(a, L, t, col, cu, s0, s1, zero_bags);
-            else fwd_segment<4, false>(a, L, t, col, cu, s0, s1, zero_bags);
+        }
+        for (int c = c_first; c <= c_last; c++) {
+            const int cu = uniform(c);
+            const int s0 = max(t.t0, offat(a, L, t, cu * a.B));
+            const int s1 = min(t.t1, offat(a, L, t, (cu + 1) * a.B));
+            if (s0 >= s1) continue;
+            const DevCol col = a.cols[cu];
+            fwd_segment(a, L, t, col, cu, s0, s1, zero_bags);
         }
     }
 
@@ -390,10 +415,11 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
     for (int b = own_lo + lane; b < own_hi; b += kWave) {
         if (offat(a, L, t, b) != offat(a, L, t, b + 1)) continue;
         const int c = b / a.B;
-        const DevCol &col = a.cols[c];
-        float4 *y = reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD + col.out_off);
-        for (int d = 0; d < col.dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (a.training) a.bag_n[b] = 0;
+        EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD +
+                                                             *gp(&a.cols[c].out_off)));
+        const int dim = *gp(&a.cols[c].dim);
+        for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.training) *gp(a.bag_n + b) = 0;
         zero_bags++;
     }
 

@@ -12,10 +12,10 @@ namespace emb {
 constexpr int kWave = 64;            // CDNA wavefront
 constexpr int kWavesPerBlock = 4;    // each wavefront owns one tile; no block-wide barriers
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kTileMax = 512;        // positions (or sorted contributors) per wavefront tile
-constexpr int kTileDefault = 512;
-constexpr int kOffCap = kTileMax + 64;   // LDS window of segment offsets per wavefront
-constexpr int kBndCap = 1024;            // bucket boundaries staged in LDS
+constexpr int kTileMax = 256;        // positions (or sorted contributors) per wavefront tile
+constexpr int kTileDefault = 256;
+constexpr int kOffCap = kTileMax + 128;  // LDS window of segment offsets per wavefront
+constexpr int kBndCap = 256;             // bucket boundaries staged in LDS (more: read from memory)
 constexpr int kMaxDimF32 = 256;
 constexpr int kMaxDimBF16 = 512;
 
@@ -37,9 +37,9 @@ struct DevCol {
     int32_t n_bnd;
     int32_t out_off;         // first output column of this embedding column
     uint32_t row_base;       // sum of rows of the columns before this one
-    int32_t lanes;           // lanes per row: pow2 >= dim / vec
-    int32_t vec;             // elements per lane per 16-byte load: 4 (fp32) or 8 (bf16)
-    int32_t glanes;          // lanes per gradient row (fp32, 4 per lane): pow2 >= dim / 4
+    int32_t lanes;           // lanes per row, 4 elements each: pow2 >= dim / 4
+    int32_t vec;             // elements per lane (4)
+    int32_t glanes;          // lanes per gradient row (same as lanes)
 };
 static_assert(sizeof(DevCol) == 96, "DevCol layout");
 

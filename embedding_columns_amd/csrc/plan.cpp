@@ -49,7 +49,7 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
     if (opts->opt < EMB_OPT_EMIT || opts->opt > EMB_OPT_ADAGRAD)
         return fail(EMB_ERR_INVALID_ARG, "unknown optimizer");
     if (opts->tile != 0 && (opts->tile % kWave != 0 || opts->tile < kWave || opts->tile > kTileMax))
-        return fail(EMB_ERR_INVALID_ARG, "tile must be 0 or a multiple of 64 in [64, 512]");
+        return fail(EMB_ERR_INVALID_ARG, "tile must be 0 or a multiple of 64 in [64, 256]");
     if (opts->opt != EMB_OPT_EMIT && !(opts->lr >= 0.f && std::isfinite(opts->lr)))
         return fail(EMB_ERR_INVALID_ARG, "lr must be finite and >= 0");
     if (opts->opt == EMB_OPT_ADAGRAD && !(opts->eps >= 0.f && std::isfinite(opts->eps)))
@@ -67,10 +67,8 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
         if (d.dim <= 0) return fail(EMB_ERR_INVALID_ARG, at + "dim must be >= 1");
         if (d.dtype == EMB_F32 && (d.dim % 4 != 0 || d.dim > kMaxDimF32))
             return fail(EMB_ERR_UNSUPPORTED, at + "fp32 dim must be a multiple of 4 and <= 256");
-        if (d.dtype == EMB_BF16 && (d.dim % 8 != 0 || d.dim > kMaxDimBF16))
-            return fail(EMB_ERR_UNSUPPORTED, at + "bf16 dim must be a multiple of 8 and <= 512");
-        if (d.dtype == EMB_BF16 && d.dim > kMaxDimF32)
-            return fail(EMB_ERR_UNSUPPORTED, at + "bf16 dim above 256 is not supported by the backward");
+        if (d.dtype == EMB_BF16 && (d.dim % 4 != 0 || d.dim > kMaxDimF32))
+            return fail(EMB_ERR_UNSUPPORTED, at + "bf16 dim must be a multiple of 4 and <= 256");
         if (d.kind == EMB_COL_HASH && d.id_lo >= d.id_hi) return fail(EMB_ERR_INVALID_ARG, at + "id_lo must be < id_hi");
         if (d.kind == EMB_COL_BUCKET) {
             if (d.n_boundaries < 0 || (d.n_boundaries > 0 && !d.boundaries))
@@ -168,8 +166,8 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         h.n_bnd = (int32_t)d.n_boundaries;
         h.out_off = off;
         h.row_base = (uint32_t)row_base;
-        h.vec = d.dtype == EMB_BF16 ? 8 : 4;
-        h.lanes = pow2_ceil(d.dim / h.vec);
+        h.vec = 4;
+        h.lanes = pow2_ceil(d.dim / 4);
         h.glanes = pow2_ceil(d.dim / 4);
         row_base += (uint64_t)d.rows;
         off += d.dim;

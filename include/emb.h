@@ -92,7 +92,7 @@ typedef struct emb_column_desc {
     int32_t kind;              /* EMB_COL_*                                             */
     int32_t pool;              /* EMB_POOL_*                                            */
     int32_t dtype;             /* EMB_F32 | EMB_BF16 (KEYED: EMB_F32)                    */
-    int32_t dim;               /* D: fp32 multiple of 4, <= 256; bf16 multiple of 8, <= 512 */
+    int32_t dim;               /* D: a multiple of 4, <= 256                              */
     int64_t rows;              /* table rows, 1 .. 2^31-1                               */
     int64_t id_lo, id_hi;      /* HASH: valid raw IDs are [id_lo, id_hi)                  */
     const float *boundaries;   /* BUCKET: device, sorted ascending fp32                 */
@@ -105,7 +105,7 @@ typedef struct emb_plan_opts {
     int32_t opt;               /* EMB_OPT_*                                            */
     float lr;                  /* learning rate (SGD, ADAGRAD)                          */
     float eps;                 /* ADAGRAD epsilon, outside the square root              */
-    int32_t tile;              /* positions per wavefront tile: 0 = default, else a multiple of 64 <= 1024 */
+    int32_t tile;              /* positions per wavefront tile: 0 = default (256), else a multiple of 64 <= 256 */
 } emb_plan_opts;
 
 typedef struct emb_plan emb_plan;    /* host object owned by the library */

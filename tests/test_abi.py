@@ -67,7 +67,8 @@ def test_plan_query_accepts_a_valid_plan(L):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(dim=6), 2, "multiple of 4"),
     (dict(dim=260), 2, "<= 256"),
-    (dict(dtype=1, dim=12), 2, "multiple of 8"),
+    (dict(dtype=1, dim=14), 2, "multiple of 4"),
+    (dict(dtype=1, dim=264), 2, "<= 256"),
     (dict(rows=0), 1, "rows"),
     (dict(rows=1 << 31), 1, "rows"),
     (dict(kind=7), 1, "kind"),

@@ -17,13 +17,13 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("tile", [64, 512])
+@pytest.mark.parametrize("tile", [64, 256])
 def test_tiny_fused_bag_emit(tile):
     # 8 hashed columns, B=256, 1000 x 16 fp32 tables, bags of 1..4, EMIT of row grads
     run_dense_case(W.config(1), seed=1001, tile=tile)
 
 
-@pytest.mark.parametrize("tile", [64, 192, 512])
+@pytest.mark.parametrize("tile", [64, 192, 256])
 def test_training_front_end_sgd(tile):
     # Poisson(3) bags, 5 % forced empty, 2 % invalid IDs, sum/mean, dims 8..64, SGD
     w = W.config(2, n_cols=24, batch=512, rows_range=(1e2, 1e4))
@@ -48,7 +48,7 @@ def test_many_tiny_columns_backward():
     run_dense_case(w, seed=3004, tile=64)
 
 
-@pytest.mark.parametrize("tile", [128, 512])
+@pytest.mark.parametrize("tile", [128, 256])
 def test_long_sequences_bf16_adagrad(tile):
     # bags of 200..2000 IDs over 4 identity columns, bf16 tables, mean, Adagrad
     w = W.config(4, n_cols=4, batch=40, rows=100_000)
@@ -122,7 +122,7 @@ def test_all_bags_empty():
     assert torch.count_nonzero(Y) == 0
 
 
-@pytest.mark.parametrize("tile", [64, 512])
+@pytest.mark.parametrize("tile", [64, 256])
 def test_one_bag_spanning_many_tiles(tile):
     # one 5000-position bag between empty bags: pieces from ~80 tiles combine
     lens = [0, 5000, 0, 3, 0, 0]
