@@ -178,27 +178,48 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
 
 // -------------------------------------------------------------- unique rows
 
+// keys of one 4096-key block, read coalesced into LDS; key[-1] = the key before the block
+struct UqLds {
+    uint32_t key[kSortTile + 1];
+    uint32_t tmp[kWavesPerBlock];
+};
+
+__device__ __forceinline__ int uq_stage(UqLds &S, const uint32_t *k, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int cnt = (int)min<int64_t>(kSortTile, n - base);
+    for (int i = threadIdx.x; i < cnt; i += kBlock) S.key[i + 1] = *gp(k + base + i);
+    if (threadIdx.x == 0) S.key[0] = base > 0 ? *gp(k + base - 1) : 0xFFFFFFFFu;
+    __syncthreads();
+    return cnt;
+}
+
+// a segment head: a valid key that differs from its predecessor
+__device__ __forceinline__ bool uq_head(const UqLds &S, int i, uint32_t total_rows, bool first)
+{
+    const uint32_t x = S.key[i + 1];
+    return x < total_rows && (first || S.key[i] != x);
+}
+
 __global__ __launch_bounds__(kBlock) void uq_count(const uint32_t *__restrict__ k, int64_t n,
                                                   uint32_t total_rows, uint32_t *__restrict__ ucnt,
                                                   uint32_t *__restrict__ misc)
 {
-    __shared__ uint32_t tmp[kWavesPerBlock];
-    const int t = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
+    __shared__ UqLds S;
+    const int cnt = uq_stage(S, k, n);
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
     uint32_t c = 0;
-    for (int j = 0; j < kSortItems; j++) {
-        const int64_t i = base + j;
-        if (i >= n) break;
-        const uint32_t x = k[i];
-        const uint32_t p = i > 0 ? k[i - 1] : 0xFFFFFFFFu;
-        c += (x < total_rows) && (i == 0 || p != x);
+    for (int i = threadIdx.x; i < cnt; i += kBlock) {
+        const bool first = base + i == 0;
+        c += uq_head(S, i, total_rows, first);
+        const uint32_t x = S.key[i + 1];
         // the first sentinel key marks the end of the valid contributors
-        if (x >= total_rows && (i == 0 || p < total_rows)) misc[0] = (uint32_t)i;
-        if (i == n - 1 && x < total_rows) misc[0] = (uint32_t)n;
+        if (x >= total_rows && (first || S.key[i] < total_rows)) *gp(misc) = (uint32_t)(base + i);
+        if (base + i == n - 1 && x < total_rows) *gp(misc) = (uint32_t)n;
     }
     uint32_t ex;
-    const uint32_t tot = block_exclusive_scan(c, tmp, ex);
-    if (t == 0) ucnt[blockIdx.x] = tot;
+    const uint32_t tot = block_exclusive_scan(c, S.tmp, ex);
+    if (threadIdx.x == 0) ucnt[blockIdx.x] = tot;
 }
 
 __global__ __launch_bounds__(kBlock) void uq_scan(const uint32_t *__restrict__ ucnt, int64_t nblk,
@@ -231,31 +252,30 @@ __global__ __launch_bounds__(kBlock) void uq_write(const uint32_t *__restrict__ 
                                                   uint32_t *__restrict__ ukeys,
                                                   uint32_t *__restrict__ user_keys)
 {
-    __shared__ uint32_t tmp[kWavesPerBlock];
-    const int t = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
+    __shared__ UqLds S;
+    const int cnt = uq_stage(S, k, n);
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    // each thread owns kSortItems consecutive keys, so ranks follow key order
+    const int i0 = threadIdx.x * kSortItems;
     uint32_t c = 0;
     for (int j = 0; j < kSortItems; j++) {
-        const int64_t i = base + j;
-        if (i >= n) break;
-        const uint32_t x = k[i];
-        c += (x < total_rows) && (i == 0 || k[i - 1] != x);
+        const int i = i0 + j;
+        if (i < cnt) c += uq_head(S, i, total_rows, base + i == 0);
     }
     uint32_t ex;
-    block_exclusive_scan(c, tmp, ex);
-    uint32_t u = uscan[blockIdx.x] + ex;
+    block_exclusive_scan(c, S.tmp, ex);
+    uint32_t u = *gp(uscan + blockIdx.x) + ex;
     for (int j = 0; j < kSortItems; j++) {
-        const int64_t i = base + j;
-        if (i >= n) break;
-        const uint32_t x = k[i];
-        if ((x < total_rows) && (i == 0 || k[i - 1] != x)) {
-            seg[u] = (uint32_t)i;
-            ukeys[u] = x;
-            if (user_keys) user_keys[u] = x;
+        const int i = i0 + j;
+        if (i < cnt && uq_head(S, i, total_rows, base + i == 0)) {
+            const uint32_t x = S.key[i + 1];
+            *gp(seg + u) = (uint32_t)(base + i);
+            *gp(ukeys + u) = x;
+            if (user_keys) *gp(user_keys + u) = x;
             u++;
         }
     }
-    if (blockIdx.x == 0 && t == 0) seg[misc[1]] = misc[0];   // seg[U] = number of valid contributors
+    if (blockIdx.x == 0 && threadIdx.x == 0) seg[misc[1]] = misc[0];   // seg[U] = valid contributors
 }
 
 // ------------------------------------------------------- segment-sum + apply
@@ -276,25 +296,33 @@ struct BwdArgs {
     float *part;
     int32_t *pcnt;
     uint32_t *tick;
+    int32_t any_mean;           // some column pools by mean
 };
 
 struct BwdLds {
-    int32_t smp[kTileMax];      // sample of each contributor
+    int32_t bag[kTileMax];      // bag of each contributor of the tile
     float wt[kTileMax];         // pooling weight of each contributor
     uint32_t seg[kOffCap];      // window of segment starts
+    uint32_t ukey[kOffCap];     // unique keys of the same segments
     float part[kWave][4];
     int32_t hseg[kWave], hpass[kWave];
 };
 
 struct BTile {
     int64_t k;
-    int t0, t1, uf, ul, wb, wn;
+    int t0, t1, uf, ul, wb, wn, U;
 };
 
 __device__ __forceinline__ int segat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
 {
     const unsigned i = (unsigned)(u - t.wb);
     return (int)(i < (unsigned)t.wn ? L.seg[i] : *gp(a.seg + u));
+}
+
+__device__ __forceinline__ uint32_t ukeyat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
+{
+    const unsigned i = (unsigned)(u - t.wb);
+    return i < (unsigned)t.wn ? L.ukey[i] : *gp(a.ukeys + u);
 }
 
 __device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const BTile &t, int p)
@@ -307,54 +335,81 @@ __device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const B
     return lo;
 }
 
-// the finished gradient g (4 fp32 per lane) of unique row u: emit or update
-__device__ __forceinline__ void seg_out(const BwdArgs &a, const DevCol &col, int c, int u,
-                                       const float (&g)[4], int q, bool qa)
+// A table row slice (4 elements per lane) and its Adagrad accumulator, read
+// when a segment starts so that the update at its end does not wait.
+struct RowPre {
+    float w[4], s[4];
+};
+
+__device__ __forceinline__ void row_load(const BwdArgs &a, const DevCol &col, int64_t e, RowPre &r)
 {
-    if (!qa) return;
+    if (a.opt == EMB_OPT_EMIT) return;
+    if (col.dtype == EMB_BF16) {
+        const uint64_t raw = *gp(reinterpret_cast<const uint64_t *>(static_cast<const uint16_t *>(col.weights) + e));
+        const uint32_t lo = (uint32_t)raw, hi = (uint32_t)(raw >> 32);
+        r.w[0] = bf16_lo(lo); r.w[1] = bf16_hi(lo); r.w[2] = bf16_lo(hi); r.w[3] = bf16_hi(hi);
+    } else {
+        const float4 raw = *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e));
+        r.w[0] = raw.x; r.w[1] = raw.y; r.w[2] = raw.z; r.w[3] = raw.w;
+    }
+    if (a.opt == EMB_OPT_ADAGRAD) {
+        const float4 sv = *gp(reinterpret_cast<const float4 *>(col.state + e));
+        r.s[0] = sv.x; r.s[1] = sv.y; r.s[2] = sv.z; r.s[3] = sv.w;
+    }
+}
+
+// the finished gradient g of unique row u (4 fp32 per lane): emit it, or
+// update the row whose old values are in `r`
+__device__ __forceinline__ void row_apply(const BwdArgs &a, const DevCol &col, int u, int64_t e,
+                                          const float (&g)[4], RowPre &r, int q)
+{
     if (a.opt == EMB_OPT_EMIT) {
         if (a.ugrads)
             *gp(reinterpret_cast<float4 *>(a.ugrads + (int64_t)u * a.maxD + q * 4)) =
                 make_float4(g[0], g[1], g[2], g[3]);
         return;
     }
-    const int64_t r = (int64_t)(*gp(a.ukeys + u) - col.row_base);
-    const int64_t e = r * col.dim + q * 4;
-    float w[4];
-    if (col.dtype == EMB_BF16) {
-        const uint64_t raw = *gp(reinterpret_cast<const uint64_t *>(static_cast<const uint16_t *>(col.weights) + e));
-        const uint32_t lo = (uint32_t)raw, hi = (uint32_t)(raw >> 32);
-        w[0] = bf16_lo(lo); w[1] = bf16_hi(lo); w[2] = bf16_lo(hi); w[3] = bf16_hi(hi);
-    } else {
-        const float4 raw = *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e));
-        w[0] = raw.x; w[1] = raw.y; w[2] = raw.z; w[3] = raw.w;
-    }
     if (a.opt == EMB_OPT_SGD) {
 #pragma unroll
-        for (int v = 0; v < 4; v++) w[v] = w[v] - a.lr * g[v];
+        for (int v = 0; v < 4; v++) r.w[v] = r.w[v] - a.lr * g[v];
     } else {
-        EMB_GLOBAL float4 *sp = gp(reinterpret_cast<float4 *>(col.state + e));
-        float4 s = *sp;
-        float acc[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            acc[v] = acc[v] + g[v] * g[v];
-            w[v] = w[v] - a.lr * g[v] / (sqrtf(acc[v]) + a.eps);
+            r.s[v] = r.s[v] + g[v] * g[v];
+            r.w[v] = r.w[v] - a.lr * g[v] / (sqrtf(r.s[v]) + a.eps);
         }
-        *sp = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *gp(reinterpret_cast<float4 *>(col.state + e)) = make_float4(r.s[0], r.s[1], r.s[2], r.s[3]);
     }
     if (col.dtype == EMB_BF16) {
-        const uint64_t o = (uint64_t)(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16)) |
-                           ((uint64_t)(f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)) << 32);
+        const uint64_t o = (uint64_t)(f32_to_bf16_rne(r.w[0]) | (f32_to_bf16_rne(r.w[1]) << 16)) |
+                           ((uint64_t)(f32_to_bf16_rne(r.w[2]) | (f32_to_bf16_rne(r.w[3]) << 16)) << 32);
         *gp(reinterpret_cast<uint64_t *>(static_cast<uint16_t *>(col.weights) + e)) = o;
     } else {
         *gp(reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e)) =
-            make_float4(w[0], w[1], w[2], w[3]);
+            make_float4(r.w[0], r.w[1], r.w[2], r.w[3]);
     }
 }
 
+__device__ __forceinline__ int64_t row_elem(const BwdArgs &a, const BwdLds &L, const BTile &t,
+                                            const DevCol &col, int u, int q)
+{
+    return (int64_t)(ukeyat(a, L, t, u) - col.row_base) * col.dim + q * 4;
+}
+
+// a segment that finished in another place than where it started: load its
+// row now and apply
+__device__ __forceinline__ void seg_out(const BwdArgs &a, const BwdLds &L, const BTile &t,
+                                       const DevCol &col, int u, const float (&g)[4], int q, bool qa)
+{
+    if (!qa) return;
+    const int64_t e = row_elem(a, L, t, col, u, q);
+    RowPre r;
+    row_load(a, col, e, r);
+    row_apply(a, col, u, e, g, r, q);
+}
+
 __device__ __forceinline__ void bwd_piece(const BwdArgs &a, const BwdLds &L, const BTile &t,
-                                          const DevCol &col, int c, int side, int u,
+                                          const DevCol &col, int side, int u,
                                           const float (&sum)[4], int leader, int q, bool qa)
 {
     const int64_t T = a.T;
@@ -381,12 +436,12 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, const BwdLds &L, con
                 for (int v = 0; v < 4; v++) tot[v] += ld_agent(pk + v);
             }
         }
-        seg_out(a, col, c, u, tot, q, qa);
+        seg_out(a, L, t, col, u, tot, q, qa);
         if (q == 0) st_agent(&a.tick[k0], 0u);
     }
 }
 
-// one column segment [s0, s1) of sorted contributors; P = lanes per gradient row
+// one column run [s0, s1) of sorted contributors; P lanes per gradient row
 __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t,
                                             const DevCol &col, int c, int s0, int s1)
 {
@@ -398,6 +453,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
     const float *gbase = a.G + col.out_off + q * 4;
+    const int cB = c * a.B;
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f}, hacc[4] = {0.f, 0.f, 0.f, 0.f};
     int hseg = -1, tseg = -1;
@@ -406,6 +462,12 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
         int u = seg_of(a, L, t, ga);
         int uend = segat(a, L, t, u + 1);
         bool before = segat(a, L, t, u) < ga;
+        int64_t e = 0;
+        RowPre pre;
+        if (!before && qa) {
+            e = row_elem(a, L, t, col, u, q);
+            row_load(a, col, e, pre);
+        }
         for (int p = ga; p < ge; p += U) {
             float4 x[U];
             float wt[U];
@@ -416,7 +478,9 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 wt[u2] = 0.f;
                 if (pp < ge) {
                     wt[u2] = L.wt[pp - t.t0];
-                    if (qa) x[u2] = *gp(reinterpret_cast<const float4 *>(gbase + (int64_t)L.smp[pp - t.t0] * a.sumD));
+                    if (qa)
+                        x[u2] = *gp(reinterpret_cast<const float4 *>(
+                            gbase + (int64_t)(L.bag[pp - t.t0] - cB) * a.sumD));
                 }
             }
 #pragma unroll
@@ -428,14 +492,18 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 #pragma unroll
                             for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                             hseg = u; hpass = false;
-                        } else {
-                            seg_out(a, col, c, u, acc, q, qa);
+                        } else if (qa) {
+                            row_apply(a, col, u, e, acc, pre, q);
                         }
 #pragma unroll
                         for (int v = 0; v < 4; v++) acc[v] = 0.f;
                         u++;
                         uend = segat(a, L, t, u + 1);
                         before = false;
+                        if (qa) {
+                            e = row_elem(a, L, t, col, u, q);
+                            row_load(a, col, e, pre);
+                        }
                     }
                     acc[0] += wt[u2] * x[u2].x;
                     acc[1] += wt[u2] * x[u2].y;
@@ -449,8 +517,8 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 #pragma unroll
                 for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                 hseg = u; hpass = false;
-            } else {
-                seg_out(a, col, c, u, acc, q, qa);
+            } else if (qa) {
+                row_apply(a, col, u, e, acc, pre, q);
             }
         } else if (before) {
 #pragma unroll
@@ -461,9 +529,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
         }
     }
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        L.part[lane][v] = hacc[v];
-    }
+    for (int v = 0; v < 4; v++) L.part[lane][v] = hacc[v];
     if (q == 0) {
         L.hseg[g] = hseg; L.hpass[g] = hpass;
     }
@@ -477,8 +543,8 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             if (!L.hpass[g2]) { ended = true; break; }
         }
-        if (ended) seg_out(a, col, c, tseg, sum, q, qa);
-        else bwd_piece(a, L, t, col, c, 1, tseg, sum, g * P, q, qa);
+        if (ended) seg_out(a, L, t, col, tseg, sum, q, qa);
+        else bwd_piece(a, L, t, col, 1, tseg, sum, g * P, q, qa);
     }
     if (g == 0 && hseg >= 0) {
         float sum[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
@@ -489,7 +555,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             pass = L.hpass[g2];
         }
-        bwd_piece(a, L, t, col, c, 0, hseg, sum, 0, q, qa);
+        bwd_piece(a, L, t, col, 0, hseg, sum, 0, q, qa);
     }
     wave_sync();
 }
@@ -502,35 +568,64 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
     BTile t;
     t.k = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
     if (t.k >= a.ntiles) return;
-    const int nv = (int)a.misc[0], U = (int)a.misc[1];
+    const int nv = (int)*gp(a.misc), U = (int)*gp(a.misc + 1);
+    t.U = U;
     t.t0 = (int)min<int64_t>(t.k * a.T, nv);
     t.t1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
     if (t.t0 >= t.t1) return;
+
+    // the tile's sorted bags and their pooling counts, loaded while searching
+    constexpr int kPL = kTileMax / kWave;
+    int bagr[kPL], nr[kPL];
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        bagr[i] = p < t.t1 ? (int)*gp(a.sval + p) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        nr[i] = (a.any_mean && p < t.t1) ? *gp(a.bag_n + bagr[i]) : 1;
+    }
     t.uf = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)t.t0) - 1;
-    t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
     t.wb = t.uf;
-    t.wn = min(t.ul + 2 - t.uf, kOffCap);
-    for (int i = lane; i < t.wn; i += kWave) L.seg[i] = *gp(a.seg + t.wb + i);
+    t.wn = min(U + 1 - t.uf, kOffCap);
+    for (int i = lane; i < t.wn; i += kWave) {
+        L.seg[i] = *gp(a.seg + t.wb + i);
+        L.ukey[i] = (t.wb + i < U) ? *gp(a.ukeys + t.wb + i) : 0xFFFFFFFFu;
+    }
     wave_sync();
-    int u = t.uf;
-    while (u <= t.ul) {
-        const int uu = uniform(u);
-        const uint32_t key = a.ukeys[uu];
-        const int c = uniform((int)wave_upper_bound(a.row_base, (int64_t)a.C + 1, key) - 1);
-        const DevCol col = a.cols[c];
-        // uniques of column c inside [uu, ul]
-        const uint32_t lim = a.row_base[c + 1];
-        const int uend = uu + (int)wave_lower_bound(a.ukeys + uu, (int64_t)(t.ul + 1 - uu), lim);
-        const int s0 = max(t.t0, segat(a, L, t, uu)), s1 = min(t.t1, segat(a, L, t, uend));
-        // stage each contributor's sample and pooling weight
-        for (int p = s0 + lane; p < s1; p += kWave) {
-            const int b = (int)*gp(a.sval + p);
-            L.smp[p - t.t0] = b - c * a.B;
-            L.wt[p - t.t0] = col.pool == EMB_POOL_MEAN ? 1.0f / (float)*gp(a.bag_n + b) : 1.0f;
+    if (L.seg[t.wn - 1] > (uint32_t)(t.t1 - 1))
+        t.ul = t.uf + (int)wave_upper_bound(L.seg, (int64_t)t.wn, (uint32_t)(t.t1 - 1)) - 1;
+    else
+        t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        if (p < t.t1) {
+            L.bag[p - t.t0] = bagr[i];
+            L.wt[p - t.t0] = 1.0f / (float)nr[i];   // mean weight; sum columns use 1
         }
-        wave_sync();
-        bwd_segment(a, L, t, col, c, s0, s1);
-        u = uend;
+    }
+    wave_sync();
+    // column runs: contributors are sorted by (column, row), and bag / B is the column
+    int p = t.t0;
+    while (p < t.t1) {
+        const int c = uniform(L.bag[p - t.t0] / a.B);
+        const int lim = (c + 1) * a.B;
+        int lo = p, hi = t.t1;          // first contributor of a later column
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (L.bag[mid - t.t0] < lim) lo = mid + 1; else hi = mid;
+        }
+        const int s1 = uniform(lo);
+        const DevCol col = a.cols[c];
+        if (col.pool != EMB_POOL_MEAN) {
+            for (int q = p + lane; q < s1; q += kWave) L.wt[q - t.t0] = 1.0f;
+            wave_sync();
+        }
+        bwd_segment(a, L, t, col, c, p, s1);
+        p = s1;
     }
 }
 
@@ -604,6 +699,7 @@ extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *
         a.part = reinterpret_cast<float *>(ws + W.bpart);
         a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
         a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
+        a.any_mean = plan->any_mean ? 1 : 0;
         const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
         hipLaunchKernelGGL(seg_apply, dim3((unsigned)blocks), dim3(kBlock), 0, st, a);
     } else if (n_uniq) {

@@ -67,7 +67,7 @@ struct emb_plan {
     int32_t key_bits = 0;          // bits needed for keys up to total_rows + 1
     int64_t max_tiles = 0;         // tiles of the largest batch
     int64_t sort_blocks = 0;       // radix blocks of the largest batch
-    bool has_hash = false, has_bucket = false, has_keyed = false;
+    bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata
     uint32_t *drow_base = nullptr; // device [n_cols + 1] row bases (after dcols)

@@ -175,6 +175,7 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         P.has_hash |= d.kind == EMB_COL_HASH || d.kind == EMB_COL_IDENTITY;
         P.has_bucket |= d.kind == EMB_COL_BUCKET;
         P.has_keyed |= d.kind == EMB_COL_KEYED;
+        P.any_mean |= d.pool == EMB_POOL_MEAN;
     }
     P.total_rows = (uint32_t)row_base;
     P.hrow_base = new (std::nothrow) uint32_t[n_cols + 1];
