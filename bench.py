@@ -17,8 +17,11 @@ timed on one batch on the host.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +31,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "embedding_columns_amd", "csrc")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP/C++ sources: a counter summary applies only to the
+    kernels it was measured on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                    + glob.glob(os.path.join(CSRC, "*.cpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", txt)
+    if not m or not t or m.group(1) != source_hash():
+        return None
+    return int(t.group(1))
 WORKLOADS = {"tiny": 1, "front-end": 2, "inference": 3, "long-seq": 4, "keyed": 5}
 
 
@@ -146,9 +175,12 @@ def run(args):
         if ev is not None:
             ev[1].record()
         if training:
-            E.emb_backward(plan.plan, G, plan.workspace, None, None, None, tstats)
+            E.emb_backward_dedup(plan.plan, plan.workspace, None, None, tstats)
+            if ev is not None:
+                ev[2].record()
+            E.emb_backward_apply(plan.plan, G, plan.workspace)
         if ev is not None:
-            ev[2].record()
+            ev[3].record()
 
     # per-batch algorithmic bytes (dense workloads: valid counts from the generator's
     # masks, distinct rows from one untimed backward per batch)
@@ -170,7 +202,7 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
     stats.zero_()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -179,7 +211,9 @@ def run(args):
     wall = time.perf_counter() - t0
     st = stats.cpu().numpy()
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    bwd_ms = np.array([e[1].elapsed_time(e[3]) for e in evs])
+    dedup_ms = np.array([e[1].elapsed_time(e[2]) for e in evs]) if training else np.zeros(1)
+    apply_ms = np.array([e[2].elapsed_time(e[3]) for e in evs]) if training else np.zeros(1)
 
     idx = [(args.warmup + i) % len(dbat) for i in range(args.steps)]
     if keyed:
@@ -199,7 +233,17 @@ def run(args):
     value = lookups / wall
     ms_step = 1000.0 * wall / args.steps
     fwd_avg = float(np.mean(fwd_ms))
-    achieved = fb / (fwd_avg * 1e-3) / 1e9
+    apply_avg = float(np.mean(apply_ms))
+    kernels = {"fwd_kernel": {"launch_us": round(1000 * fwd_avg, 2), "algorithmic_bytes": int(fb),
+                              "gbs": round(fb / (fwd_avg * 1e-3) / 1e9, 1)}}
+    if training:
+        kernels["seg_apply"] = {"launch_us": round(1000 * apply_avg, 2), "algorithmic_bytes": int(ub),
+                                "gbs": round(ub / (apply_avg * 1e-3) / 1e9, 1)}
+        kernels["dedup_sort_unique"] = {"us": round(1000 * float(np.mean(dedup_ms)), 2)}
+    dom = "fwd_kernel" if (not training or fwd_avg >= apply_avg) else "seg_apply"
+    dk = kernels[dom]
+    achieved = dk["gbs"]
+    traffic = measured_traffic(dom, w.name)
     out = {
         "metric": "pooled embedding lookups/sec (fwd+bwd) at 1 GPU; achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -220,10 +264,11 @@ def run(args):
                    "tile": plan.opts.tile or 256, "fwd_launches_per_step": 1},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "fwd_ms": round(fwd_avg, 4),
-        "bwd_ms": round(float(np.mean(bwd_ms)), 4) if training else 0.0,
-        "roofline": {"kernel": "fwd_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": int(fb)},
+        "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": dk["algorithmic_bytes"], "launch_us": dk["launch_us"]},
+        "kernels": kernels,
     }
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
     "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_backward",
+    "emb_backward_dedup", "emb_backward_apply",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
     "emb_table_rows", "emb_table_bulk_insert", "emb_table_lookup_or_insert", "emb_table_find",
     "emb_table_export", "emb_last_error", "EmbeddingColumns", "KeyedTable",
@@ -70,6 +71,8 @@ _SIGS = {
     "emb_plan_destroy": [_VP],
     "emb_forward": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
+    "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
     "emb_plan_workspace_view": [_VP, _VP, C.POINTER(WorkspaceView)],
     "emb_table_query": [_I64, _I64, _I32, C.POINTER(C.c_size_t)],
     "emb_table_create": [_I64, _I64, _I32, _I32, _F, _VP, _VP, C.POINTER(_VP)],
@@ -159,6 +162,16 @@ def emb_backward(plan, grad_out, workspace, uniq_keys=None, uniq_grads=None, n_u
                  stats=None, stream=None):
     _check(lib().emb_backward(plan, _ptr(grad_out), _ptr(workspace), _ptr(uniq_keys),
                               _ptr(uniq_grads), _ptr(n_uniq), _ptr(stats), _stream(stream)))
+
+
+def emb_backward_dedup(plan, workspace, uniq_keys=None, n_uniq=None, stats=None, stream=None):
+    _check(lib().emb_backward_dedup(plan, _ptr(workspace), _ptr(uniq_keys), _ptr(n_uniq),
+                                    _ptr(stats), _stream(stream)))
+
+
+def emb_backward_apply(plan, grad_out, workspace, uniq_grads=None, stream=None):
+    _check(lib().emb_backward_apply(plan, _ptr(grad_out), _ptr(workspace), _ptr(uniq_grads),
+                                    _stream(stream)))
 
 
 def emb_plan_workspace_view(plan, workspace):

@@ -633,19 +633,24 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
 
 using namespace emb;
 
-extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *workspace,
-                                   uint32_t *uniq_keys, float *uniq_grads, int64_t *n_uniq,
-                                   int64_t *stats, void *stream)
+static emb_status bwd_check(emb_plan *plan, void *workspace)
 {
-    if (!plan || !grad_out || !workspace) return fail(EMB_ERR_INVALID_ARG, "plan, grad_out and workspace are required");
-    if (!aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned");
+    if (!plan || !workspace) return fail(EMB_ERR_INVALID_ARG, "plan and workspace are required");
     if (!aligned(workspace, 256)) return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    if (uniq_grads && (plan->opt != EMB_OPT_EMIT || !aligned(uniq_grads, 16)))
-        return fail(EMB_ERR_INVALID_ARG, "uniq_grads needs the EMIT optimizer and 16-byte alignment");
+    if (plan->last_n < 0) return fail(EMB_ERR_INVALID_ARG, "no training forward ran on this plan");
+    return EMB_OK;
+}
+
+static int sort_passes(const emb_plan *plan) { return (plan->key_bits + kRadixBits - 1) / kRadixBits; }
+
+extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32_t *uniq_keys,
+                                         int64_t *n_uniq, int64_t *stats, void *stream)
+{
+    emb_status s = bwd_check(plan, workspace);
+    if (s != EMB_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
     const int64_t n = plan->last_n;
-    if (n < 0) return fail(EMB_ERR_INVALID_ARG, "no training forward ran on this plan");
     const WsLayout &W = plan->ws;
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + W.keys);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + W.bags);
@@ -654,58 +659,87 @@ extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + W.hist);
     uint32_t *dtot = reinterpret_cast<uint32_t *>(ws + W.dtot);
     uint32_t *misc = reinterpret_cast<uint32_t *>(ws + W.misc);
-    const int64_t nblk = std::max<int64_t>(1, (n + kSortTile - 1) / kSortTile);
-    const int passes = (plan->key_bits + kRadixBits - 1) / kRadixBits;
-    hipError_t e = hipSuccess;
-    if (n > 0) {
-        for (int p = 0; p < passes; p++) {
-            const int shift = p * kRadixBits;
-            hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk);
-            hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
-            hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
-                               shift, hist, dtot, nblk);
-            std::swap(k0, k1);
-            std::swap(v0, v1);
-        }
-    }
     uint32_t *ucnt = reinterpret_cast<uint32_t *>(ws + W.ucnt);
     uint32_t *uscan = reinterpret_cast<uint32_t *>(ws + W.uscan);
     uint32_t *seg = reinterpret_cast<uint32_t *>(ws + W.seg);
     uint32_t *ukeys = reinterpret_cast<uint32_t *>(ws + W.ukeys);
-    if (n > 0) {
-        hipLaunchKernelGGL(uq_count, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
-        hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, nblk, uscan, misc, n_uniq, stats);
-        hipLaunchKernelGGL(uq_write, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
-                           uscan, misc, seg, ukeys, uniq_keys);
-        BwdArgs a{};
-        a.cols = plan->dcols;
-        a.row_base = plan->drow_base;
-        a.C = plan->n_cols;
-        a.B = plan->batch;
-        a.sumD = plan->sum_dim;
-        a.maxD = plan->max_dim;
-        a.T = plan->tile;
-        a.opt = plan->opt;
-        a.lr = plan->lr;
-        a.eps = plan->eps;
-        a.ntiles = std::max<int64_t>(1, (n + plan->tile - 1) / plan->tile);
-        a.G = grad_out;
-        a.sval = v0;
-        a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
-        a.seg = seg;
-        a.ukeys = ukeys;
-        a.misc = misc;
-        a.ugrads = uniq_grads;
-        a.part = reinterpret_cast<float *>(ws + W.bpart);
-        a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
-        a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
-        a.any_mean = plan->any_mean ? 1 : 0;
-        const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-        hipLaunchKernelGGL(seg_apply, dim3((unsigned)blocks), dim3(kBlock), 0, st, a);
-    } else if (n_uniq) {
-        e = hipMemsetAsync(n_uniq, 0, sizeof(int64_t), st);
+    const int64_t nblk = std::max<int64_t>(1, (n + kSortTile - 1) / kSortTile);
+    if (n == 0) {
+        hipError_t e = n_uniq ? hipMemsetAsync(n_uniq, 0, sizeof(int64_t), st) : hipSuccess;
+        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward: ") + hipGetErrorString(e));
+        return EMB_OK;
     }
-    if (e == hipSuccess) e = hipGetLastError();
-    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+    for (int p = 0; p < sort_passes(plan); p++) {
+        const int shift = p * kRadixBits;
+        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk);
+        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
+        hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
+                           shift, hist, dtot, nblk);
+        std::swap(k0, k1);
+        std::swap(v0, v1);
+    }
+    hipLaunchKernelGGL(uq_count, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
+    hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, nblk, uscan, misc, n_uniq, stats);
+    hipLaunchKernelGGL(uq_write, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
+                       uscan, misc, seg, ukeys, uniq_keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
     return EMB_OK;
+}
+
+extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, void *workspace,
+                                         float *uniq_grads, void *stream)
+{
+    emb_status s = bwd_check(plan, workspace);
+    if (s != EMB_OK) return s;
+    if (!grad_out || !aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned device memory");
+    if (uniq_grads && (plan->opt != EMB_OPT_EMIT || !aligned(uniq_grads, 16)))
+        return fail(EMB_ERR_INVALID_ARG, "uniq_grads needs the EMIT optimizer and 16-byte alignment");
+    const int64_t n = plan->last_n;
+    if (n == 0) return EMB_OK;
+    char *ws = static_cast<char *>(workspace);
+    const WsLayout &W = plan->ws;
+    BwdArgs a{};
+    a.cols = plan->dcols;
+    a.row_base = plan->drow_base;
+    a.C = plan->n_cols;
+    a.B = plan->batch;
+    a.sumD = plan->sum_dim;
+    a.maxD = plan->max_dim;
+    a.T = plan->tile;
+    a.opt = plan->opt;
+    a.lr = plan->lr;
+    a.eps = plan->eps;
+    a.ntiles = std::max<int64_t>(1, (n + plan->tile - 1) / plan->tile);
+    a.G = grad_out;
+    // the sorted bags sit in the buffer the last radix pass wrote
+    a.sval = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.vals2 : W.bags));
+    a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
+    a.seg = reinterpret_cast<const uint32_t *>(ws + W.seg);
+    a.ukeys = reinterpret_cast<const uint32_t *>(ws + W.ukeys);
+    a.misc = reinterpret_cast<const uint32_t *>(ws + W.misc);
+    a.ugrads = uniq_grads;
+    a.part = reinterpret_cast<float *>(ws + W.bpart);
+    a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
+    a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
+    a.any_mean = plan->any_mean ? 1 : 0;
+    const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(seg_apply, dim3((unsigned)blocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("seg_apply launch: ") + hipGetErrorString(e));
+    return EMB_OK;
+}
+
+extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *workspace,
+                                   uint32_t *uniq_keys, float *uniq_grads, int64_t *n_uniq,
+                                   int64_t *stats, void *stream)
+{
+    emb_status s = bwd_check(plan, workspace);
+    if (s != EMB_OK) return s;
+    if (!grad_out || !aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned device memory");
+    if (uniq_grads && (!plan || plan->opt != EMB_OPT_EMIT || !aligned(uniq_grads, 16)))
+        return fail(EMB_ERR_INVALID_ARG, "uniq_grads needs the EMIT optimizer and 16-byte alignment");
+    s = emb_backward_dedup(plan, workspace, uniq_keys, n_uniq, stats, stream);
+    if (s != EMB_OK) return s;
+    return emb_backward_apply(plan, grad_out, workspace, uniq_grads, stream);
 }

@@ -163,6 +163,20 @@ emb_status emb_backward(emb_plan *plan, const float *grad_out, void *workspace,
                         uint32_t *uniq_keys, float *uniq_grads, int64_t *n_uniq, int64_t *stats,
                         void *stream);
 
+/* emb_backward in two parts, for callers that schedule them apart (the
+ * deduplication does not read grad_out, so it can run while the upstream
+ * gradient is still being computed):
+ *   emb_backward_dedup  radix sort of the touched row keys and the distinct
+ *                       keys (RecIS Fig. 3 "Reduce-ID": each row once, with the
+ *                       map back to its contributors); uniq_keys / n_uniq as above;
+ *   emb_backward_apply  segment-sum of grad_out per distinct row and the row
+ *                       update (or uniq_grads for EMIT).
+ * apply must follow dedup on the same workspace. */
+emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32_t *uniq_keys,
+                              int64_t *n_uniq, int64_t *stats, void *stream);
+emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, void *workspace,
+                              float *uniq_grads, void *stream);
+
 /* Device views into a workspace after a training forward (parity checks):
  * keys uint32 [n_ids] (row_base_c + row; sum(rows) for a dropped position,
  * sum(rows)+1 for a DEFAULT one), bags int32 [n_ids] (bag index c*B+s),

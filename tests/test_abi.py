@@ -115,3 +115,5 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_forward(None, None, None, None, None, 0, None, None, 0, None, None) == 1
     assert L.lib().emb_backward(None, None, None, None, None, None, None, None) == 1
     assert "plan" in L.emb_last_error()
+    assert L.lib().emb_backward_dedup(None, None, None, None, None, None) == 1
+    assert L.lib().emb_backward_apply(None, None, None, None, None) == 1
