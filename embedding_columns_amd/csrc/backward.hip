@@ -306,6 +306,9 @@ struct BwdLds {
     uint32_t ukey[kOffCap];     // unique keys of the same segments
     float part[kWave][4];
     int32_t hseg[kWave], hpass[kWave];
+    int32_t njob;                  // segments whose last piece arrived here: summed by the
+    int32_t job_u[4], job_c[4];    //   whole wavefront once the walk is done
+    int64_t job_k0[4], job_k1[4];
 };
 
 struct BTile {
@@ -408,9 +411,11 @@ __device__ __forceinline__ void seg_out(const BwdArgs &a, const BwdLds &L, const
     row_apply(a, col, u, e, g, r, q);
 }
 
-__device__ __forceinline__ void bwd_piece(const BwdArgs &a, const BwdLds &L, const BTile &t,
-                                          const DevCol &col, int side, int u,
-                                          const float (&sum)[4], int leader, int q, bool qa)
+// a piece of a segment that crosses a tile boundary: publish it; the tile whose
+// piece arrives last queues the segment for the wavefront-wide combine
+__device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLds &L, const BTile &t, int c,
+                                          int side, int u, const float (&sum)[4], int leader,
+                                          int q, bool qa)
 {
     const int64_t T = a.T;
     const int ss = segat(a, L, t, u), se = segat(a, L, t, u + 1);
@@ -420,25 +425,54 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, const BwdLds &L, con
 #pragma unroll
         for (int v = 0; v < 4; v++) st_agent(a.part + slot * a.maxD + q * 4 + v, sum[v]);
     }
-    wait_vm();
+    wait_vm();                                 // the piece is visible before the ticket
     uint32_t old = 0;
     if (q == 0) old = ticket_add(&a.tick[k0]);
     old = __shfl(old, leader, kWave);
-    if (old == (uint32_t)(k1 - k0)) {
-        float tot[4] = {0.f, 0.f, 0.f, 0.f};
-        if (qa) {
-            const float *p0 = a.part + (k0 * 2 + 1) * a.maxD + q * 4;
-#pragma unroll
-            for (int v = 0; v < 4; v++) tot[v] = ld_agent(p0 + v);
-            for (int64_t kk = k0 + 1; kk <= k1; kk++) {
-                const float *pk = a.part + (kk * 2) * a.maxD + q * 4;
-#pragma unroll
-                for (int v = 0; v < 4; v++) tot[v] += ld_agent(pk + v);
-            }
-        }
-        seg_out(a, L, t, col, u, tot, q, qa);
-        if (q == 0) st_agent(&a.tick[k0], 0u);
+    if (old == (uint32_t)(k1 - k0) && q == 0) {
+        const int j = atomicAdd(&L.njob, 1);   // at most two per tile (its first and last segment)
+        L.job_u[j] = u;
+        L.job_c[j] = c;
+        L.job_k0[j] = k0;
+        L.job_k1[j] = k1;
     }
+}
+
+// Sum the pieces of a queued segment in a fixed order with all 64 lanes: lane
+// slice j = lane / P takes pieces j, j + 64/P, ... (several loads in flight per
+// lane), then the slices are added by a butterfly over the slice bits.
+__device__ __forceinline__ void bwd_job(const BwdArgs &a, const BwdLds &L, const BTile &t, int j)
+{
+    const int u = L.job_u[j], c = uniform(L.job_c[j]);
+    const int64_t k0 = L.job_k0[j], k1 = L.job_k1[j];
+    const DevCol col = a.cols[c];
+    const int P = col.glanes, lp = __ffs(P) - 1;
+    const int lane = lane_id(), sl = lane >> lp, q = lane & (P - 1), nsl = kWave >> lp;
+    const bool qa = q < col.dim / 4;
+    constexpr int UJ = 4;
+    float tot[4] = {0.f, 0.f, 0.f, 0.f};
+    // piece i = 0 is tile k0's outgoing slot, piece i >= 1 is tile k0+i's incoming slot
+    const int64_t npc = k1 - k0 + 1;
+    for (int64_t i0 = 0; i0 < npc; i0 += (int64_t)nsl * UJ) {
+        float x[UJ][4];
+#pragma unroll
+        for (int r = 0; r < UJ; r++) {
+            const int64_t i = i0 + (int64_t)r * nsl + sl;
+            const int64_t slot = i == 0 ? k0 * 2 + 1 : (k0 + i) * 2;
+            const bool ok = qa && i < npc;
+#pragma unroll
+            for (int v = 0; v < 4; v++) x[r][v] = ok ? ld_agent(a.part + slot * a.maxD + q * 4 + v) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < UJ; r++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) tot[v] += x[r][v];
+    }
+    for (int o = P; o < kWave; o <<= 1)
+#pragma unroll
+        for (int v = 0; v < 4; v++) tot[v] += __shfl_xor(tot[v], o, kWave);
+    if (sl == 0) seg_out(a, L, t, col, u, tot, q, qa);
+    if (lane == 0) st_agent(&a.tick[k0], 0u);  // ready for the next call
 }
 
 // one column run [s0, s1) of sorted contributors; P lanes per gradient row
@@ -544,7 +578,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             if (!L.hpass[g2]) { ended = true; break; }
         }
         if (ended) seg_out(a, L, t, col, tseg, sum, q, qa);
-        else bwd_piece(a, L, t, col, 1, tseg, sum, g * P, q, qa);
+        else bwd_piece(a, L, t, c, 1, tseg, sum, g * P, q, qa);
     }
     if (g == 0 && hseg >= 0) {
         float sum[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
@@ -555,7 +589,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             pass = L.hpass[g2];
         }
-        bwd_piece(a, L, t, col, 0, hseg, sum, 0, q, qa);
+        bwd_piece(a, L, t, c, 0, hseg, sum, 0, q, qa);
     }
     wave_sync();
 }
@@ -607,6 +641,7 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
             L.wt[p - t.t0] = 1.0f / (float)nr[i];   // mean weight; sum columns use 1
         }
     }
+    if (lane == 0) L.njob = 0;
     wave_sync();
     // column runs: contributors are sorted by (column, row), and bag / B is the column
     int p = t.t0;
@@ -627,6 +662,9 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
         bwd_segment(a, L, t, col, c, p, s1);
         p = s1;
     }
+    wave_sync();
+    const int nj = uniform(L.njob);
+    for (int j = 0; j < nj; j++) bwd_job(a, L, t, j);
 }
 
 }  // namespace emb

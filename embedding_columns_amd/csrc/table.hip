@@ -128,32 +128,69 @@ __device__ __forceinline__ void stat_max(int64_t *stats, int idx, int64_t v)
     if (stats && lane_id() == 0 && v) atomicMax((unsigned long long *)&stats[idx], (unsigned long long)v);
 }
 
+// Counting under a skewed key stream: one block takes 1024 occurrences, adds them
+// up per slot in an LDS hash (each hot key is counted once per block instead
+// of once per occurrence), then adds each distinct slot's count to the table.
+constexpr int kCountPerThread = 4;
+constexpr int kCountTile = kBlock * kCountPerThread;
+constexpr int kLdsSlots = 2 * kCountTile;      // load factor <= 1/2: every insert finds room
+
 __global__ __launch_bounds__(kBlock) void ht_count(TabArgs a, const int64_t *__restrict__ keys,
                                                   int64_t n, int32_t *__restrict__ pos,
                                                   int64_t *stats)
 {
-    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    int64_t ins = 0, full = 0, probes = 0;
-    if (p < n) {
-        const int64_t key = keys[p];
-        if (key < 1) {
-            pos[p] = EMB_ROW_DROPPED;
-        } else {
-            bool inserted;
-            const int64_t s = probe_insert(a, (unsigned long long)key, inserted, probes);
-            if (s < 0) {
-                pos[p] = kPosRefused;
-                full = 1;
-            } else {
-                atomicAdd(&a.count[s], 1);
-                pos[p] = (int32_t)s;
-                ins = inserted;
-            }
-        }
+    __shared__ int32_t lslot[kLdsSlots];
+    __shared__ int32_t lcnt[kLdsSlots];
+    __shared__ unsigned long long lstat[3];
+    for (int i = threadIdx.x; i < kLdsSlots; i += kBlock) {
+        lslot[i] = -1;
+        lcnt[i] = 0;
     }
-    stat_add(stats, EMB_STAT_TABLE_INSERTED, ins);
-    stat_add(stats, EMB_STAT_TABLE_FULL, full);
-    stat_max(stats, EMB_STAT_MAX_PROBE, probes);
+    if (threadIdx.x < 3) lstat[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kCountTile;
+    int64_t ins = 0, full = 0, probes = 0;
+    for (int j = 0; j < kCountPerThread; j++) {
+        const int64_t p = base + (int64_t)j * kBlock + threadIdx.x;
+        if (p >= n) break;
+        const int64_t key = *gp(keys + p);
+        if (key < 1) {
+            *gp(pos + p) = EMB_ROW_DROPPED;
+            continue;
+        }
+        bool inserted;
+        int64_t pr = 0;
+        const int64_t s = probe_insert(a, (unsigned long long)key, inserted, pr);
+        probes = max(probes, pr);
+        if (s < 0) {
+            *gp(pos + p) = kPosRefused;
+            full++;
+            continue;
+        }
+        *gp(pos + p) = (int32_t)s;
+        ins += inserted;
+        // count this occurrence in the block's LDS hash
+        uint32_t h = ((uint32_t)s * 2654435761u) >> (32 - 11);   // 2^11 = kLdsSlots
+        while (true) {
+            const int32_t cur = atomicCAS(&lslot[h], -1, (int32_t)s);
+            if (cur == -1 || cur == (int32_t)s) break;
+            h = (h + 1) & (kLdsSlots - 1);
+        }
+        atomicAdd(&lcnt[h], 1);
+    }
+    if (stats) {
+        atomicAdd(&lstat[0], (unsigned long long)ins);
+        atomicAdd(&lstat[1], (unsigned long long)full);
+        atomicMax(&lstat[2], (unsigned long long)probes);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kLdsSlots; i += kBlock)
+        if (lslot[i] >= 0) atomicAdd(&a.count[lslot[i]], lcnt[i]);
+    if (stats && threadIdx.x == 0) {
+        if (lstat[0]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_INSERTED], lstat[0]);
+        if (lstat[1]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_FULL], lstat[1]);
+        if (lstat[2]) atomicMax((unsigned long long *)&stats[EMB_STAT_MAX_PROBE], lstat[2]);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void ht_admit(TabArgs a, const int64_t *__restrict__ keys,
@@ -384,7 +421,8 @@ emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int
     if (n == 0) return EMB_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const TabArgs a = tab_args(*table);
-    hipLaunchKernelGGL(ht_count, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
+    const unsigned cgrid = (unsigned)std::max<int64_t>(1, (n + kCountTile - 1) / kCountTile);
+    hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_admit, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_resolve, dim3(grid_of(n)), dim3(kBlock), 0, st, a, n, rows_out);
     return launched("lookup_or_insert");
