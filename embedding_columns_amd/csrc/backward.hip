@@ -27,22 +27,17 @@ namespace emb {
 
 // ---------------------------------------------------------------- radix sort
 
-__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
-                                                 int shift, uint32_t *__restrict__ hist,
-                                                 int64_t nblk)
+// lanes of this wavefront whose digit equals mine (active lanes only), by one
+// ballot per digit bit
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool in)
 {
-    __shared__ uint32_t h[kRadix];
-    const int t = threadIdx.x;
-    h[t] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-#pragma unroll 4
-    for (int i = 0; i < kSortItems; i++) {
-        const int64_t idx = base + (int64_t)i * kBlock + t;
-        if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & (kRadix - 1)], 1u);
+    uint64_t peers = __ballot(in);
+#pragma unroll
+    for (int b = 0; b < kRadixBits; b++) {
+        const uint64_t m = __ballot((d >> b) & 1u);
+        peers &= ((d >> b) & 1u) ? m : ~m;
     }
-    __syncthreads();
-    hist[(int64_t)t * nblk + blockIdx.x] = h[t];
+    return peers;
 }
 
 // exclusive scan of 256 values held one per thread; returns the total
@@ -67,6 +62,55 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     excl = wpre + x - v;
     __syncthreads();
     return tot;
+}
+
+// exclusive scan of kRadix values, kDigitsPerThread consecutive ones per thread
+constexpr int kDigitsPerThread = kRadix / kBlock;
+static_assert(kRadix % kBlock == 0, "digits per thread");
+
+__device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDigitsPerThread],
+                                                         uint32_t (&ex)[kDigitsPerThread],
+                                                         uint32_t *tmp)
+{
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kDigitsPerThread; i++) sum += v[i];
+    uint32_t base;
+    const uint32_t tot = block_exclusive_scan(sum, tmp, base);
+#pragma unroll
+    for (int i = 0; i < kDigitsPerThread; i++) {
+        ex[i] = base;
+        base += v[i];
+    }
+    return tot;
+}
+
+// per-block digit histogram; equal digits within a wavefront are added once
+__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
+                                                 int shift, uint32_t *__restrict__ hist,
+                                                 int64_t nblk)
+{
+    __shared__ uint32_t h[kRadix];
+    const int t = threadIdx.x, lane = lane_id();
+    for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t k[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; i++) {
+        const int64_t idx = base + (int64_t)i * kBlock + t;
+        k[i] = idx < n ? *gp(keys + idx) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kSortItems; i++) {
+        const bool in = base + (int64_t)i * kBlock + t < n;
+        const uint32_t d = (k[i] >> shift) & (kRadix - 1);
+        const uint64_t peers = match_digit(d, in);
+        if (in && (peers & lt_mask) == 0) atomicAdd(&h[d], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
 }
 
 // one block per digit: exclusive scan of hist[d][0..nblk) in place, total -> dtot[d]
@@ -109,10 +153,19 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     const int cnt = (int)min<int64_t>(kSortTile, n - base);
 
     // digit offsets: global prefix over digits + this block's offset within each digit
-    uint32_t dex;
-    block_exclusive_scan(dtot[t], S.tmp, dex);
-    S.gbase[t] = dex + hist[(int64_t)t * nblk + blockIdx.x];
-    for (int i = 0; i < kWavesPerBlock; i++) S.run[i][t] = 0;
+    {
+        uint32_t v[kDigitsPerThread], ex[kDigitsPerThread];
+#pragma unroll
+        for (int i = 0; i < kDigitsPerThread; i++) v[i] = dtot[t * kDigitsPerThread + i];
+        digit_exclusive_scan(v, ex, S.tmp);
+#pragma unroll
+        for (int i = 0; i < kDigitsPerThread; i++) {
+            const int d = t * kDigitsPerThread + i;
+            S.gbase[d] = ex[i] + hist[(int64_t)d * nblk + blockIdx.x];
+        }
+        for (int d = t; d < kRadix; d += kBlock)
+            for (int i = 0; i < kWavesPerBlock; i++) S.run[i][d] = 0;
+    }
     __syncthreads();
 
     // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
@@ -123,15 +176,10 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     for (int j = 0; j < kSortItems; j++) {
         const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
         const bool in = li < cnt;
-        key[j] = in ? kin[base + li] : 0u;
-        val[j] = in ? vin[base + li] : 0u;
+        key[j] = in ? *gp(kin + base + li) : 0u;
+        val[j] = in ? *gp(vin + base + li) : 0u;
         const uint32_t d = (key[j] >> shift) & (kRadix - 1);
-        uint64_t peers = __ballot(in);
-#pragma unroll
-        for (int b = 0; b < kRadixBits; b++) {
-            const uint64_t m = __ballot((d >> b) & 1u);
-            peers &= ((d >> b) & 1u) ? m : ~m;
-        }
+        const uint64_t peers = match_digit(d, in);
         const uint32_t before = S.run[w][d];
         rank[j] = before + (uint32_t)__popcll(peers & lt_mask);
         const bool leader = in && (peers >> lane) == 1ull;   // highest lane of its digit group
@@ -142,17 +190,25 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     __syncthreads();
     // block-local digit histogram -> local prefix; per-wave offsets inside each digit
     {
-        uint32_t tot = 0, woff[kWavesPerBlock];
+        uint32_t tot[kDigitsPerThread], lex[kDigitsPerThread], woff[kDigitsPerThread][kWavesPerBlock];
 #pragma unroll
-        for (int i = 0; i < kWavesPerBlock; i++) {
-            woff[i] = tot;
-            tot += S.run[i][t];
+        for (int i = 0; i < kDigitsPerThread; i++) {
+            const int d = t * kDigitsPerThread + i;
+            tot[i] = 0;
+#pragma unroll
+            for (int k = 0; k < kWavesPerBlock; k++) {
+                woff[i][k] = tot[i];
+                tot[i] += S.run[k][d];
+            }
         }
-        uint32_t lex;
-        block_exclusive_scan(tot, S.tmp, lex);
-        S.lpre[t] = lex;
+        digit_exclusive_scan(tot, lex, S.tmp);
 #pragma unroll
-        for (int i = 0; i < kWavesPerBlock; i++) S.run[i][t] = lex + woff[i];
+        for (int i = 0; i < kDigitsPerThread; i++) {
+            const int d = t * kDigitsPerThread + i;
+            S.lpre[d] = lex[i];
+#pragma unroll
+            for (int k = 0; k < kWavesPerBlock; k++) S.run[k][d] = lex[i] + woff[i][k];
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -171,23 +227,23 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
         const uint32_t k = S.skey[lp];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = S.gbase[d] + (uint32_t)lp - S.lpre[d];
-        kout[dst] = k;
-        vout[dst] = S.sval[lp];
+        *gp(kout + dst) = k;
+        *gp(vout + dst) = S.sval[lp];
     }
 }
 
 // -------------------------------------------------------------- unique rows
 
-// keys of one 4096-key block, read coalesced into LDS; key[-1] = the key before the block
+// keys of one 2048-key block, read coalesced into LDS; key[-1] = the key before the block
 struct UqLds {
-    uint32_t key[kSortTile + 1];
+    uint32_t key[kUqTile + 1];
     uint32_t tmp[kWavesPerBlock];
 };
 
 __device__ __forceinline__ int uq_stage(UqLds &S, const uint32_t *k, int64_t n)
 {
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-    const int cnt = (int)min<int64_t>(kSortTile, n - base);
+    const int64_t base = (int64_t)blockIdx.x * kUqTile;
+    const int cnt = (int)min<int64_t>(kUqTile, n - base);
     for (int i = threadIdx.x; i < cnt; i += kBlock) S.key[i + 1] = *gp(k + base + i);
     if (threadIdx.x == 0) S.key[0] = base > 0 ? *gp(k + base - 1) : 0xFFFFFFFFu;
     __syncthreads();
@@ -207,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void uq_count(const uint32_t *__restrict__ 
 {
     __shared__ UqLds S;
     const int cnt = uq_stage(S, k, n);
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int64_t base = (int64_t)blockIdx.x * kUqTile;
     uint32_t c = 0;
     for (int i = threadIdx.x; i < cnt; i += kBlock) {
         const bool first = base + i == 0;
@@ -254,18 +310,18 @@ __global__ __launch_bounds__(kBlock) void uq_write(const uint32_t *__restrict__ 
 {
     __shared__ UqLds S;
     const int cnt = uq_stage(S, k, n);
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-    // each thread owns kSortItems consecutive keys, so ranks follow key order
-    const int i0 = threadIdx.x * kSortItems;
+    const int64_t base = (int64_t)blockIdx.x * kUqTile;
+    // each thread owns kUqItems consecutive keys, so ranks follow key order
+    const int i0 = threadIdx.x * kUqItems;
     uint32_t c = 0;
-    for (int j = 0; j < kSortItems; j++) {
+    for (int j = 0; j < kUqItems; j++) {
         const int i = i0 + j;
         if (i < cnt) c += uq_head(S, i, total_rows, base + i == 0);
     }
     uint32_t ex;
     block_exclusive_scan(c, S.tmp, ex);
     uint32_t u = *gp(uscan + blockIdx.x) + ex;
-    for (int j = 0; j < kSortItems; j++) {
+    for (int j = 0; j < kUqItems; j++) {
         const int i = i0 + j;
         if (i < cnt && uq_head(S, i, total_rows, base + i == 0)) {
             const uint32_t x = S.key[i + 1];
@@ -702,6 +758,7 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     uint32_t *seg = reinterpret_cast<uint32_t *>(ws + W.seg);
     uint32_t *ukeys = reinterpret_cast<uint32_t *>(ws + W.ukeys);
     const int64_t nblk = std::max<int64_t>(1, (n + kSortTile - 1) / kSortTile);
+    const int64_t ublk = std::max<int64_t>(1, (n + kUqTile - 1) / kUqTile);
     if (n == 0) {
         hipError_t e = n_uniq ? hipMemsetAsync(n_uniq, 0, sizeof(int64_t), st) : hipSuccess;
         if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward: ") + hipGetErrorString(e));
@@ -716,9 +773,9 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
         std::swap(k0, k1);
         std::swap(v0, v1);
     }
-    hipLaunchKernelGGL(uq_count, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
-    hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, nblk, uscan, misc, n_uniq, stats);
-    hipLaunchKernelGGL(uq_write, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
+    hipLaunchKernelGGL(uq_count, dim3((unsigned)ublk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
+    hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, ublk, uscan, misc, n_uniq, stats);
+    hipLaunchKernelGGL(uq_write, dim3((unsigned)ublk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
                        uscan, misc, seg, ukeys, uniq_keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));

@@ -20,10 +20,12 @@ constexpr int kMaxDimF32 = 256;
 constexpr int kMaxDimBF16 = 512;
 
 // radix sort of (key, value) pairs
-constexpr int kRadixBits = 8;
+constexpr int kRadixBits = 9;                      // 3 passes for keys of <= 27 bits
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 16;                       // keys per thread
 constexpr int kSortTile = kBlock * kSortItems;       // 4096 keys per block
+constexpr int kUqItems = 8;                          // unique-row kernels: keys per thread
+constexpr int kUqTile = kBlock * kUqItems;           // 2048 keys per block
 
 // One column as the kernels read it (plan device memory), 96 bytes.
 struct DevCol {
@@ -67,6 +69,7 @@ struct emb_plan {
     int32_t key_bits = 0;          // bits needed for keys up to total_rows + 1
     int64_t max_tiles = 0;         // tiles of the largest batch
     int64_t sort_blocks = 0;       // radix blocks of the largest batch
+    int64_t uq_blocks = 0;         // unique-row blocks of the largest batch
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata

@@ -95,6 +95,7 @@ void plan_layout(emb_plan &P)
     const int64_t nb = (int64_t)P.n_cols * P.batch;
     P.max_tiles = std::max<int64_t>(1, (N + P.tile - 1) / P.tile);
     P.sort_blocks = std::max<int64_t>(1, (N + kSortTile - 1) / kSortTile);
+    P.uq_blocks = std::max<int64_t>(1, (N + kUqTile - 1) / kUqTile);
     WsLayout &L = P.ws;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -110,8 +111,8 @@ void plan_layout(emb_plan &P)
     L.dtot = take(4 * kRadix);
     L.seg = take(4 * (N + 1));
     L.ukeys = take(4 * N);
-    L.ucnt = take(4 * P.sort_blocks);
-    L.uscan = take(4 * (P.sort_blocks + 1));
+    L.ucnt = take(4 * P.uq_blocks);
+    L.uscan = take(4 * (P.uq_blocks + 1));
     L.misc = take(64);
     L.bpart = take(sizeof(float) * 2 * P.max_tiles * P.max_dim);
     L.bcnt = take(4 * 2 * P.max_tiles);
