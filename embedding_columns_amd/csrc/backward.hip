@@ -95,19 +95,25 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
     for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t k[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
         const int64_t idx = base + (int64_t)i * kBlock + t;
         k[i] = idx < n ? *gp(keys + idx) : 0u;
     }
+    // plain LDS atomics; a wavefront whose lanes all carry one digit (hot rows in
+    // the high passes) adds once
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
         const bool in = base + (int64_t)i * kBlock + t < n;
         const uint32_t d = (k[i] >> shift) & (kRadix - 1);
-        const uint64_t peers = match_digit(d, in);
-        if (in && (peers & lt_mask) == 0) atomicAdd(&h[d], (uint32_t)__popcll(peers));
+        const uint64_t act = __ballot(in);
+        const uint32_t d0 = uniform(d);
+        if (__ballot(in && d == d0) == act) {
+            if (lane == 0 && act) atomicAdd(&h[d0], (uint32_t)__popcll(act));
+        } else if (in) {
+            atomicAdd(&h[d], 1u);
+        }
     }
     __syncthreads();
     for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
@@ -152,6 +158,20 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
     const int cnt = (int)min<int64_t>(kSortTile, n - base);
 
+    // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
+    // so (wave, j, lane) order is index order and the ranking below is stable.
+    // All loads are issued first: the barriers and fences below would otherwise
+    // hold each load behind the previous step.
+    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kSortItems; j++) {
+        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
+        const bool in = li < cnt;
+        key[j] = in ? *gp(kin + base + li) : 0u;
+        val[j] = in ? *gp(vin + base + li) : 0u;
+    }
+
     // digit offsets: global prefix over digits + this block's offset within each digit
     {
         uint32_t v[kDigitsPerThread], ex[kDigitsPerThread];
@@ -168,16 +188,10 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     }
     __syncthreads();
 
-    // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
-    // so (wave, j, lane) order is index order and the ranking below is stable
-    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int j = 0; j < kSortItems; j++) {
         const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
         const bool in = li < cnt;
-        key[j] = in ? *gp(kin + base + li) : 0u;
-        val[j] = in ? *gp(vin + base + li) : 0u;
         const uint32_t d = (key[j] >> shift) & (kRadix - 1);
         const uint64_t peers = match_digit(d, in);
         const uint32_t before = S.run[w][d];
@@ -244,8 +258,18 @@ __device__ __forceinline__ int uq_stage(UqLds &S, const uint32_t *k, int64_t n)
 {
     const int64_t base = (int64_t)blockIdx.x * kUqTile;
     const int cnt = (int)min<int64_t>(kUqTile, n - base);
-    for (int i = threadIdx.x; i < cnt; i += kBlock) S.key[i + 1] = *gp(k + base + i);
+    uint32_t x[kUqTile / kBlock];
+#pragma unroll
+    for (int j = 0; j < kUqTile / kBlock; j++) {
+        const int i = j * kBlock + threadIdx.x;
+        x[j] = i < cnt ? *gp(k + base + i) : 0u;
+    }
     if (threadIdx.x == 0) S.key[0] = base > 0 ? *gp(k + base - 1) : 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < kUqTile / kBlock; j++) {
+        const int i = j * kBlock + threadIdx.x;
+        if (i < cnt) S.key[i + 1] = x[j];
+    }
     __syncthreads();
     return cnt;
 }
@@ -353,6 +377,7 @@ struct BwdArgs {
     int32_t *pcnt;
     uint32_t *tick;
     int32_t any_mean;           // some column pools by mean
+    int32_t zero;               // 0, unknown to the compiler: keeps repeated row loads distinct
 };
 
 struct BwdLds {
@@ -372,16 +397,20 @@ struct BTile {
     int t0, t1, uf, ul, wb, wn, U;
 };
 
-__device__ __forceinline__ int segat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
+// Segment starts and keys of the segments a tile touches, from its LDS window.
+// The window always covers them: it starts at the tile's first segment uf and
+// holds kOffCap > kTileMax + 1 entries (or all up to U), while every later
+// segment of the tile starts at a distinct contributor inside the tile, so the
+// tile needs entries uf .. uf + kTileMax at most.  Reading LDS only keeps
+// global loads (and the waits they bring) out of the walk.
+__device__ __forceinline__ int segat(const BwdArgs &, const BwdLds &L, const BTile &t, int u)
 {
-    const unsigned i = (unsigned)(u - t.wb);
-    return (int)(i < (unsigned)t.wn ? L.seg[i] : *gp(a.seg + u));
+    return (int)L.seg[u - t.wb];
 }
 
-__device__ __forceinline__ uint32_t ukeyat(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
+__device__ __forceinline__ uint32_t ukeyat(const BwdArgs &, const BwdLds &L, const BTile &t, int u)
 {
-    const unsigned i = (unsigned)(u - t.wb);
-    return i < (unsigned)t.wn ? L.ukey[i] : *gp(a.ukeys + u);
+    return L.ukey[u - t.wb];
 }
 
 __device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const BTile &t, int p)
@@ -394,24 +423,26 @@ __device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const B
     return lo;
 }
 
-// A table row slice (4 elements per lane) and its Adagrad accumulator, read
-// when a segment starts so that the update at its end does not wait.
+// A table row slice (4 elements per lane, raw bits: fp32, or bf16 pairs in w[0..1])
+// and its Adagrad accumulator, read when a segment starts so that the update at
+// its end does not wait.  Decoding waits for the load, so it happens at the update.
 struct RowPre {
-    float w[4], s[4];
+    uint32_t w[4];
+    float s[4];
 };
 
+template <int OPT, bool BF>
 __device__ __forceinline__ void row_load(const BwdArgs &a, const DevCol &col, int64_t e, RowPre &r)
 {
-    if (a.opt == EMB_OPT_EMIT) return;
-    if (col.dtype == EMB_BF16) {
-        const uint64_t raw = *gp(reinterpret_cast<const uint64_t *>(static_cast<const uint16_t *>(col.weights) + e));
-        const uint32_t lo = (uint32_t)raw, hi = (uint32_t)(raw >> 32);
-        r.w[0] = bf16_lo(lo); r.w[1] = bf16_hi(lo); r.w[2] = bf16_lo(hi); r.w[3] = bf16_hi(hi);
+    if (OPT == EMB_OPT_EMIT) return;
+    if (BF) {
+        const uint2 raw = *gp(reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(col.weights) + e));
+        r.w[0] = raw.x; r.w[1] = raw.y;
     } else {
-        const float4 raw = *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + e));
+        const uint4 raw = *gp(reinterpret_cast<const uint4 *>(static_cast<const float *>(col.weights) + e));
         r.w[0] = raw.x; r.w[1] = raw.y; r.w[2] = raw.z; r.w[3] = raw.w;
     }
-    if (a.opt == EMB_OPT_ADAGRAD) {
+    if (OPT == EMB_OPT_ADAGRAD) {
         const float4 sv = *gp(reinterpret_cast<const float4 *>(col.state + e));
         r.s[0] = sv.x; r.s[1] = sv.y; r.s[2] = sv.z; r.s[3] = sv.w;
     }
@@ -419,33 +450,40 @@ __device__ __forceinline__ void row_load(const BwdArgs &a, const DevCol &col, in
 
 // the finished gradient g of unique row u (4 fp32 per lane): emit it, or
 // update the row whose old values are in `r`
+template <int OPT, bool BF>
 __device__ __forceinline__ void row_apply(const BwdArgs &a, const DevCol &col, int u, int64_t e,
                                           const float (&g)[4], RowPre &r, int q)
 {
-    if (a.opt == EMB_OPT_EMIT) {
+    if (OPT == EMB_OPT_EMIT) {
         if (a.ugrads)
             *gp(reinterpret_cast<float4 *>(a.ugrads + (int64_t)u * a.maxD + q * 4)) =
                 make_float4(g[0], g[1], g[2], g[3]);
         return;
     }
-    if (a.opt == EMB_OPT_SGD) {
+    float w[4];
+    if (BF) {
+        w[0] = bf16_lo(r.w[0]); w[1] = bf16_hi(r.w[0]); w[2] = bf16_lo(r.w[1]); w[3] = bf16_hi(r.w[1]);
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; v++) r.w[v] = r.w[v] - a.lr * g[v];
+        for (int v = 0; v < 4; v++) w[v] = __uint_as_float(r.w[v]);
+    }
+    if (OPT == EMB_OPT_SGD) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) w[v] = w[v] - a.lr * g[v];
     } else {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             r.s[v] = r.s[v] + g[v] * g[v];
-            r.w[v] = r.w[v] - a.lr * g[v] / (sqrtf(r.s[v]) + a.eps);
+            w[v] = w[v] - a.lr * g[v] / (sqrtf(r.s[v]) + a.eps);
         }
         *gp(reinterpret_cast<float4 *>(col.state + e)) = make_float4(r.s[0], r.s[1], r.s[2], r.s[3]);
     }
-    if (col.dtype == EMB_BF16) {
-        const uint64_t o = (uint64_t)(f32_to_bf16_rne(r.w[0]) | (f32_to_bf16_rne(r.w[1]) << 16)) |
-                           ((uint64_t)(f32_to_bf16_rne(r.w[2]) | (f32_to_bf16_rne(r.w[3]) << 16)) << 32);
+    if (BF) {
+        const uint64_t o = (uint64_t)(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16)) |
+                           ((uint64_t)(f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)) << 32);
         *gp(reinterpret_cast<uint64_t *>(static_cast<uint16_t *>(col.weights) + e)) = o;
     } else {
-        *gp(reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e)) =
-            make_float4(r.w[0], r.w[1], r.w[2], r.w[3]);
+        *gp(reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e)) = make_float4(w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -457,14 +495,15 @@ __device__ __forceinline__ int64_t row_elem(const BwdArgs &a, const BwdLds &L, c
 
 // a segment that finished in another place than where it started: load its
 // row now and apply
+template <int OPT, bool BF>
 __device__ __forceinline__ void seg_out(const BwdArgs &a, const BwdLds &L, const BTile &t,
                                        const DevCol &col, int u, const float (&g)[4], int q, bool qa)
 {
     if (!qa) return;
     const int64_t e = row_elem(a, L, t, col, u, q);
     RowPre r;
-    row_load(a, col, e, r);
-    row_apply(a, col, u, e, g, r, q);
+    row_load<OPT, BF>(a, col, e, r);
+    row_apply<OPT, BF>(a, col, u, e, g, r, q);
 }
 
 // a piece of a segment that crosses a tile boundary: publish it; the tile whose
@@ -497,6 +536,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLds &L, const BTi
 // Sum the pieces of a queued segment in a fixed order with all 64 lanes: lane
 // slice j = lane / P takes pieces j, j + 64/P, ... (several loads in flight per
 // lane), then the slices are added by a butterfly over the slice bits.
+template <int OPT>
 __device__ __forceinline__ void bwd_job(const BwdArgs &a, const BwdLds &L, const BTile &t, int j)
 {
     const int u = L.job_u[j], c = uniform(L.job_c[j]);
@@ -527,22 +567,25 @@ __device__ __forceinline__ void bwd_job(const BwdArgs &a, const BwdLds &L, const
     for (int o = P; o < kWave; o <<= 1)
 #pragma unroll
         for (int v = 0; v < 4; v++) tot[v] += __shfl_xor(tot[v], o, kWave);
-    if (sl == 0) seg_out(a, L, t, col, u, tot, q, qa);
+    if (sl == 0) {
+        if (col.dtype == EMB_BF16) seg_out<OPT, true>(a, L, t, col, u, tot, q, qa);
+        else seg_out<OPT, false>(a, L, t, col, u, tot, q, qa);
+    }
     if (lane == 0) st_agent(&a.tick[k0], 0u);  // ready for the next call
 }
 
 // one column run [s0, s1) of sorted contributors; P lanes per gradient row
+template <int OPT, bool BF>
 __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t,
                                             const DevCol &col, int c, int s0, int s1)
 {
-    constexpr int U = 8;
+    constexpr int U = 4;
     const int P = col.glanes, lp = __ffs(P) - 1;
     const int G = kWave >> lp;
     const int lane = lane_id(), g = lane >> lp, q = lane & (P - 1);
     const bool qa = q < col.dim / 4;
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
-    const float *gbase = a.G + col.out_off + q * 4;
     const int cB = c * a.B;
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f}, hacc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -552,55 +595,66 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
         int u = seg_of(a, L, t, ga);
         int uend = segat(a, L, t, u + 1);
         bool before = segat(a, L, t, u) < ga;
-        int64_t e = 0;
-        RowPre pre;
-        if (!before && qa) {
-            e = row_elem(a, L, t, col, u, q);
-            row_load(a, col, e, pre);
-        }
+        // Row loads are issued for every contributor, unconditionally: the row of
+        // the segment holding it (lanes past the row's end read lane 0's slice),
+        // used only where a segment starts.  Loads that are always issued keep the
+        // compiler's wait counts exact; conditional ones made it wait for every
+        // earlier load before issuing the next.  Repeats of a row hit in cache.
+        const int qq = qa ? q : 0;
+        RowPre cur;
+        row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u, qq), cur);
+        int64_t e = row_elem(a, L, t, col, u, qq);
+        const float *gq = a.G + col.out_off + qq * 4;
         for (int p = ga; p < ge; p += U) {
+            // one batch: the rows of its contributors' segments, then U gradient
+            // slices, all in flight together
             float4 x[U];
             float wt[U];
+            bool st[U];
+            RowPre pre[U];
+            int ue = uend, ns = 0;
 #pragma unroll
-            for (int u2 = 0; u2 < U; u2++) {
-                const int pp = p + u2;
-                x[u2] = make_float4(0.f, 0.f, 0.f, 0.f);
-                wt[u2] = 0.f;
-                if (pp < ge) {
-                    wt[u2] = L.wt[pp - t.t0];
-                    if (qa)
-                        x[u2] = *gp(reinterpret_cast<const float4 *>(
-                            gbase + (int64_t)(L.bag[pp - t.t0] - cB) * a.sumD));
+            for (int j = 0; j < U; j++) {
+                st[j] = p + j < ge && p + j == ue;
+                if (st[j]) {
+                    ns++;
+                    ue = segat(a, L, t, u + ns + 1);   // end of segment u + ns
                 }
+                // a.zero stops the compiler from merging repeats of one row into
+                // register copies, which would wait for the load
+                row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u + ns, qq) + (int64_t)j * a.zero, pre[j]);
             }
 #pragma unroll
-            for (int u2 = 0; u2 < U; u2++) {
-                const int pp = p + u2;
-                if (pp < ge) {
-                    if (pp == uend) {
+            for (int j = 0; j < U; j++) {
+                const int pl = min(p + j, ge - 1) - t.t0;
+                wt[j] = p + j < ge ? L.wt[pl] : 0.f;
+                x[j] = *gp(reinterpret_cast<const float4 *>(gq + (int64_t)(L.bag[pl] - cB) * a.sumD));
+            }
+#pragma unroll
+            for (int j = 0; j < U; j++) {
+                if (p + j < ge) {
+                    if (st[j]) {                   // segment u ended just before p + j
                         if (before) {
 #pragma unroll
                             for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                             hseg = u; hpass = false;
                         } else if (qa) {
-                            row_apply(a, col, u, e, acc, pre, q);
+                            row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
                         }
 #pragma unroll
                         for (int v = 0; v < 4; v++) acc[v] = 0.f;
                         u++;
-                        uend = segat(a, L, t, u + 1);
                         before = false;
-                        if (qa) {
-                            e = row_elem(a, L, t, col, u, q);
-                            row_load(a, col, e, pre);
-                        }
+                        cur = pre[j];
+                        e = row_elem(a, L, t, col, u, qq);
                     }
-                    acc[0] += wt[u2] * x[u2].x;
-                    acc[1] += wt[u2] * x[u2].y;
-                    acc[2] += wt[u2] * x[u2].z;
-                    acc[3] += wt[u2] * x[u2].w;
+                    acc[0] += wt[j] * x[j].x;
+                    acc[1] += wt[j] * x[j].y;
+                    acc[2] += wt[j] * x[j].z;
+                    acc[3] += wt[j] * x[j].w;
                 }
             }
+            uend = ue;
         }
         if (uend == ge) {
             if (before) {
@@ -608,7 +662,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                 hseg = u; hpass = false;
             } else if (qa) {
-                row_apply(a, col, u, e, acc, pre, q);
+                row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
             }
         } else if (before) {
 #pragma unroll
@@ -633,7 +687,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             if (!L.hpass[g2]) { ended = true; break; }
         }
-        if (ended) seg_out(a, L, t, col, tseg, sum, q, qa);
+        if (ended) seg_out<OPT, BF>(a, L, t, col, tseg, sum, q, qa);
         else bwd_piece(a, L, t, c, 1, tseg, sum, g * P, q, qa);
     }
     if (g == 0 && hseg >= 0) {
@@ -650,13 +704,14 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     wave_sync();
 }
 
-__global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
+template <int OPT>
+__global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 {
-    __shared__ BwdLds lds[kWavesPerBlock];
+    __shared__ BwdLds lds[kTileWaves];
     const int w = threadIdx.x / kWave, lane = lane_id();
     BwdLds &L = lds[w];
     BTile t;
-    t.k = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     const int nv = (int)*gp(a.misc), U = (int)*gp(a.misc + 1);
     t.U = U;
@@ -680,9 +735,23 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
     t.uf = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)t.t0) - 1;
     t.wb = t.uf;
     t.wn = min(U + 1 - t.uf, kOffCap);
-    for (int i = lane; i < t.wn; i += kWave) {
-        L.seg[i] = *gp(a.seg + t.wb + i);
-        L.ukey[i] = (t.wb + i < U) ? *gp(a.ukeys + t.wb + i) : 0xFFFFFFFFu;
+    {
+        // all window loads in flight at once
+        uint32_t sg[kOffCap / kWave], uk[kOffCap / kWave];
+#pragma unroll
+        for (int j = 0; j < kOffCap / kWave; j++) {
+            const int i = lane + kWave * j;
+            sg[j] = i < t.wn ? *gp(a.seg + t.wb + i) : 0u;
+            uk[j] = (i < t.wn && t.wb + i < U) ? *gp(a.ukeys + t.wb + i) : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (int j = 0; j < kOffCap / kWave; j++) {
+            const int i = lane + kWave * j;
+            if (i < t.wn) {
+                L.seg[i] = sg[j];
+                L.ukey[i] = uk[j];
+            }
+        }
     }
     wave_sync();
     if (L.seg[t.wn - 1] > (uint32_t)(t.t1 - 1))
@@ -715,12 +784,13 @@ __global__ __launch_bounds__(kBlock) void seg_apply(BwdArgs a)
             for (int q = p + lane; q < s1; q += kWave) L.wt[q - t.t0] = 1.0f;
             wave_sync();
         }
-        bwd_segment(a, L, t, col, c, p, s1);
+        if (col.dtype == EMB_BF16) bwd_segment<OPT, true>(a, L, t, col, c, p, s1);
+        else bwd_segment<OPT, false>(a, L, t, col, c, p, s1);
         p = s1;
     }
     wave_sync();
     const int nj = uniform(L.njob);
-    for (int j = 0; j < nj; j++) bwd_job(a, L, t, j);
+    for (int j = 0; j < nj; j++) bwd_job<OPT>(a, L, t, j);
 }
 
 }  // namespace emb
@@ -818,8 +888,15 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
     a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
     a.any_mean = plan->any_mean ? 1 : 0;
-    const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(seg_apply, dim3((unsigned)blocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    a.zero = 0;
+    const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.opt == EMB_OPT_EMIT)
+        hipLaunchKernelGGL(seg_apply<EMB_OPT_EMIT>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
+    else if (a.opt == EMB_OPT_SGD)
+        hipLaunchKernelGGL(seg_apply<EMB_OPT_SGD>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL(seg_apply<EMB_OPT_ADAGRAD>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("seg_apply launch: ") + hipGetErrorString(e));
     return EMB_OK;

@@ -47,14 +47,18 @@ struct FwdArgs {
     uint32_t total_rows;
 };
 
+constexpr int kColCache = 8;
+
 struct WaveLds {
     int32_t rows[kTileMax];          // transformed row of each tile position
+    int32_t pbag[kTileMax];          // bag of each tile position (training)
     int32_t off[kOffCap];            // window of CSR offsets
     union {
         float part[kWave][4];        // per-lane partial sum of each run's first bag
         float bnd[kBndCap];          // bucket boundaries of the current column
     } x;
     int32_t hbag[kWave], hcnt[kWave], hpass[kWave];
+    int32_t cout[kColCache], cdim[kColCache];   // output offset and dim of columns c_first + i
 };
 
 struct TileCtx {
@@ -70,29 +74,42 @@ __device__ __forceinline__ int offat(const FwdArgs &a, const WaveLds &L, const T
     return i < (unsigned)t.wn ? L.off[i] : *gp(a.off + b);
 }
 
+// Offsets of the bags the walk touches (bf .. bl + 1).  When the LDS window
+// covers them all (W, the usual case) the walk reads LDS only: a global
+// fallback inside the walk makes the compiler wait for every outstanding load
+// and store before each lookup.
+template <bool W>
+__device__ __forceinline__ int offw(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+{
+    if (W) return L.off[b - t.wb];
+    return offat(a, L, t, b);
+}
+
 // the non-empty bag containing position p (p inside the tile)
+template <bool W>
 __device__ __forceinline__ int bag_of(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int p)
 {
     int lo = t.bf, hi = t.bl + 1;   // off[lo] <= p < off[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (offat(a, L, t, mid) <= p) lo = mid; else hi = mid;
+        if (offw<W>(a, L, t, mid) <= p) lo = mid; else hi = mid;
     }
     return lo;
 }
 
 // the next non-empty bag after b (a later position exists)
+template <bool W>
 __device__ __forceinline__ int next_bag(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
 {
     int nb = b + 1;
-    while (offat(a, L, t, nb + 1) == offat(a, L, t, nb)) nb++;
+    while (offw<W>(a, L, t, nb + 1) == offw<W>(a, L, t, nb)) nb++;
     return nb;
 }
 
 template <int V>
 __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int c, int bag,
                                         const float (&acc)[V], int n, int q, bool qa,
-                                        int64_t &zero_bags)
+                                        int32_t &zero_bags)
 {
     const int s = bag - c * a.B;
     if (qa) {
@@ -112,14 +129,14 @@ __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int
 
 // a piece of a bag that crosses a tile boundary: publish it, and if this is the
 // last piece to arrive, sum all pieces in tile order and write the bag
-template <int V>
+template <int V, bool W>
 __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t,
                                            const DevCol &col, int c, int side, int bag,
                                            const float (&sum)[V], int n, int leader, int q, bool qa,
-                                           int64_t &zero_bags)
+                                           int32_t &zero_bags)
 {
     const int64_t T = a.T;
-    const int bs = offat(a, L, t, bag), be = offat(a, L, t, bag + 1);
+    const int bs = offw<W>(a, L, t, bag), be = offw<W>(a, L, t, bag + 1);
     const int64_t k0 = bs / T, k1 = (be - 1) / T;
     const int64_t slot = t.k * 2 + side;
     float *pp = a.part + slot * a.maxD + q * V;
@@ -138,27 +155,55 @@ __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, c
         int tn = ld_agent(a.pcnt + k0 * 2 + 1);
 #pragma unroll
         for (int v = 0; v < V; v++) tot[v] = qa ? ld_agent(p0 + v) : 0.f;
-        for (int64_t kk = k0 + 1; kk <= k1; kk++) {
-            const float *pk = a.part + (kk * 2) * a.maxD + q * V;
-            tn += ld_agent(a.pcnt + kk * 2);
+        // the incoming pieces of tiles k0+1 .. k1, four in flight at a time,
+        // added in tile order
+        constexpr int UP = 4;
+        for (int64_t k2 = k0 + 1; k2 <= k1; k2 += UP) {
+            float x[UP][V];
+            int xn[UP];
 #pragma unroll
-            for (int v = 0; v < V; v++) tot[v] += qa ? ld_agent(pk + v) : 0.f;
+            for (int r = 0; r < UP; r++) {
+                const int64_t kk = min(k2 + r, k1);
+                const float *pk = a.part + (kk * 2) * a.maxD + q * V;
+                xn[r] = ld_agent(a.pcnt + kk * 2);
+#pragma unroll
+                for (int v = 0; v < V; v++) x[r][v] = qa ? ld_agent(pk + v) : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < UP; r++) {
+                if (k2 + r > k1) break;
+                tn += xn[r];
+#pragma unroll
+                for (int v = 0; v < V; v++) tot[v] += x[r][v];
+            }
         }
         bag_out<V>(a, col, c, bag, tot, tn, q, qa, zero_bags);
         if (q == 0) st_agent(&a.tick[k0], 0u);   // ready for the next call
     }
 }
 
+// 4 row elements of one lane as loaded: fp32, or bf16 pairs
+template <bool BF> struct RowRawT { using type = float4; };
+template <> struct RowRawT<true> { using type = uint2; };
+template <bool BF> using RowRaw = typename RowRawT<BF>::type;
+
+__device__ __forceinline__ float4 row_f32(const float4 &v) { return v; }
+__device__ __forceinline__ float4 row_f32(const uint2 &v)
+{
+    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+}
+
 // one column segment [s0, s1) of the tile.  A row is read by P lanes (a power
-// of two), 4 elements per lane: 16-byte loads for fp32 rows, 8-byte for bf16.
+// of two), 4 elements per lane: 16-byte loads for fp32 rows (BF false), 8-byte
+// for bf16.
+template <bool BF, bool W>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
-                                            int64_t &zero_bags)
+                                            int32_t &zero_bags)
 {
     constexpr int V = 4;
     constexpr int U = 8;                       // row loads in flight per lane
-    const bool bf = col.dtype == EMB_BF16;
-    const int esz = bf ? 2 : 4;
+    constexpr int esz = BF ? 2 : 4;
     const int P = col.lanes, lp = __ffs(P) - 1;
     const int G = kWave >> lp;
     const int lane = lane_id(), g = lane >> lp, q = lane & (P - 1);
@@ -166,7 +211,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     const bool qa = q < D / V;
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
-    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)q * V * esz;
+    // lanes past the row's end read lane 0's slice and ignore it
+    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)(qa ? q : 0) * V * esz;
     const int64_t rstride = (int64_t)D * esz;
 
     float acc[V], hacc[V];
@@ -176,29 +222,19 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     bool hpass = false;
 
     if (ga < ge) {
-        int b = bag_of(a, L, t, ga);
-        int bend = offat(a, L, t, b + 1);
-        bool before = offat(a, L, t, b) < ga;
+        int b = bag_of<W>(a, L, t, ga);
+        int bend = offw<W>(a, L, t, b + 1);
+        bool before = offw<W>(a, L, t, b) < ga;
         for (int p = ga; p < ge; p += U) {
+            // every load is issued (dropped / default / past-the-run positions read
+            // row 0), so that the single wait below covers exactly these loads
             int r[U];
-            float4 w[U];
+            RowRaw<BF> h[U];
 #pragma unroll
             for (int u = 0; u < U; u++) r[u] = (p + u < ge) ? L.rows[p + u - t.t0] : -1;
-            if (bf) {
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    uint64_t h = 0;
-                    if (r[u] >= 0 && qa) h = *gp(reinterpret_cast<const uint64_t *>(wbase + r[u] * rstride));
-                    const uint32_t lo = (uint32_t)h, hi = (uint32_t)(h >> 32);
-                    w[u] = make_float4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi));
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; u++) {
-                    w[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (r[u] >= 0 && qa) w[u] = *gp(reinterpret_cast<const float4 *>(wbase + r[u] * rstride));
-                }
-            }
+            for (int u = 0; u < U; u++)
+                h[u] = *gp(reinterpret_cast<const RowRaw<BF> *>(wbase + (int64_t)max(r[u], 0) * rstride));
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int pp = p + u;
@@ -214,12 +250,16 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
 #pragma unroll
                         for (int v = 0; v < V; v++) acc[v] = 0.f;
                         cnt = 0;
-                        b = next_bag(a, L, t, b);
-                        bend = offat(a, L, t, b + 1);
+                        b = next_bag<W>(a, L, t, b);
+                        bend = offw<W>(a, L, t, b + 1);
                         before = false;
                     }
-                    acc[0] += w[u].x; acc[1] += w[u].y; acc[2] += w[u].z; acc[3] += w[u].w;
+                    if (r[u] >= 0) {
+                        const float4 w = row_f32(h[u]);
+                        acc[0] += w.x; acc[1] += w.y; acc[2] += w.z; acc[3] += w.w;
+                    }
                     cnt += (r[u] != -1);
+                    if (q == 0) L.pbag[pp - t.t0] = b;
                 }
             }
         }
@@ -266,7 +306,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             if (!L.hpass[g2]) { ended = true; break; }
         }
         if (ended) bag_out<V>(a, col, c, tbag, sum, n, q, qa, zero_bags);
-        else tile_piece<V>(a, L, t, col, c, 1, tbag, sum, n, g * P, q, qa, zero_bags);
+        else tile_piece<V, W>(a, L, t, col, c, 1, tbag, sum, n, g * P, q, qa, zero_bags);
     }
     // the bag that came in from the previous tile
     if (g == 0 && hbag >= 0) {
@@ -282,7 +322,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             n += L.hcnt[g2];
             pass = L.hpass[g2];
         }
-        tile_piece<V>(a, L, t, col, c, 0, hbag, sum, n, 0, q, qa, zero_bags);
+        tile_piece<V, W>(a, L, t, col, c, 0, hbag, sum, n, 0, q, qa, zero_bags);
     }
     wave_sync();
 }
@@ -300,9 +340,19 @@ __device__ __forceinline__ int bucket_count(B b, int nb, float x)
 
 constexpr int kMargin = 64;             // offsets staged before the tile's first bag
 
+constexpr int kPL = kTileMax / kWave;  // tile positions per lane: t0 + lane + 64 i
+
+// The raw inputs of the tile's positions, loaded once at the start of the tile so
+// that they arrive while the offsets are searched.
+struct TileIn {
+    int64_t id[kPL];
+    float fv[kPL];
+    int32_t kr[kPL];
+};
+
 __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
-                                              int64_t (&cnt)[4])
+                                              const TileIn &in, int32_t (&cnt)[4])
 {
     const int lane = lane_id();
     const int nbd = col.n_bnd;
@@ -312,21 +362,24 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
         wave_sync();
     }
     const uint64_t rows = (uint64_t)col.rows;
-    for (int p = s0 + lane; p < s1; p += kWave) {
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        if (p < s0 || p >= s1) continue;
         int r;
         if (col.kind == EMB_COL_HASH) {
-            const int64_t id = *gp(a.ids + p);
+            const int64_t id = in.id[i];
             r = (id >= col.id_lo && id < col.id_hi)
                     ? (int)mod_magic(splitmix64((uint64_t)id), rows, col.magic) : -1;
         } else if (col.kind == EMB_COL_IDENTITY) {
-            const int64_t id = *gp(a.ids + p);
+            const int64_t id = in.id[i];
             r = (id >= 0 && (uint64_t)id < rows) ? (int)id : -1;
         } else if (col.kind == EMB_COL_BUCKET) {
-            const float x = *gp(a.fvals + p);
+            const float x = in.fv[i];
             r = (x != x) ? -1 : (staged ? bucket_count(L.x.bnd, nbd, x)
                                         : bucket_count(gp(col.boundaries), nbd, x));
         } else {
-            const int kr = *gp(a.krows + p);
+            const int kr = in.kr[i];
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
         L.rows[p - t.t0] = r;
@@ -334,27 +387,51 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
         cnt[1] += (r >= 0);
         cnt[2] += (r == -1);
         cnt[3] += (r == -2);
-        if (a.training) {
+        if (a.training)
             *gp(a.keys + p) = r >= 0 ? col.row_base + (uint32_t)r
                                      : (r == -2 ? a.total_rows + 1u : a.total_rows);
-            *gp(a.bags + p) = bag_of(a, L, t, p);
-        }
     }
     wave_sync();
 }
 
-__global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
+// Positions of column c inside the tile.  The first column starts at or before
+// t0 and the last ends at or after t1; the other boundaries are bags bf+1 .. bl,
+// inside the LDS window when it covers the walk (win).
+__device__ __forceinline__ int col_lo(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int c,
+                                      int c_first, bool win)
 {
-    __shared__ WaveLds lds[kWavesPerBlock];
+    if (c == c_first) return t.t0;
+    return max(t.t0, win ? offw<true>(a, L, t, c * a.B) : offat(a, L, t, c * a.B));
+}
+
+__device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int c,
+                                      int c_last, bool win)
+{
+    if (c == c_last) return t.t1;
+    return min(t.t1, win ? offw<true>(a, L, t, (c + 1) * a.B) : offat(a, L, t, (c + 1) * a.B));
+}
+
+__global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
+{
+    __shared__ WaveLds lds[kTileWaves];
     const int w = threadIdx.x / kWave, lane = lane_id();
     WaveLds &L = lds[w];
     TileCtx t;
-    t.k = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     const int N = (int)a.N, T = a.T, nbag = a.C * a.B;
     t.t0 = (int)min<int64_t>(t.k * T, N);
     t.t1 = (int)min<int64_t>((t.k + 1) * T, N);
     const bool last = t.k == a.ntiles - 1;
+    TileIn in;
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        const bool ok = p < t.t1;
+        in.id[i] = (a.ids && ok) ? *gp(a.ids + p) : 0;
+        in.fv[i] = (a.fvals && ok) ? *gp(a.fvals + p) : 0.f;
+        in.kr[i] = (a.krows && ok) ? *gp(a.krows + p) : 0;
+    }
 
     // the bags this tile touches: one global search for the first, then the
     // offsets window in LDS answers the rest
@@ -367,7 +444,20 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
         t.wb = 0;
     }
     t.wn = min(nbag + 1 - t.wb, kOffCap);
-    for (int i = lane; i < t.wn; i += kWave) L.off[i] = *gp(a.off + t.wb + i);
+    {
+        // all window loads in flight at once
+        int o[kOffCap / kWave];
+#pragma unroll
+        for (int j = 0; j < kOffCap / kWave; j++) {
+            const int i = lane + kWave * j;
+            o[j] = i < t.wn ? *gp(a.off + t.wb + i) : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kOffCap / kWave; j++) {
+            const int i = lane + kWave * j;
+            if (i < t.wn) L.off[i] = o[j];
+        }
+    }
     wave_sync();
     if (t.t0 < t.t1) {
         const int f = t.bf - t.wb;
@@ -388,36 +478,55 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a)
         own_hi = nbag;
     }
 
-    int64_t cnt[4] = {0, 0, 0, 0};
-    int64_t zero_bags = 0;
+    int32_t cnt[4] = {0, 0, 0, 0};   // per lane: at most kPL positions, kWave bags
+    int32_t zero_bags = 0;
     if (t.t0 < t.t1) {
         const int c_first = t.bf / a.B, c_last = t.bl / a.B;
+        const bool win = t.bl + 1 < t.wb + t.wn;   // the window covers every bag the walk reads
         // transform every position of the tile, then walk each column segment
         for (int c = c_first; c <= c_last; c++) {
             const int cu = uniform(c);
-            const int s0 = max(t.t0, offat(a, L, t, cu * a.B));
-            const int s1 = min(t.t1, offat(a, L, t, (cu + 1) * a.B));
+            if (cu - c_first < kColCache && lane == 0) {
+                L.cout[cu - c_first] = a.cols[cu].out_off;
+                L.cdim[cu - c_first] = a.cols[cu].dim;
+            }
+            const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            fwd_transform(a, L, t, col, s0, s1, cnt);
+            fwd_transform(a, L, t, col, s0, s1, in, cnt);
         }
         for (int c = c_first; c <= c_last; c++) {
             const int cu = uniform(c);
-            const int s0 = max(t.t0, offat(a, L, t, cu * a.B));
-            const int s1 = min(t.t1, offat(a, L, t, (cu + 1) * a.B));
+            const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            fwd_segment(a, L, t, col, cu, s0, s1, zero_bags);
+            if (win) {
+                if (col.dtype == EMB_BF16) fwd_segment<true, true>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, true>(a, L, t, col, cu, s0, s1, zero_bags);
+            } else {
+                if (col.dtype == EMB_BF16) fwd_segment<true, false>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, false>(a, L, t, col, cu, s0, s1, zero_bags);
+            }
+        }
+        if (a.training) {
+#pragma unroll
+            for (int i = 0; i < kPL; i++) {
+                const int p = t.t0 + lane + kWave * i;
+                if (p < t.t1) *gp(a.bags + p) = L.pbag[p - t.t0];
+            }
         }
     }
 
     // bags with no position that this tile owns: the zero default
+    const int c_base = t.t0 < t.t1 ? t.bf / a.B : 0;
     for (int b = own_lo + lane; b < own_hi; b += kWave) {
         if (offat(a, L, t, b) != offat(a, L, t, b + 1)) continue;
         const int c = b / a.B;
-        EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD +
-                                                             *gp(&a.cols[c].out_off)));
-        const int dim = *gp(&a.cols[c].dim);
+        // columns of the tile's own bags were cached when transformed
+        const bool cached = t.t0 < t.t1 && c >= c_base && c - c_base < kColCache && c <= t.bl / a.B;
+        const int oo = cached ? L.cout[c - c_base] : (int)*gp(&a.cols[c].out_off);
+        const int dim = cached ? L.cdim[c - c_base] : *gp(&a.cols[c].dim);
+        EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD + oo));
         for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (a.training) *gp(a.bag_n + b) = 0;
         zero_bags++;
@@ -480,8 +589,8 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     a.stats = stats;
     a.total_rows = plan->total_rows;
     if (training) plan->last_n = n_ids;
-    const int64_t blocks = (a.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+    const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
+    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kTileBlock), 0,
                        static_cast<hipStream_t>(stream), a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));

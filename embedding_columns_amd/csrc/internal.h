@@ -12,6 +12,14 @@ namespace emb {
 constexpr int kWave = 64;            // CDNA wavefront
 constexpr int kWavesPerBlock = 4;    // each wavefront owns one tile; no block-wide barriers
 constexpr int kBlock = kWave * kWavesPerBlock;
+// The tile kernels (forward, segment apply) launch one wavefront per workgroup:
+// their tiles take very different times, and a single-wave workgroup frees its
+// slot as soon as its tile is done.
+#ifndef EMB_TILE_WAVES
+#define EMB_TILE_WAVES 1
+#endif
+constexpr int kTileWaves = EMB_TILE_WAVES;
+constexpr int kTileBlock = kWave * kTileWaves;
 constexpr int kTileMax = 256;        // positions (or sorted contributors) per wavefront tile
 constexpr int kTileDefault = 256;
 constexpr int kOffCap = kTileMax + 128;  // LDS window of segment offsets per wavefront
@@ -44,6 +52,7 @@ struct DevCol {
     int32_t glanes;          // lanes per gradient row (same as lanes)
 };
 static_assert(sizeof(DevCol) == 96, "DevCol layout");
+static_assert(kOffCap % kWave == 0, "window loads are unrolled per lane");
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
