@@ -157,20 +157,24 @@ def run(args):
     G = W.make_grad(w, seed=cfg, device=dev)
     stats = torch.zeros(E.STAT_COUNT, dtype=torch.int64, device=dev)
     Y = torch.empty(w.batch, w.sum_dim, dtype=torch.float32, device=dev)
-    krows = torch.empty(max_ids, dtype=torch.int32, device=dev) if keyed else None
+    # keyed: one rows buffer per step, read after the timed region for the counts
+    krows = torch.empty(n_pool, max_ids, dtype=torch.int32, device=dev) if keyed else None
     kinds = {c.kind for c in w.cols}
 
-    tstats = stats if (args.stats or keyed) else None
+    # the keyed table's counters (admissions, a full table) are always kept; the
+    # forward / backward counters only with --stats (their atomics cost time)
+    tstats = stats if args.stats else None
+    kstats = stats if (args.stats or keyed) else None
 
     def step(i, ev=None):
         d = dbat[i % len(dbat)]
         n = d["n"]
         if keyed:
-            table.lookup_or_insert(d["ids"], rows_out=krows[:n], stats=tstats)
+            table.lookup_or_insert(d["ids"], rows_out=krows[i][:n], stats=kstats)
         if ev is not None:
             ev[0].record()
         E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
-                      d["fv"] if 2 in kinds else None, krows[:n] if keyed else None, n, Y,
+                      d["fv"] if 2 in kinds else None, krows[i][:n] if keyed else None, n, Y,
                       plan.workspace, training, tstats)
         if ev is not None:
             ev[1].record()
@@ -217,12 +221,19 @@ def run(args):
 
     idx = [(args.warmup + i) % len(dbat) for i in range(args.steps)]
     if keyed:
-        lookups = int(st[1] + st[3])                     # admitted rows + DEFAULT reads
+        # per timed step: positions reading a row, reading DEFAULT, distinct rows
+        rows_read, defaults, distinct = [], [], []
+        for i in range(args.steps):
+            r = krows[args.warmup + i][:batches[args.warmup + i].n]
+            rows_read.append(int((r >= 0).sum().item()))
+            defaults.append(int((r == -2).sum().item()))
+            distinct.append(int(torch.unique(r[r >= 0]).numel()))
+        lookups = sum(rows_read) + sum(defaults)         # admitted rows + DEFAULT reads
         n_steps = args.steps
-        fb = np.mean([fwd_bytes(w, batches[j], [counts[j][0][0]], [st[1] / n_steps], True)
-                      for j in idx])
+        fb = np.mean([fwd_bytes(w, batches[j], [counts[j][0][0]], [rows_read[k]], True)
+                      for k, j in enumerate(idx)])
         valid = lookups / n_steps
-        ub = bwd_bytes(w, st[1] / n_steps, [st[5] / n_steps])
+        ub = np.mean([bwd_bytes(w, rows_read[k], [distinct[k]]) for k in range(n_steps)])
         table_bytes = 8 * batches[0].n + 16 * batches[0].n + 4 * batches[0].n
         step_bytes = fb + ub + table_bytes
     else:

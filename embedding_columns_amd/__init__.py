@@ -288,13 +288,15 @@ class EmbeddingColumns:
         self._n = n_ids
         return out
 
-    def backward(self, grad_out, want_keys=False, want_grads=False, stats=None):
-        """Returns (uniq_keys, uniq_grads, n_uniq) device tensors (None where not asked)."""
+    def backward(self, grad_out, want_keys=False, want_grads=False, stats=None, want_count=True):
+        """Returns (uniq_keys, uniq_grads, n_uniq) device tensors (None where not asked).
+        With nothing asked (no keys, grads, count or stats) and SGD / Adagrad, the
+        library skips building the unique-row list."""
         n = max(getattr(self, "_n", 0), 1)
         keys = torch.empty(n, dtype=torch.int32, device=self.device) if want_keys else None
         grads = (torch.empty(n, self.max_dim, dtype=torch.float32, device=self.device)
                  if want_grads else None)
-        nu = torch.zeros(1, dtype=torch.int64, device=self.device)
+        nu = torch.zeros(1, dtype=torch.int64, device=self.device) if want_count else None
         emb_backward(self.plan, grad_out.contiguous(), self.workspace, keys, grads, nu, stats)
         return keys, grads, nu
 

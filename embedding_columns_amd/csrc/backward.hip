@@ -88,8 +88,11 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDi
 // per-block digit histogram; equal digits within a wavefront are added once
 __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
                                                  int shift, uint32_t *__restrict__ hist,
-                                                 int64_t nblk)
+                                                 int64_t nblk, uint32_t *__restrict__ misc)
 {
+    // the first pass starts the count of valid contributors at n; the last
+    // pass lowers it to the position of the first sentinel key
+    if (shift == 0 && blockIdx.x == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
     __shared__ uint32_t h[kRadix];
     const int t = threadIdx.x, lane = lane_id();
     for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
@@ -151,7 +154,8 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
                                                     uint32_t *__restrict__ kout,
                                                     uint32_t *__restrict__ vout, int64_t n,
                                                     int shift, const uint32_t *__restrict__ hist,
-                                                    const uint32_t *__restrict__ dtot, int64_t nblk)
+                                                    const uint32_t *__restrict__ dtot, int64_t nblk,
+                                                    uint32_t sentinel, uint32_t *__restrict__ misc)
 {
     __shared__ SortLds S;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
@@ -237,12 +241,20 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     }
     __syncthreads();
     // write each digit run contiguously
+    uint32_t first_sentinel = 0xFFFFFFFFu;
     for (int lp = t; lp < cnt; lp += kBlock) {
         const uint32_t k = S.skey[lp];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = S.gbase[d] + (uint32_t)lp - S.lpre[d];
         *gp(kout + dst) = k;
         *gp(vout + dst) = S.sval[lp];
+        if (k >= sentinel) first_sentinel = min(first_sentinel, dst);
+    }
+    // last pass: every key >= sentinel (dropped / default rows) sorts after the
+    // valid ones, so the smallest destination of such a key is their count
+    if (misc) {
+        for (int o = 1; o < kWave; o <<= 1) first_sentinel = min(first_sentinel, (uint32_t)__shfl_xor((int)first_sentinel, o, kWave));
+        if (lane == 0 && first_sentinel != 0xFFFFFFFFu) atomicMin(misc, first_sentinel);
     }
 }
 
@@ -371,6 +383,7 @@ struct BwdArgs {
     const int32_t *bag_n;
     const uint32_t *seg;        // [U + 1]
     const uint32_t *ukeys;      // [U]
+    const uint32_t *skeys;      // sorted keys (segments found from them when seg is not built)
     const uint32_t *misc;       // [0] = valid contributors, [1] = U
     float *ugrads;              // EMIT output or NULL
     float *part;
@@ -704,7 +717,63 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     wave_sync();
 }
 
-template <int OPT>
+// The segments of tile t from the sorted keys, without a unique list: heads
+// (positions whose key differs from the previous one) are compacted into the
+// window in position order; a first segment that began in an earlier tile, or
+// a last one that goes on into a later tile, gets its true start / end from a
+// search of the sorted keys.  Window indices are then local (wb = 0).
+__device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L, BTile &t, int nv)
+{
+    constexpr int kPL = kTileMax / kWave;
+    const int lane = lane_id();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t kr[kPL];
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        kr[i] = p < t.t1 ? *gp(a.skeys + p) : 0u;
+    }
+    const uint32_t kprev = t.t0 > 0 ? *gp(a.skeys + t.t0 - 1) : 0xFFFFFFFFu;
+    const uint32_t knext = t.t1 < nv ? *gp(a.skeys + t.t1) : 0xFFFFFFFFu;
+    // tile keys into LDS (the bag array is filled later), to compare neighbours
+    int32_t *tk = L.bag;
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        if (p < t.t1) tk[p - t.t0] = (int32_t)kr[i];
+    }
+    wave_sync();
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int p = t.t0 + lane + kWave * i;
+        const bool head = p < t.t1 && (p == t.t0 || (uint32_t)tk[p - t.t0 - 1] != kr[i]);
+        const uint64_t m = __ballot(head);
+        if (head) {
+            const int j = base + __popcll(m & lt_mask);
+            L.seg[j] = (uint32_t)p;
+            L.ukey[j] = kr[i];
+        }
+        base += __popcll(m);
+    }
+    wave_sync();
+    const int nseg = base;
+    const uint32_t k0 = L.ukey[0], kl = L.ukey[nseg - 1];
+    int start = t.t0, end = t.t1;
+    if (kprev == k0) start = (int)wave_lower_bound(a.skeys, (int64_t)t.t0, k0);
+    if (knext == kl) end = t.t1 + (int)wave_upper_bound(a.skeys + t.t1, (int64_t)(nv - t.t1), kl);
+    if (lane == 0) {
+        L.seg[0] = (uint32_t)start;
+        L.seg[nseg] = (uint32_t)end;
+    }
+    wave_sync();
+    t.wb = 0;
+    t.wn = nseg + 1;
+    t.uf = 0;
+    t.ul = nseg - 1;
+}
+
+template <int OPT, bool KM>
 __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 {
     __shared__ BwdLds lds[kTileWaves];
@@ -713,8 +782,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     BTile t;
     t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
-    const int nv = (int)*gp(a.misc), U = (int)*gp(a.misc + 1);
-    t.U = U;
+    const int nv = (int)*gp(a.misc);
     t.t0 = (int)min<int64_t>(t.k * a.T, nv);
     t.t1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
     if (t.t0 >= t.t1) return;
@@ -732,32 +800,38 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         const int p = t.t0 + lane + kWave * i;
         nr[i] = (a.any_mean && p < t.t1) ? *gp(a.bag_n + bagr[i]) : 1;
     }
-    t.uf = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)t.t0) - 1;
-    t.wb = t.uf;
-    t.wn = min(U + 1 - t.uf, kOffCap);
-    {
-        // all window loads in flight at once
-        uint32_t sg[kOffCap / kWave], uk[kOffCap / kWave];
+    if (KM) {
+        seg_window_from_keys(a, L, t, nv);
+    } else {
+        const int U = (int)*gp(a.misc + 1);
+        t.U = U;
+        t.uf = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)t.t0) - 1;
+        t.wb = t.uf;
+        t.wn = min(U + 1 - t.uf, kOffCap);
+        {
+            // all window loads in flight at once
+            uint32_t sg[kOffCap / kWave], uk[kOffCap / kWave];
 #pragma unroll
-        for (int j = 0; j < kOffCap / kWave; j++) {
-            const int i = lane + kWave * j;
-            sg[j] = i < t.wn ? *gp(a.seg + t.wb + i) : 0u;
-            uk[j] = (i < t.wn && t.wb + i < U) ? *gp(a.ukeys + t.wb + i) : 0xFFFFFFFFu;
-        }
+            for (int j = 0; j < kOffCap / kWave; j++) {
+                const int i = lane + kWave * j;
+                sg[j] = i < t.wn ? *gp(a.seg + t.wb + i) : 0u;
+                uk[j] = (i < t.wn && t.wb + i < U) ? *gp(a.ukeys + t.wb + i) : 0xFFFFFFFFu;
+            }
 #pragma unroll
-        for (int j = 0; j < kOffCap / kWave; j++) {
-            const int i = lane + kWave * j;
-            if (i < t.wn) {
-                L.seg[i] = sg[j];
-                L.ukey[i] = uk[j];
+            for (int j = 0; j < kOffCap / kWave; j++) {
+                const int i = lane + kWave * j;
+                if (i < t.wn) {
+                    L.seg[i] = sg[j];
+                    L.ukey[i] = uk[j];
+                }
             }
         }
+        wave_sync();
+        if (L.seg[t.wn - 1] > (uint32_t)(t.t1 - 1))
+            t.ul = t.uf + (int)wave_upper_bound(L.seg, (int64_t)t.wn, (uint32_t)(t.t1 - 1)) - 1;
+        else
+            t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
     }
-    wave_sync();
-    if (L.seg[t.wn - 1] > (uint32_t)(t.t1 - 1))
-        t.ul = t.uf + (int)wave_upper_bound(L.seg, (int64_t)t.wn, (uint32_t)(t.t1 - 1)) - 1;
-    else
-        t.ul = (int)wave_upper_bound(a.seg, (int64_t)U + 1, (uint32_t)(t.t1 - 1)) - 1;
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
         const int p = t.t0 + lane + kWave * i;
@@ -834,14 +908,26 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
         if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward: ") + hipGetErrorString(e));
         return EMB_OK;
     }
-    for (int p = 0; p < sort_passes(plan); p++) {
+    // Without an EMIT optimizer and with nothing asked about the unique rows, the
+    // apply kernel finds segments in the sorted keys itself and the unique-list
+    // kernels are skipped.
+    const bool from_keys = plan->opt != EMB_OPT_EMIT && !uniq_keys && !n_uniq && !stats;
+    plan->seg_from_keys = from_keys;
+    const int passes = sort_passes(plan);
+    for (int p = 0; p < passes; p++) {
         const int shift = p * kRadixBits;
-        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk);
+        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
         hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
         hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
-                           shift, hist, dtot, nblk);
+                           shift, hist, dtot, nblk, plan->total_rows,
+                           (from_keys && p == passes - 1) ? misc : nullptr);
         std::swap(k0, k1);
         std::swap(v0, v1);
+    }
+    if (from_keys) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
+        return EMB_OK;
     }
     hipLaunchKernelGGL(uq_count, dim3((unsigned)ublk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
     hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, ublk, uscan, misc, n_uniq, stats);
@@ -879,6 +965,7 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.G = grad_out;
     // the sorted bags sit in the buffer the last radix pass wrote
     a.sval = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.vals2 : W.bags));
+    a.skeys = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.keys2 : W.keys));
     a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
     a.seg = reinterpret_cast<const uint32_t *>(ws + W.seg);
     a.ukeys = reinterpret_cast<const uint32_t *>(ws + W.ukeys);
@@ -891,12 +978,17 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.zero = 0;
     const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(kTileBlock);
     if (a.opt == EMB_OPT_EMIT)
-        hipLaunchKernelGGL(seg_apply<EMB_OPT_EMIT>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_EMIT, false>), grid, block, 0, st, a);
+    else if (a.opt == EMB_OPT_SGD && plan->seg_from_keys)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, true>), grid, block, 0, st, a);
     else if (a.opt == EMB_OPT_SGD)
-        hipLaunchKernelGGL(seg_apply<EMB_OPT_SGD>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, false>), grid, block, 0, st, a);
+    else if (plan->seg_from_keys)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL(seg_apply<EMB_OPT_ADAGRAD>, dim3((unsigned)blocks), dim3(kTileBlock), 0, st, a);
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, false>), grid, block, 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("seg_apply launch: ") + hipGetErrorString(e));
     return EMB_OK;

@@ -81,6 +81,7 @@ struct emb_plan {
     int64_t uq_blocks = 0;         // unique-row blocks of the largest batch
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
+    bool seg_from_keys = false;    // the last dedup skipped the unique list (see emb_backward_dedup)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata
     uint32_t *drow_base = nullptr; // device [n_cols + 1] row bases (after dcols)
     uint32_t *hrow_base = nullptr; // host copy

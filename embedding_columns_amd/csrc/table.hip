@@ -55,9 +55,9 @@ static TabArgs tab_args(const emb_table &t)
 
 // probe for `key`, inserting it into the first empty slot on the way; returns
 // the slot, or -1 if all capacity slots hold other keys.  `inserted` tells
-// whether this thread placed the key.
-__device__ __forceinline__ int64_t probe_insert(const TabArgs &a, unsigned long long key,
-                                                bool &inserted, int64_t &probes)
+// whether this thread placed the key.  Slot by slot (small tables).
+__device__ __forceinline__ int64_t probe_insert_slots(const TabArgs &a, unsigned long long key,
+                                                      bool &inserted, int64_t &probes)
 {
     const uint64_t mask = (uint64_t)a.cap - 1;
     uint64_t h = splitmix64(key) & mask;
@@ -77,6 +77,64 @@ __device__ __forceinline__ int64_t probe_insert(const TabArgs &a, unsigned long 
             return (int64_t)h;
         }
         h = (h + 1) & mask;
+    }
+    probes = a.cap;
+    return -1;
+}
+
+// The same probe sequence read 16 slots (two 64-byte lines) per round: the line
+// holding the home slot and the next one, so that nearly every probe sequence
+// ends after one round trip instead of one per slot.  Plain loads may see an
+// empty slot that another thread has just filled; the compare-and-swap then
+// returns the real key.  Keys never change once placed.
+constexpr int kLineSlots = 8;
+
+__device__ __forceinline__ int64_t probe_insert(const TabArgs &a, unsigned long long key,
+                                                bool &inserted, int64_t &probes)
+{
+    if (a.cap < 2 * kLineSlots) return probe_insert_slots(a, key, inserted, probes);
+    const uint64_t mask = (uint64_t)a.cap - 1;
+    uint64_t h = splitmix64(key) & mask;
+    inserted = false;
+    int64_t scanned = 0;
+    while (scanned < a.cap) {
+        const uint64_t l0 = h & ~(uint64_t)(kLineSlots - 1);
+        const uint64_t l1 = (l0 + kLineSlots) & mask;
+        const int first = (int)(h - l0);
+        unsigned long long kk[2 * kLineSlots];
+        const uint4 *q0 = reinterpret_cast<const uint4 *>(a.keys + l0);
+        const uint4 *q1 = reinterpret_cast<const uint4 *>(a.keys + l1);
+        uint4 v[kLineSlots];
+#pragma unroll
+        for (int j = 0; j < kLineSlots / 2; j++) {
+            v[j] = *gp(q0 + j);
+            v[kLineSlots / 2 + j] = *gp(q1 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < kLineSlots; j++) {
+            kk[2 * j] = ((unsigned long long)v[j].y << 32) | v[j].x;
+            kk[2 * j + 1] = ((unsigned long long)v[j].w << 32) | v[j].z;
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * kLineSlots; j++) {
+            if (j < first) continue;
+            const uint64_t s = j < kLineSlots ? l0 + j : l1 + (j - kLineSlots);
+            unsigned long long k = kk[j];
+            if (k == 0ull) {
+                k = atomicCAS(&a.keys[s], 0ull, key);
+                if (k == 0ull) {
+                    inserted = true;
+                    probes = scanned + (j - first) + 1;
+                    return (int64_t)s;
+                }
+            }
+            if (k == key) {
+                probes = scanned + (j - first) + 1;
+                return (int64_t)s;
+            }
+        }
+        scanned += 2 * kLineSlots - first;
+        h = (l1 + kLineSlots) & mask;
     }
     probes = a.cap;
     return -1;
@@ -131,52 +189,46 @@ __device__ __forceinline__ void stat_max(int64_t *stats, int idx, int64_t v)
 // Counting under a skewed key stream: one block takes 1024 occurrences, adds them
 // up per slot in an LDS hash (each hot key is counted once per block instead
 // of once per occurrence), then adds each distinct slot's count to the table.
-constexpr int kCountPerThread = 4;
-constexpr int kCountTile = kBlock * kCountPerThread;
+constexpr int kCountTile = 1024;               // occurrences per block, one per thread
 constexpr int kLdsSlots = 2 * kCountTile;      // load factor <= 1/2: every insert finds room
+constexpr int kLdsSlotBits = 11;
+static_assert((1 << kLdsSlotBits) == kLdsSlots, "LDS hash size");
 
-__global__ __launch_bounds__(kBlock) void ht_count(TabArgs a, const int64_t *__restrict__ keys,
-                                                  int64_t n, int32_t *__restrict__ pos,
-                                                  int64_t *stats)
+__global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t *__restrict__ keys,
+                                                      int64_t n, int32_t *__restrict__ pos,
+                                                      int64_t *stats)
 {
     __shared__ int32_t lslot[kLdsSlots];
     __shared__ int32_t lcnt[kLdsSlots];
     __shared__ unsigned long long lstat[3];
-    for (int i = threadIdx.x; i < kLdsSlots; i += kBlock) {
+    for (int i = threadIdx.x; i < kLdsSlots; i += kCountTile) {
         lslot[i] = -1;
         lcnt[i] = 0;
     }
     if (threadIdx.x < 3) lstat[threadIdx.x] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kCountTile;
+    const int64_t p = (int64_t)blockIdx.x * kCountTile + threadIdx.x;
     int64_t ins = 0, full = 0, probes = 0;
-    for (int j = 0; j < kCountPerThread; j++) {
-        const int64_t p = base + (int64_t)j * kBlock + threadIdx.x;
-        if (p >= n) break;
-        const int64_t key = *gp(keys + p);
-        if (key < 1) {
-            *gp(pos + p) = EMB_ROW_DROPPED;
-            continue;
-        }
+    const int64_t key = p < n ? *gp(keys + p) : 0;
+    if (p < n && key < 1) *gp(pos + p) = EMB_ROW_DROPPED;
+    if (key >= 1) {
         bool inserted;
-        int64_t pr = 0;
-        const int64_t s = probe_insert(a, (unsigned long long)key, inserted, pr);
-        probes = max(probes, pr);
+        const int64_t s = probe_insert(a, (unsigned long long)key, inserted, probes);
         if (s < 0) {
             *gp(pos + p) = kPosRefused;
-            full++;
-            continue;
+            full = 1;
+        } else {
+            *gp(pos + p) = (int32_t)s;
+            ins = inserted;
+            // count this occurrence in the block's LDS hash
+            uint32_t h = ((uint32_t)s * 2654435761u) >> (32 - kLdsSlotBits);
+            while (true) {
+                const int32_t cur = atomicCAS(&lslot[h], -1, (int32_t)s);
+                if (cur == -1 || cur == (int32_t)s) break;
+                h = (h + 1) & (kLdsSlots - 1);
+            }
+            atomicAdd(&lcnt[h], 1);
         }
-        *gp(pos + p) = (int32_t)s;
-        ins += inserted;
-        // count this occurrence in the block's LDS hash
-        uint32_t h = ((uint32_t)s * 2654435761u) >> (32 - 11);   // 2^11 = kLdsSlots
-        while (true) {
-            const int32_t cur = atomicCAS(&lslot[h], -1, (int32_t)s);
-            if (cur == -1 || cur == (int32_t)s) break;
-            h = (h + 1) & (kLdsSlots - 1);
-        }
-        atomicAdd(&lcnt[h], 1);
     }
     if (stats) {
         atomicAdd(&lstat[0], (unsigned long long)ins);
@@ -184,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void ht_count(TabArgs a, const int64_t *__r
         atomicMax(&lstat[2], (unsigned long long)probes);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kLdsSlots; i += kBlock)
+    for (int i = threadIdx.x; i < kLdsSlots; i += kCountTile)
         if (lslot[i] >= 0) atomicAdd(&a.count[lslot[i]], lcnt[i]);
     if (stats && threadIdx.x == 0) {
         if (lstat[0]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_INSERTED], lstat[0]);
@@ -422,7 +474,7 @@ emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int
     hipStream_t st = static_cast<hipStream_t>(stream);
     const TabArgs a = tab_args(*table);
     const unsigned cgrid = (unsigned)std::max<int64_t>(1, (n + kCountTile - 1) / kCountTile);
-    hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
+    hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_admit, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_resolve, dim3(grid_of(n)), dim3(kBlock), 0, st, a, n, rows_out);
     return launched("lookup_or_insert");

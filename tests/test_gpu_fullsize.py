@@ -33,7 +33,15 @@ def _gpu_step(w, b, weights, states, G):
     ws = tuple(t.clone() for t in cols.workspace_view(b.n)) if w.training else None
     out = {"Y": Y, "ws": ws, "cols": cols}
     if w.training:
-        out["ukeys"], _, out["nu"] = cols.backward(G, want_keys=True)
+        # the unique-row list, from a dedup of its own (the apply is not run here)
+        keys = torch.empty(b.n, dtype=torch.int32, device=DEV)
+        nu = torch.zeros(1, dtype=torch.int64, device=DEV)
+        E.emb_backward_dedup(cols.plan, cols.workspace, keys, nu, None)
+        out["ukeys"], out["nu"] = keys, nu
+        torch.cuda.synchronize()
+        # then the benchmark's step: forward again, backward with nothing asked back
+        cols.forward(off, ids=ids, fvals=fv, training=True)
+        cols.backward(G, want_count=False)
     torch.cuda.synchronize()
     return out
 

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_harness import run_dense_case, Step, to_np, check_forward, oracle_columns
+from gpu_harness import run_dense_case, Step, to_np, check_forward, check_rows_sgd, oracle_columns
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -53,6 +53,26 @@ def test_long_sequences_bf16_adagrad(tile):
     # bags of 200..2000 IDs over 4 identity columns, bf16 tables, mean, Adagrad
     w = W.config(4, n_cols=4, batch=40, rows=100_000)
     run_dense_case(w, seed=4004, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+def test_training_front_end_sgd_segments_from_keys(tile):
+    # the benchmark's backward: nothing asked back, segments found from the sorted keys
+    w = W.config(2, n_cols=24, batch=512, rows_range=(1e2, 1e4))
+    run_dense_case(w, seed=2012, tile=tile, ask_unique=False)
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+def test_long_sequences_adagrad_segments_from_keys(tile):
+    # hot rows: segments of thousands of contributors spanning many tiles
+    w = W.config(4, n_cols=4, batch=40, rows=5_000)
+    run_dense_case(w, seed=4014, tile=tile, ask_unique=False)
+
+
+def test_many_tiny_columns_segments_from_keys():
+    w = W.config(3, n_cols=60, batch=96, rows_range=(100, 5000), opt=W.OPT_SGD, lr=0.01,
+                 training=True)
+    run_dense_case(w, seed=3014, tile=64, ask_unique=False)
 
 
 def test_deterministic_across_runs():
@@ -128,6 +148,30 @@ def test_one_bag_spanning_many_tiles(tile):
     lens = [0, 5000, 0, 3, 0, 0]
     w, b = _custom(_hash_cols(2, dim=32, pool=W.MEAN), lens)
     _run_custom(w, b, tile)
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+def test_hot_row_segment_spanning_many_tiles_sgd(tile):
+    # one row looked up 5000 times (plus a few others): with nothing asked back,
+    # the segment's start and end tiles are found by searching the sorted keys
+    cols = [W.Column(W.IDENTITY, W.MEAN, W.F32, 50, 32)]
+    lens = [3, 2500, 0, 2500, 1, 4]
+    n = sum(lens)
+    ids = np.full(n, 7, dtype=np.int64)
+    ids[:3] = [1, 2, 7]
+    ids[-5:] = [49, 0, 7, 3, 3]
+    w, b = _custom(cols, lens, ids=ids, opt=W.OPT_SGD, lr=0.01)
+    wts, sts = W.make_tables(w, seed=11, device="cpu")
+    G = W.make_grad(w, seed=11, device="cpu")
+    st = Step(w, b, wts, sts, tile=tile)
+    st.forward(training=True)
+    st.backward(G, ask_unique=False)
+    torch.cuda.synchronize()
+    host_w = to_np(wts[0])
+    oc = oracle_columns(w, [host_w.copy()])
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
+                                         opt=w.opt, lr=w.lr)
+    check_rows_sgd(cols[0], host_w, to_np(st.gw[0]), oc.weights[0], urow, ub[:, :32], w.lr)
 
 
 def test_single_position_and_all_invalid():
