@@ -2,10 +2,12 @@
 //
 // ONE launch covers every column.  Work follows element count, not column count
 // (RecIS Sec. 3.1, "Thread mapping for skewed inputs"): all columns' positions
-// form one flat index space (column-major bags), cut into equal tiles of T
+// form one flat index space (column-major bags), cut into tiles of about T
 // positions, one tile per wavefront.  Inside a tile:
-//   1. three wavefront-parallel searches over the CSR offsets find the bags the
-//      tile touches; their offsets are staged in LDS;
+//   1. a wavefront-parallel search over the CSR offsets finds the tile's first
+//      bag and the offsets around it are staged in LDS; the nominal tile ends
+//      k T and (k+1) T move to the end of a short bag they cut, so short bags
+//      are never split;
 //   2. per column segment, each lane transforms positions (hash + exact mod,
 //      identity, bucketize on LDS-staged boundaries, keyed rows), with the
 //      validity filter of an embedding column (RECom explainer: out-of-range
@@ -13,11 +15,11 @@
 //      bag of every position for the backward;
 //   3. the wavefront splits into groups of P lanes (P * 16 bytes = one table row);
 //      each group walks a contiguous run of positions, issuing 8 independent
-//      16-byte row loads per lane before accumulating them in fp32 registers, and
+//      row loads per lane before accumulating them in fp32 registers, and
 //      a bag that ends inside the run is written by that group alone -- the
 //      unique-writer forward of RecIS Sec. 3.2 / Algorithm 1, no atomics on Y,
 //      empty bags produce zero;
-//   4. bags cut by group boundaries are combined in LDS; bags cut by tile
+//   4. bags cut by group boundaries are combined in LDS; long bags cut by tile
 //      boundaries leave fp32 partials in the workspace and the last tile to
 //      arrive (atomic ticket) sums the pieces in tile order, so the result does
 //      not depend on arrival order.
@@ -48,10 +50,15 @@ struct FwdArgs {
 };
 
 constexpr int kColCache = 8;
+// A bag of at most kShort positions is never cut by a tile boundary: the tile
+// holding its start finishes it (tiles span at most kTileMax + kShort - 1
+// positions).  Only longer bags are split and combined through the workspace.
+constexpr int kShort = 64;
+constexpr int kSpan = kTileMax + kShort;
 
 struct WaveLds {
-    int32_t rows[kTileMax];          // transformed row of each tile position
-    int32_t pbag[kTileMax];          // bag of each tile position (training)
+    int32_t rows[kSpan];             // transformed row of each tile position
+    int32_t pbag[kSpan];             // bag of each tile position (training)
     int32_t off[kOffCap];            // window of CSR offsets
     union {
         float part[kWave][4];        // per-lane partial sum of each run's first bag
@@ -63,6 +70,7 @@ struct WaveLds {
 
 struct TileCtx {
     int64_t k;
+    int p0;          // k * T: the tile's inputs were loaded from here
     int t0, t1;      // positions of this tile
     int bf, bl;      // first / last non-empty bag touching the tile
     int wb, wn;      // LDS window: offsets[wb .. wb+wn)
@@ -340,7 +348,7 @@ __device__ __forceinline__ int bucket_count(B b, int nb, float x)
 
 constexpr int kMargin = 64;             // offsets staged before the tile's first bag
 
-constexpr int kPL = kTileMax / kWave;  // tile positions per lane: t0 + lane + 64 i
+constexpr int kPL = kSpan / kWave;     // tile positions per lane: p0 + lane + 64 i
 
 // The raw inputs of the tile's positions, loaded once at the start of the tile so
 // that they arrive while the offsets are searched.
@@ -364,7 +372,7 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
     const uint64_t rows = (uint64_t)col.rows;
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
+        const int p = t.p0 + lane + kWave * i;
         if (p < s0 || p >= s1) continue;
         int r;
         if (col.kind == EMB_COL_HASH) {
@@ -420,14 +428,16 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     const int N = (int)a.N, T = a.T, nbag = a.C * a.B;
-    t.t0 = (int)min<int64_t>(t.k * T, N);
-    t.t1 = (int)min<int64_t>((t.k + 1) * T, N);
+    // nominal range [k T, (k+1) T); the real one moves each end to the end of a
+    // short bag that the nominal boundary cuts
+    const int x0 = (int)min<int64_t>(t.k * T, N), x1 = (int)min<int64_t>((t.k + 1) * T, N);
+    t.p0 = x0;
     const bool last = t.k == a.ntiles - 1;
     TileIn in;
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        const bool ok = p < t.t1;
+        const int p = x0 + lane + kWave * i;
+        const bool ok = p < N;
         in.id[i] = (a.ids && ok) ? *gp(a.ids + p) : 0;
         in.fv[i] = (a.fvals && ok) ? *gp(a.fvals + p) : 0.f;
         in.kr[i] = (a.krows && ok) ? *gp(a.krows + p) : 0;
@@ -436,11 +446,11 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     // the bags this tile touches: one global search for the first, then the
     // offsets window in LDS answers the rest
     int own_lo, own_hi;
-    if (t.t0 < t.t1) {
-        t.bf = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t0) - 1;
-        t.wb = max(0, t.bf - kMargin);
+    int b0 = nbag;
+    if (x0 < x1) {
+        b0 = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, x0) - 1;   // bag holding x0
+        t.wb = max(0, b0 - kMargin);
     } else {
-        t.bf = nbag;
         t.wb = 0;
     }
     t.wn = min(nbag + 1 - t.wb, kOffCap);
@@ -459,12 +469,40 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         }
     }
     wave_sync();
-    if (t.t0 < t.t1) {
-        const int f = t.bf - t.wb;
-        if (L.off[t.wn - 1] > t.t1 - 1)
-            t.bl = t.bf + (int)wave_upper_bound(L.off + f, (int64_t)(t.wn - f), t.t1 - 1) - 1;
-        else
-            t.bl = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t1 - 1) - 1;
+    t.t0 = x0;
+    t.t1 = x1;
+    if (x0 < x1) {
+        // start: a short bag begun before x0 belongs to the previous tile (which
+        // ends at its end); the same rule, applied there, gives that tile's end
+        t.bf = b0;
+        t.bl = b0;                     // provisional, for offat's window checks
+        if (x0 > 0) {
+            const int bs = offat(a, L, t, b0), be = offat(a, L, t, b0 + 1);
+            if (bs < x0 && be - bs <= kShort && be < min(x0 + T, N)) {
+                t.t0 = be;
+                int nb = b0 + 1;
+                while (offat(a, L, t, nb + 1) == be) nb++;
+                t.bf = nb;
+            }
+        }
+        // end: the bag holding x1, finished here if short
+        int b1 = -1;
+        if (x1 < N) {
+            const int f = b0 - t.wb;
+            b1 = (L.off[t.wn - 1] > x1)
+                     ? b0 + (int)wave_upper_bound(L.off + f, (int64_t)(t.wn - f), x1) - 1
+                     : (int)wave_upper_bound(a.off, (int64_t)nbag + 1, x1) - 1;
+            const int bs = offat(a, L, t, b1), be = offat(a, L, t, b1 + 1);
+            if (bs < x1 && be - bs <= kShort && be < min(x1 + T, N)) t.t1 = be;
+        }
+        if (t.t1 != x1) {
+            t.bl = b1;                 // the short bag finished here
+        } else {
+            const int f = b0 - t.wb;
+            t.bl = (L.off[t.wn - 1] > t.t1 - 1)
+                       ? b0 + (int)wave_upper_bound(L.off + f, (int64_t)(t.wn - f), t.t1 - 1) - 1
+                       : (int)wave_upper_bound(a.off, (int64_t)nbag + 1, t.t1 - 1) - 1;
+        }
         // owned bags start in [t0, t1): empty bags sitting exactly at t0 come first
         own_lo = t.bf + 1;
         if (offat(a, L, t, t.bf) == t.t0) {
@@ -473,6 +511,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         }
         own_hi = last ? nbag : t.bl + 1;
     } else {
+        t.bf = nbag;
         t.bl = nbag - 1;
         own_lo = 0;
         own_hi = nbag;
@@ -511,8 +550,8 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         if (a.training) {
 #pragma unroll
             for (int i = 0; i < kPL; i++) {
-                const int p = t.t0 + lane + kWave * i;
-                if (p < t.t1) *gp(a.bags + p) = L.pbag[p - t.t0];
+                const int p = t.p0 + lane + kWave * i;
+                if (p >= t.t0 && p < t.t1) *gp(a.bags + p) = L.pbag[p - t.t0];
             }
         }
     }
