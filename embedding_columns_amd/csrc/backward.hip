@@ -393,9 +393,19 @@ struct BwdArgs {
     int32_t zero;               // 0, unknown to the compiler: keeps repeated row loads distinct
 };
 
+// A segment of at most kSegShort contributors is never cut by a tile boundary:
+// the tile holding its start finishes it.  Tiles span at most
+// kTileMax + kSegShort - 1 contributors; the sorted keys around the nominal
+// range (kKeyWin of them) are staged in LDS to place the boundaries.
+constexpr int kSegShort = 64;
+constexpr int kSegSpan = kTileMax + kSegShort;
+constexpr int kKeyWin = kSegShort + kTileMax + 2 * kSegShort;   // keys [x0 - 64, x0 + 384)
+static_assert(kKeyWin % kWave == 0, "key window loads are unrolled per lane");
+
 struct BwdLds {
-    int32_t bag[kTileMax];      // bag of each contributor of the tile
-    float wt[kTileMax];         // pooling weight of each contributor
+    int32_t bag[kSegSpan];      // bag of each contributor of the tile
+    float wt[kSegSpan];         // pooling weight of each contributor
+    uint32_t kw[kKeyWin];       // sorted keys x0 - 64 .. x0 + 383 (sentinels outside [0, nv))
     uint32_t seg[kOffCap];      // window of segment starts
     uint32_t ukey[kOffCap];     // unique keys of the same segments
     float part[kWave][4];
@@ -412,9 +422,9 @@ struct BTile {
 
 // Segment starts and keys of the segments a tile touches, from its LDS window.
 // The window always covers them: it starts at the tile's first segment uf and
-// holds kOffCap > kTileMax + 1 entries (or all up to U), while every later
+// holds kOffCap > kSegSpan entries (or all up to U), while every later
 // segment of the tile starts at a distinct contributor inside the tile, so the
-// tile needs entries uf .. uf + kTileMax at most.  Reading LDS only keeps
+// tile needs entries uf .. uf + kSegSpan - 1 at most.  Reading LDS only keeps
 // global loads (and the waits they bring) out of the walk.
 __device__ __forceinline__ int segat(const BwdArgs &, const BwdLds &L, const BTile &t, int u)
 {
@@ -722,44 +732,32 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 // window in position order; a first segment that began in an earlier tile, or
 // a last one that goes on into a later tile, gets its true start / end from a
 // search of the sorted keys.  Window indices are then local (wb = 0).
-__device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L, BTile &t, int nv)
+__device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L, BTile &t, int nv, int x0)
 {
-    constexpr int kPL = kTileMax / kWave;
+    constexpr int kPL = kSegSpan / kWave;
     const int lane = lane_id();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t kr[kPL];
-#pragma unroll
-    for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        kr[i] = p < t.t1 ? *gp(a.skeys + p) : 0u;
-    }
-    const uint32_t kprev = t.t0 > 0 ? *gp(a.skeys + t.t0 - 1) : 0xFFFFFFFFu;
-    const uint32_t knext = t.t1 < nv ? *gp(a.skeys + t.t1) : 0xFFFFFFFFu;
-    // tile keys into LDS (the bag array is filled later), to compare neighbours
-    int32_t *tk = L.bag;
-#pragma unroll
-    for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        if (p < t.t1) tk[p - t.t0] = (int32_t)kr[i];
-    }
-    wave_sync();
+    const int kb = x0 - kSegShort;                 // position of L.kw[0]
     int base = 0;
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
         const int p = t.t0 + lane + kWave * i;
-        const bool head = p < t.t1 && (p == t.t0 || (uint32_t)tk[p - t.t0 - 1] != kr[i]);
+        const bool head = p < t.t1 && (p == t.t0 || L.kw[p - 1 - kb] != L.kw[p - kb]);
         const uint64_t m = __ballot(head);
         if (head) {
             const int j = base + __popcll(m & lt_mask);
             L.seg[j] = (uint32_t)p;
-            L.ukey[j] = kr[i];
+            L.ukey[j] = L.kw[p - kb];
         }
         base += __popcll(m);
     }
     wave_sync();
     const int nseg = base;
     const uint32_t k0 = L.ukey[0], kl = L.ukey[nseg - 1];
+    const uint32_t kprev = t.t0 > 0 ? L.kw[t.t0 - 1 - kb] : 0xFFFFFFFFu;
+    const uint32_t knext = t.t1 < nv ? L.kw[t.t1 - kb] : 0xFFFFFFFFu;
     int start = t.t0, end = t.t1;
+    // only a long segment crosses a tile boundary: its ends come from a search
     if (kprev == k0) start = (int)wave_lower_bound(a.skeys, (int64_t)t.t0, k0);
     if (knext == kl) end = t.t1 + (int)wave_upper_bound(a.skeys + t.t1, (int64_t)(nv - t.t1), kl);
     if (lane == 0) {
@@ -773,6 +771,27 @@ __device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L
     t.ul = nseg - 1;
 }
 
+// Where a tile boundary lands: the nominal boundary x, or the end of the short
+// segment (run of equal sorted keys) that x cuts.  The run is measured inside
+// the staged keys x - 64 .. x + 63; a run reaching either edge counts as long.
+// Tiles on both sides of x evaluate this on the same keys, so they agree.
+__device__ __forceinline__ int seg_boundary(const BwdLds &L, int x, int x0, int nv, int T)
+{
+    if (x <= 0 || x >= nv) return x;
+    const int lane = lane_id();
+    const int kb = x0 - kSegShort;
+    const uint32_t kx = L.kw[x - kb];
+    const uint32_t lo = L.kw[x - kSegShort + lane - kb];   // keys x-64 .. x-1
+    const uint32_t hi = L.kw[x + lane - kb];               // keys x .. x+63
+    const bool lo_in = x - kSegShort + lane >= 0;
+    const int below = __popcll(__ballot(!lo_in || lo < kx));   // keys before the run
+    const int same = __popcll(__ballot(x + lane < nv && hi == kx));
+    const int ss = x - kSegShort + below, se = x + same;
+    const bool touches = (below == 0 && x - kSegShort >= 0) || same == kSegShort;
+    if (ss < x && !touches && se - ss <= kSegShort && se < min(x + T, nv)) return se;
+    return x;
+}
+
 template <int OPT, bool KM>
 __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 {
@@ -783,25 +802,39 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     const int nv = (int)*gp(a.misc);
-    t.t0 = (int)min<int64_t>(t.k * a.T, nv);
-    t.t1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
-    if (t.t0 >= t.t1) return;
+    const int x0 = (int)min<int64_t>(t.k * a.T, nv), x1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
+    if (x0 >= x1) return;
 
-    // the tile's sorted bags and their pooling counts, loaded while searching
-    constexpr int kPL = kTileMax / kWave;
+    // the sorted keys around the nominal range, and the bags of its contributors
+    // and of the short segment that may extend it, all loaded in one round
+    constexpr int kPL = kSegSpan / kWave;
     int bagr[kPL], nr[kPL];
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        bagr[i] = p < t.t1 ? (int)*gp(a.sval + p) : 0;
+        const int p = x0 + lane + kWave * i;
+        bagr[i] = p < nv ? (int)*gp(a.sval + p) : 0;
+    }
+    {
+        uint32_t kv[kKeyWin / kWave];
+#pragma unroll
+        for (int j = 0; j < kKeyWin / kWave; j++) {
+            const int p = x0 - kSegShort + lane + kWave * j;
+            kv[j] = (p >= 0 && p < nv) ? *gp(a.skeys + p) : (p < 0 ? 0u : 0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int j = 0; j < kKeyWin / kWave; j++) L.kw[lane + kWave * j] = kv[j];
     }
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        nr[i] = (a.any_mean && p < t.t1) ? *gp(a.bag_n + bagr[i]) : 1;
+        const int p = x0 + lane + kWave * i;
+        nr[i] = (a.any_mean && p < nv) ? *gp(a.bag_n + bagr[i]) : 1;
     }
+    wave_sync();
+    t.t0 = seg_boundary(L, x0, x0, nv, a.T);
+    t.t1 = seg_boundary(L, x1, x0, nv, a.T);
+
     if (KM) {
-        seg_window_from_keys(a, L, t, nv);
+        seg_window_from_keys(a, L, t, nv, x0);
     } else {
         const int U = (int)*gp(a.misc + 1);
         t.U = U;
@@ -834,8 +867,8 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     }
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
-        const int p = t.t0 + lane + kWave * i;
-        if (p < t.t1) {
+        const int p = x0 + lane + kWave * i;
+        if (p >= t.t0 && p < t.t1) {
             L.bag[p - t.t0] = bagr[i];
             L.wt[p - t.t0] = 1.0f / (float)nr[i];   // mean weight; sum columns use 1
         }
