@@ -29,11 +29,12 @@ namespace emb {
 
 // lanes of this wavefront whose digit equals mine (active lanes only), by one
 // ballot per digit bit
+template <int BITS = kRadixBits>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool in)
 {
     uint64_t peers = __ballot(in);
 #pragma unroll
-    for (int b = 0; b < kRadixBits; b++) {
+    for (int b = 0; b < BITS; b++) {
         const uint64_t m = __ballot((d >> b) & 1u);
         peers &= ((d >> b) & 1u) ? m : ~m;
     }
@@ -88,8 +89,10 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDi
 // per-block digit histogram; equal digits within a wavefront are added once
 __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
                                                  int shift, uint32_t *__restrict__ hist,
-                                                 int64_t nblk, uint32_t *__restrict__ misc)
+                                                 int64_t nblk, uint32_t *__restrict__ misc,
+                                                 const uint32_t *need)
 {
+    if (need && *gp(need) == 0u) return;             // the column sort did everything
     // the first pass starts the count of valid contributors at n; the last
     // pass lowers it to the position of the first sentinel key
     if (shift == 0 && blockIdx.x == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
@@ -124,8 +127,9 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
 
 // one block per digit: exclusive scan of hist[d][0..nblk) in place, total -> dtot[d]
 __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
-                                                 uint32_t *__restrict__ dtot)
+                                                 uint32_t *__restrict__ dtot, const uint32_t *need)
 {
+    if (need && *gp(need) == 0u) return;
     __shared__ uint32_t tmp[kWavesPerBlock];
     uint32_t *h = hist + (int64_t)blockIdx.x * nblk;
     uint32_t carry = 0;
@@ -155,8 +159,10 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
                                                     uint32_t *__restrict__ vout, int64_t n,
                                                     int shift, const uint32_t *__restrict__ hist,
                                                     const uint32_t *__restrict__ dtot, int64_t nblk,
-                                                    uint32_t sentinel, uint32_t *__restrict__ misc)
+                                                    uint32_t sentinel, uint32_t *__restrict__ misc,
+                                                    const uint32_t *need)
 {
+    if (need && *gp(need) == 0u) return;
     __shared__ SortLds S;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
@@ -255,6 +261,157 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
     if (misc) {
         for (int o = 1; o < kWave; o <<= 1) first_sentinel = min(first_sentinel, (uint32_t)__shfl_xor((int)first_sentinel, o, kWave));
         if (lane == 0 && first_sentinel != 0xFFFFFFFFu) atomicMin(misc, first_sentinel);
+    }
+}
+
+// ------------------------------------------------ column-local sort in LDS
+//
+// Positions are column-major and a column's keys (row_base_c + row) lie in its
+// own key range, so sorting all keys equals sorting each column's positions in
+// place.  When every column has at most kColCap positions, one workgroup per
+// column sorts them entirely in LDS (a stable LSD radix sort on the row within
+// the column, 7-bit digits), with dropped / DEFAULT keys last inside the
+// column instead of at the end of the array.  A larger column raises a flag in
+// misc[2] and the global radix passes, which otherwise return at once, sort
+// everything.
+
+constexpr int kCSWaves = 16;
+constexpr int kCSBlock = kCSWaves * kWave;
+constexpr int kCSBits = 7;
+constexpr int kCSRadix = 1 << kCSBits;
+constexpr int kColCap = 12288;
+constexpr int kCSItems = kColCap / kCSBlock;            // items per thread
+static_assert(kColCap % (kCSBlock) == 0, "column capacity");
+
+struct ColSortLds {
+    uint32_t key[2][kColCap];          // local keys, ping-pong
+    uint16_t idx[2][kColCap];          // position within the column
+    uint32_t run[kCSWaves][kCSRadix];  // per-wave digit counts, then destinations
+    uint32_t dpre[kCSRadix];
+    int32_t range[2];
+};
+
+__global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict__ kin,
+                                                    const uint32_t *__restrict__ vin,
+                                                    uint32_t *kout, uint32_t *vout, int64_t n,
+                                                    int32_t B, const uint32_t *__restrict__ row_base,
+                                                    uint32_t total_rows, uint32_t *misc)
+{
+    __shared__ ColSortLds S;
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const int c = blockIdx.x;
+    if (c == 0 && t == 0) *gp(misc) = (uint32_t)n;   // every position is a contributor slot
+    // the column's positions: bags are non-decreasing in position and bag / B is the column
+    if (w == 0) {
+        const int64_t p0 = wave_lower_bound(vin, n, (uint32_t)c * (uint32_t)B);
+        const int64_t p1 = wave_lower_bound(vin, n, (uint32_t)(c + 1) * (uint32_t)B);
+        if (lane == 0) {
+            S.range[0] = (int32_t)p0;
+            S.range[1] = (int32_t)p1;
+        }
+    }
+    __syncthreads();
+    const int P0 = S.range[0], cnt = S.range[1] - S.range[0];
+    if (cnt > kColCap) {
+        if (t == 0) *gp(misc + 2) = 1u;               // the global passes take over
+        return;
+    }
+    if (cnt == 0) return;
+    const uint32_t rb = row_base[c], rows = row_base[c + 1] - rb;
+    const int bits = 32 - __clz((int)(rows + 1));
+    const int passes = (bits + kCSBits - 1) / kCSBits;
+
+    // local key: the row, or rows / rows + 1 for dropped / DEFAULT
+    {
+        uint32_t kv[kCSItems];
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {
+            const int i = j * kCSBlock + t;
+            kv[j] = i < cnt ? *gp(kin + P0 + i) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {
+            const int i = j * kCSBlock + t;
+            if (i < cnt) {
+                S.key[0][i] = kv[j] < total_rows ? kv[j] - rb : rows + (kv[j] - total_rows);
+                S.idx[0][i] = (uint16_t)i;
+            }
+        }
+    }
+    __syncthreads();
+
+    // wave w ranks items w*per .. (w+1)*per-1 in (j, lane) order: stable
+    const int per = ((cnt + kCSWaves * kWave - 1) / (kCSWaves * kWave)) * kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int pass = 0; pass < passes; pass++) {
+        const int src = pass & 1, dst = src ^ 1, shift = pass * kCSBits;
+        for (int d = lane; d < kCSRadix; d += kWave) S.run[w][d] = 0;
+        wave_sync();
+        uint32_t rank[kCSItems], dig[kCSItems];
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {
+            const int i = w * per + j * kWave + lane;
+            const bool in = j * kWave < per && i < cnt;
+            const uint32_t d = in ? (S.key[src][i] >> shift) & (kCSRadix - 1) : 0u;
+            const uint64_t peers = match_digit<kCSBits>(d, in);
+            const uint32_t before = S.run[w][d];
+            rank[j] = before + (uint32_t)__popcll(peers & lt_mask);
+            dig[j] = d;
+            const bool leader = in && (peers >> lane) == 1ull;
+            wave_sync();
+            if (leader) S.run[w][d] = before + (uint32_t)__popcll(peers);
+            wave_sync();
+        }
+        __syncthreads();
+        // destinations: digit-major over (digit, wave)
+        if (t < kCSRadix) {
+            uint32_t tot = 0;
+            for (int k = 0; k < kCSWaves; k++) tot += S.run[k][t];
+            S.dpre[t] = tot;
+        }
+        __syncthreads();
+        if (t < kCSRadix) {
+            uint32_t base = 0;
+            for (int d = 0; d < t; d++) base += S.dpre[d];
+            for (int k = 0; k < kCSWaves; k++) {
+                const uint32_t x = S.run[k][t];
+                S.run[k][t] = base;
+                base += x;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {
+            const int i = w * per + j * kWave + lane;
+            if (j * kWave < per && i < cnt) {
+                const uint32_t o = S.run[w][dig[j]] + rank[j];
+                S.key[dst][o] = S.key[src][i];
+                S.idx[dst][o] = S.idx[src][i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // back to global keys; the bags are gathered before any is written (in place)
+    const int fin = passes & 1;
+    uint32_t ko[kCSItems], vo[kCSItems];
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = j * kCSBlock + t;
+        if (i < cnt) {
+            const uint32_t k = S.key[fin][i];
+            ko[j] = k < rows ? k + rb : total_rows + (k - rows);
+            vo[j] = *gp(vin + P0 + S.idx[fin][i]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = j * kCSBlock + t;
+        if (i < cnt) {
+            *gp(kout + P0 + i) = ko[j];
+            *gp(vout + P0 + i) = vo[j];
+        }
     }
 }
 
@@ -391,6 +548,7 @@ struct BwdArgs {
     uint32_t *tick;
     int32_t any_mean;           // some column pools by mean
     int32_t zero;               // 0, unknown to the compiler: keeps repeated row loads distinct
+    uint32_t total_rows;        // keys >= this are dropped / DEFAULT contributors: no row
 };
 
 // A segment of at most kSegShort contributors is never cut by a tile boundary:
@@ -510,10 +668,18 @@ __device__ __forceinline__ void row_apply(const BwdArgs &a, const DevCol &col, i
     }
 }
 
+// first element of lane slice q of unique row u; the dropped / DEFAULT keys that
+// the column sort leaves inside a column point at row 0 (read, never written)
 __device__ __forceinline__ int64_t row_elem(const BwdArgs &a, const BwdLds &L, const BTile &t,
                                             const DevCol &col, int u, int q)
 {
-    return (int64_t)(ukeyat(a, L, t, u) - col.row_base) * col.dim + q * 4;
+    const uint32_t k = ukeyat(a, L, t, u);
+    return (int64_t)(k < a.total_rows ? k - col.row_base : 0u) * col.dim + q * 4;
+}
+
+__device__ __forceinline__ bool seg_live(const BwdArgs &a, const BwdLds &L, const BTile &t, int u)
+{
+    return ukeyat(a, L, t, u) < a.total_rows;
 }
 
 // a segment that finished in another place than where it started: load its
@@ -661,7 +827,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 #pragma unroll
                             for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                             hseg = u; hpass = false;
-                        } else if (qa) {
+                        } else if (qa && seg_live(a, L, t, u)) {
                             row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
                         }
 #pragma unroll
@@ -684,7 +850,7 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 #pragma unroll
                 for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                 hseg = u; hpass = false;
-            } else if (qa) {
+            } else if (qa && seg_live(a, L, t, u)) {
                 row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
             }
         } else if (before) {
@@ -710,8 +876,13 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             if (!L.hpass[g2]) { ended = true; break; }
         }
-        if (ended) seg_out<OPT, BF>(a, L, t, col, tseg, sum, q, qa);
-        else bwd_piece(a, L, t, c, 1, tseg, sum, g * P, q, qa);
+        if (!seg_live(a, L, t, tseg)) {
+            // dropped / DEFAULT contributors: nothing to update
+        } else if (ended) {
+            seg_out<OPT, BF>(a, L, t, col, tseg, sum, q, qa);
+        } else {
+            bwd_piece(a, L, t, c, 1, tseg, sum, g * P, q, qa);
+        }
     }
     if (g == 0 && hseg >= 0) {
         float sum[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
@@ -722,9 +893,43 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
             for (int v = 0; v < 4; v++) sum[v] += L.part[g2 * P + q][v];
             pass = L.hpass[g2];
         }
-        bwd_piece(a, L, t, c, 0, hseg, sum, 0, q, qa);
+        if (seg_live(a, L, t, hseg)) bwd_piece(a, L, t, c, 0, hseg, sum, 0, q, qa);
     }
     wave_sync();
+}
+
+// number of leading keys i < n with key[i] < k or key[i] >= hi: the start of the
+// run of k when every key before it is smaller or at least hi (a 64-ary search)
+__device__ __forceinline__ int64_t wave_count_before(const uint32_t *key, int64_t n, uint32_t k,
+                                                     uint32_t hi)
+{
+    int64_t lo = 0, up = n;
+    const int l = lane_id();
+    while (up - lo > 64) {
+        const int64_t step = (up - lo + 63) / 64;
+        const int64_t i = lo + (int64_t)l * step;
+        bool b = false;
+        if (i < up) {
+            const uint32_t x = *gp(key + i);
+            b = x < k || x >= hi;
+        }
+        const int cnt = __popcll(__ballot(b));
+        if (cnt == 0) { up = lo; break; }
+        const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;
+        const int64_t nup = (lo + (int64_t)cnt * step < up) ? lo + (int64_t)cnt * step : up;
+        lo = nlo;
+        up = nup;
+    }
+    if (up > lo) {
+        const int64_t i = lo + l;
+        bool b = false;
+        if (i < up) {
+            const uint32_t x = *gp(key + i);
+            b = x < k || x >= hi;
+        }
+        lo += __popcll(__ballot(b));
+    }
+    return lo;
 }
 
 // The segments of tile t from the sorted keys, without a unique list: heads
@@ -757,8 +962,10 @@ __device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L
     const uint32_t kprev = t.t0 > 0 ? L.kw[t.t0 - 1 - kb] : 0xFFFFFFFFu;
     const uint32_t knext = t.t1 < nv ? L.kw[t.t1 - kb] : 0xFFFFFFFFu;
     int start = t.t0, end = t.t1;
-    // only a long segment crosses a tile boundary: its ends come from a search
-    if (kprev == k0) start = (int)wave_lower_bound(a.skeys, (int64_t)t.t0, k0);
+    // only a long segment crosses a tile boundary: its ends come from a search.
+    // Keys before the run are smaller, or dropped / DEFAULT keys (>= total_rows)
+    // that the column sort left at the end of earlier columns.
+    if (kprev == k0) start = (int)wave_count_before(a.skeys, (int64_t)t.t0, k0, a.total_rows);
     if (knext == kl) end = t.t1 + (int)wave_upper_bound(a.skeys + t.t1, (int64_t)(nv - t.t1), kl);
     if (lane == 0) {
         L.seg[0] = (uint32_t)start;
@@ -784,10 +991,12 @@ __device__ __forceinline__ int seg_boundary(const BwdLds &L, int x, int x0, int 
     const uint32_t lo = L.kw[x - kSegShort + lane - kb];   // keys x-64 .. x-1
     const uint32_t hi = L.kw[x + lane - kb];               // keys x .. x+63
     const bool lo_in = x - kSegShort + lane >= 0;
-    const int below = __popcll(__ballot(!lo_in || lo < kx));   // keys before the run
+    // equal keys are adjacent: the run is a suffix of the keys below x and a
+    // prefix of those from x
+    const int before = __popcll(__ballot(lo_in && lo == kx));
     const int same = __popcll(__ballot(x + lane < nv && hi == kx));
-    const int ss = x - kSegShort + below, se = x + same;
-    const bool touches = (below == 0 && x - kSegShort >= 0) || same == kSegShort;
+    const int ss = x - before, se = x + same;
+    const bool touches = (before == kSegShort) || same == kSegShort;
     if (ss < x && !touches && se - ss <= kSegShort && se < min(x + T, nv)) return se;
     return x;
 }
@@ -947,13 +1156,23 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     const bool from_keys = plan->opt != EMB_OPT_EMIT && !uniq_keys && !n_uniq && !stats;
     plan->seg_from_keys = from_keys;
     const int passes = sort_passes(plan);
+    // segments found from the keys can also come from the column sort, which
+    // leaves dropped / DEFAULT keys inside each column; the global passes then
+    // run only if a column was too large for it (misc[2], cleared by the forward)
+    const uint32_t *need = nullptr;
+    if (from_keys) {
+        uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
+        hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, kf, vf,
+                           n, plan->batch, plan->drow_base, plan->total_rows, misc);
+        need = misc + 2;
+    }
     for (int p = 0; p < passes; p++) {
         const int shift = p * kRadixBits;
-        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
-        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
+        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc, need);
+        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot, need);
         hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
                            shift, hist, dtot, nblk, plan->total_rows,
-                           (from_keys && p == passes - 1) ? misc : nullptr);
+                           (from_keys && p == passes - 1) ? misc : nullptr, need);
         std::swap(k0, k1);
         std::swap(v0, v1);
     }
@@ -1009,6 +1228,7 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
     a.any_mean = plan->any_mean ? 1 : 0;
     a.zero = 0;
+    a.total_rows = plan->total_rows;
     const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(kTileBlock);

@@ -174,6 +174,34 @@ def test_hot_row_segment_spanning_many_tiles_sgd(tile):
     check_rows_sgd(cols[0], host_w, to_np(st.gw[0]), oc.weights[0], urow, ub[:, :32], w.lr)
 
 
+@pytest.mark.parametrize("big", [12288, 12289, 20000])
+def test_segments_from_keys_column_sort_capacity(big):
+    # the column-local sort takes columns of up to 12288 positions; one larger
+    # column sends the whole step to the global radix passes
+    cols = [W.Column(W.HASH, W.SUM, W.F32, 300, 16, 0, 1 << 40),
+            W.Column(W.IDENTITY, W.MEAN, W.F32, 5000, 8),
+            W.Column(W.HASH, W.MEAN, W.F32, 40, 32, 0, 1 << 40)]
+    B = 8
+    lens = [5] * B + [0] * (B - 1) + [big] + [3, 0, 1, 700, 2, 2, 9, 4]
+    n = sum(lens)
+    rng = np.random.default_rng(big)
+    ids = rng.integers(-3, 5200, size=n, dtype=np.int64)
+    w, b = _custom(cols, lens, ids=ids, B=B, opt=W.OPT_SGD, lr=0.01)
+    wts, sts = W.make_tables(w, seed=13, device="cpu")
+    G = W.make_grad(w, seed=13, device="cpu")
+    st = Step(w, b, wts, sts, tile=256)
+    st.forward(training=True)
+    st.backward(G, ask_unique=False)
+    torch.cuda.synchronize()
+    host_w = [to_np(x) for x in wts]
+    oc = oracle_columns(w, [x.copy() for x in host_w])
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
+                                         opt=w.opt, lr=w.lr)
+    for c, col in enumerate(cols):
+        sel = ucol == c
+        check_rows_sgd(col, host_w[c], to_np(st.gw[c]), oc.weights[c], urow[sel], ub[sel][:, :col.dim], w.lr)
+
+
 def test_single_position_and_all_invalid():
     cols = _hash_cols(2, dim=8)
     w, b = _custom(cols, [1, 0, 0, 4], ids=np.array([5, -1, -7, 1 << 41, -2], dtype=np.int64))
