@@ -32,13 +32,19 @@ namespace emb {
 template <int BITS = kRadixBits>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool in)
 {
-    uint64_t peers = __ballot(in);
+    // per bit: m = lanes whose bit is set; a lane differs from me where m does
+    // not equal my bit broadcast (bm, 0 or all ones); peers = lanes differing
+    // in no bit
+    uint32_t mis_lo = 0u, mis_hi = 0u;
 #pragma unroll
     for (int b = 0; b < BITS; b++) {
-        const uint64_t m = __ballot((d >> b) & 1u);
-        peers &= ((d >> b) & 1u) ? m : ~m;
+        const uint32_t bm = (uint32_t)__builtin_amdgcn_sbfe((int)d, b, 1);
+        const uint64_t m = __ballot(bm != 0u);
+        mis_lo |= (uint32_t)m ^ bm;
+        mis_hi |= (uint32_t)(m >> 32) ^ bm;
     }
-    return peers;
+    const uint64_t act = __ballot(in);
+    return act & ~(((uint64_t)mis_hi << 32) | mis_lo);
 }
 
 // exclusive scan of 256 values held one per thread; returns the total
@@ -282,36 +288,28 @@ constexpr int kCSRadix = 1 << kCSBits;
 constexpr int kColCap = 12288;
 constexpr int kCSItems = kColCap / kCSBlock;            // items per thread
 static_assert(kColCap % (kCSBlock) == 0, "column capacity");
+static_assert(kCSRadix == 2 * kWave, "the digit scan spans two wavefronts");
 
 struct ColSortLds {
     uint32_t key[2][kColCap];          // local keys, ping-pong
     uint16_t idx[2][kColCap];          // position within the column
     uint32_t run[kCSWaves][kCSRadix];  // per-wave digit counts, then destinations
     uint32_t dpre[kCSRadix];
-    int32_t range[2];
 };
 
 __global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict__ kin,
                                                     const uint32_t *__restrict__ vin,
                                                     uint32_t *kout, uint32_t *vout, int64_t n,
-                                                    int32_t B, const uint32_t *__restrict__ row_base,
+                                                    const uint32_t *__restrict__ cstart,
+                                                    const uint32_t *__restrict__ row_base,
                                                     uint32_t total_rows, uint32_t *misc)
 {
     __shared__ ColSortLds S;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int c = blockIdx.x;
     if (c == 0 && t == 0) *gp(misc) = (uint32_t)n;   // every position is a contributor slot
-    // the column's positions: bags are non-decreasing in position and bag / B is the column
-    if (w == 0) {
-        const int64_t p0 = wave_lower_bound(vin, n, (uint32_t)c * (uint32_t)B);
-        const int64_t p1 = wave_lower_bound(vin, n, (uint32_t)(c + 1) * (uint32_t)B);
-        if (lane == 0) {
-            S.range[0] = (int32_t)p0;
-            S.range[1] = (int32_t)p1;
-        }
-    }
-    __syncthreads();
-    const int P0 = S.range[0], cnt = S.range[1] - S.range[0];
+    // the column's positions, recorded by the forward
+    const int P0 = (int)cstart[c], cnt = (int)cstart[c + 1] - P0;
     if (cnt > kColCap) {
         if (t == 0) *gp(misc + 2) = 1u;               // the global passes take over
         return;
@@ -347,36 +345,58 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict_
         const int src = pass & 1, dst = src ^ 1, shift = pass * kCSBits;
         for (int d = lane; d < kCSRadix; d += kWave) S.run[w][d] = 0;
         wave_sync();
-        uint32_t rank[kCSItems], dig[kCSItems];
+        // rank = items of the same digit in earlier rounds of this wave (the
+        // value the group's lowest lane gets back from its LDS add: one wave's
+        // LDS operations run in order) + lower lanes of this round
+        uint32_t rank[kCSItems], dig[kCSItems], prev[kCSItems];
+        int lead[kCSItems];
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {         // all key reads first
+            const int i = w * per + j * kWave + lane;
+            dig[j] = (j * kWave < per && i < cnt) ? S.key[src][i] : 0u;
+        }
 #pragma unroll
         for (int j = 0; j < kCSItems; j++) {
             const int i = w * per + j * kWave + lane;
             const bool in = j * kWave < per && i < cnt;
-            const uint32_t d = in ? (S.key[src][i] >> shift) & (kCSRadix - 1) : 0u;
+            const uint32_t d = in ? (dig[j] >> shift) & (kCSRadix - 1) : 0u;
             const uint64_t peers = match_digit<kCSBits>(d, in);
-            const uint32_t before = S.run[w][d];
-            rank[j] = before + (uint32_t)__popcll(peers & lt_mask);
+            lead[j] = in ? __ffsll((unsigned long long)peers) - 1 : lane;
+            rank[j] = (uint32_t)__popcll(peers & lt_mask);
             dig[j] = d;
-            const bool leader = in && (peers >> lane) == 1ull;
-            wave_sync();
-            if (leader) S.run[w][d] = before + (uint32_t)__popcll(peers);
-            wave_sync();
+            prev[j] = 0u;
+            if (in && lead[j] == lane) prev[j] = atomicAdd(&S.run[w][d], (uint32_t)__popcll(peers));
         }
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
         __syncthreads();
-        // destinations: digit-major over (digit, wave)
+        // destinations, digit-major over (digit, wave): thread d < 128 holds
+        // digit d's per-wave counts; a scan over the two waves of digits gives
+        // each digit's start
+        uint32_t cw[kCSWaves], incl = 0;
         if (t < kCSRadix) {
             uint32_t tot = 0;
-            for (int k = 0; k < kCSWaves; k++) tot += S.run[k][t];
-            S.dpre[t] = tot;
+#pragma unroll
+            for (int k = 0; k < kCSWaves; k++) {
+                cw[k] = S.run[k][t];
+                tot += cw[k];
+            }
+            incl = tot;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += y;
+            }
+            incl -= tot;                                   // exclusive within the wave
+            if (t == kWave - 1) S.dpre[0] = incl + tot;    // digits 0..63 in total
         }
         __syncthreads();
         if (t < kCSRadix) {
-            uint32_t base = 0;
-            for (int d = 0; d < t; d++) base += S.dpre[d];
+            uint32_t base = incl + (t >= kWave ? S.dpre[0] : 0u);
+#pragma unroll
             for (int k = 0; k < kCSWaves; k++) {
-                const uint32_t x = S.run[k][t];
                 S.run[k][t] = base;
-                base += x;
+                base += cw[k];
             }
         }
         __syncthreads();
@@ -1163,7 +1183,8 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     if (from_keys) {
         uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
         hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, kf, vf,
-                           n, plan->batch, plan->drow_base, plan->total_rows, misc);
+                           n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,
+                           plan->total_rows, misc);
         need = misc + 2;
     }
     for (int p = 0; p < passes; p++) {

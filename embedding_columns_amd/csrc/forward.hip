@@ -48,6 +48,7 @@ struct FwdArgs {
     int64_t *stats;
     uint32_t total_rows;
     uint32_t *sort_flag;     // set by the backward's column sort when a column is too large
+    uint32_t *cstart;        // training: first position of each column, [C + 1]
 };
 
 constexpr int kColCache = 8;
@@ -518,6 +519,15 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         own_lo = 0;
         own_hi = nbag;
     }
+    if (a.training) {
+        // every bag is owned by exactly one tile: the owner of a column's first bag
+        // records where the column starts (for the backward's column sort)
+        for (int c = (own_lo + a.B - 1) / a.B + lane; c * a.B < own_hi; c += kWave) {
+            const unsigned i = (unsigned)(c * a.B - t.wb);
+            *gp(a.cstart + c) = (uint32_t)(i < (unsigned)t.wn ? L.off[i] : *gp(a.off + c * a.B));
+        }
+        if (last && lane == 0) *gp(a.cstart + a.C) = (uint32_t)N;
+    }
 
     int32_t cnt[4] = {0, 0, 0, 0};   // per lane: at most kPL positions, kWave bags
     int32_t zero_bags = 0;
@@ -558,19 +568,36 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         }
     }
 
-    // bags with no position that this tile owns: the zero default
+    // bags with no position that this tile owns: the zero default.  Usually their
+    // offsets are in the LDS window and their columns were cached by the
+    // transform: then the loop reads LDS only (a global read in it would wait
+    // for every Y store issued so far)
     const int c_base = t.t0 < t.t1 ? t.bf / a.B : 0;
-    for (int b = own_lo + lane; b < own_hi; b += kWave) {
-        if (offat(a, L, t, b) != offat(a, L, t, b + 1)) continue;
-        const int c = b / a.B;
-        // columns of the tile's own bags were cached when transformed
-        const bool cached = t.t0 < t.t1 && c >= c_base && c - c_base < kColCache && c <= t.bl / a.B;
-        const int oo = cached ? L.cout[c - c_base] : (int)*gp(&a.cols[c].out_off);
-        const int dim = cached ? L.cdim[c - c_base] : *gp(&a.cols[c].dim);
-        EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)(b - c * a.B) * a.sumD + oo));
-        for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (a.training) *gp(a.bag_n + b) = 0;
-        zero_bags++;
+    const bool zfast = t.t0 < t.t1 && own_lo >= t.wb && own_hi < t.wb + t.wn &&
+                       own_lo / a.B >= c_base && (own_hi - 1) / a.B <= t.bl / a.B &&
+                       (own_hi - 1) / a.B - c_base < kColCache;
+    if (zfast) {
+        for (int b = own_lo + lane; b < own_hi; b += kWave) {
+            if (L.off[b - t.wb] != L.off[b + 1 - t.wb]) continue;
+            const int c = b / a.B;
+            const int dim = L.cdim[c - c_base];
+            EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(
+                a.Y + (int64_t)(b - c * a.B) * a.sumD + L.cout[c - c_base]));
+            for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (a.training) *gp(a.bag_n + b) = 0;
+            zero_bags++;
+        }
+    } else {
+        for (int b = own_lo + lane; b < own_hi; b += kWave) {
+            if (offat(a, L, t, b) != offat(a, L, t, b + 1)) continue;
+            const int c = b / a.B;
+            EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(
+                a.Y + (int64_t)(b - c * a.B) * a.sumD + *gp(&a.cols[c].out_off)));
+            const int dim = *gp(&a.cols[c].dim);
+            for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (a.training) *gp(a.bag_n + b) = 0;
+            zero_bags++;
+        }
     }
 
     if (a.stats) {
@@ -630,6 +657,7 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     a.stats = stats;
     a.total_rows = plan->total_rows;
     a.sort_flag = reinterpret_cast<uint32_t *>(ws + plan->ws.misc) + 2;
+    a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
     if (training) plan->last_n = n_ids;
     const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
     hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kTileBlock), 0,

@@ -62,6 +62,7 @@ struct WsLayout {
     size_t hist, dtot;                        // radix histograms, digit totals
     size_t seg, ukeys, ucnt, uscan, misc;     // unique rows: segment starts, keys, block counts
     size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
+    size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
     size_t total;
 };
 

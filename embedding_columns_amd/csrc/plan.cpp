@@ -117,6 +117,7 @@ void plan_layout(emb_plan &P)
     L.bpart = take(sizeof(float) * 2 * P.max_tiles * P.max_dim);
     L.bcnt = take(4 * 2 * P.max_tiles);
     L.btick = take(4 * P.max_tiles);
+    L.cstart = take(4 * ((size_t)P.n_cols + 1));
     L.total = o;
 }
 
