@@ -569,6 +569,7 @@ struct BwdArgs {
     int32_t any_mean;           // some column pools by mean
     int32_t zero;               // 0, unknown to the compiler: keeps repeated row loads distinct
     uint32_t total_rows;        // keys >= this are dropped / DEFAULT contributors: no row
+    int32_t xcd_chunk;          // tile order over the XCDs (0: contiguous ranges)
 };
 
 // A segment of at most kSegShort contributors is never cut by a tile boundary:
@@ -649,6 +650,19 @@ __device__ __forceinline__ void row_load(const BwdArgs &a, const DevCol &col, in
     }
 }
 
+template <int OPT, bool BF>
+__device__ __forceinline__ void row_landed(const RowPre &r)
+{
+    if (OPT == EMB_OPT_EMIT) return;
+    landed(r.w[0]);
+    landed(r.w[1]);
+    if (!BF) {
+        landed(r.w[2]);
+        landed(r.w[3]);
+    }
+    if (OPT == EMB_OPT_ADAGRAD) landed(make_float4(r.s[0], r.s[1], r.s[2], r.s[3]));
+}
+
 // the finished gradient g of unique row u (4 fp32 per lane): emit it, or
 // update the row whose old values are in `r`
 template <int OPT, bool BF>
@@ -675,13 +689,13 @@ __device__ __forceinline__ void row_apply(const BwdArgs &a, const DevCol &col, i
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             r.s[v] = r.s[v] + g[v] * g[v];
-            w[v] = w[v] - a.lr * g[v] / (sqrtf(r.s[v]) + a.eps);
+            // hardware square root and reciprocal (about 1 ulp each)
+            w[v] = w[v] - a.lr * g[v] * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(r.s[v]) + a.eps);
         }
         *gp(reinterpret_cast<float4 *>(col.state + e)) = make_float4(r.s[0], r.s[1], r.s[2], r.s[3]);
     }
     if (BF) {
-        const uint64_t o = (uint64_t)(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16)) |
-                           ((uint64_t)(f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)) << 32);
+        const uint64_t o = (uint64_t)bf16x2_rne(w[0], w[1]) | ((uint64_t)bf16x2_rne(w[2], w[3]) << 32);
         *gp(reinterpret_cast<uint64_t *>(static_cast<uint16_t *>(col.weights) + e)) = o;
     } else {
         *gp(reinterpret_cast<float4 *>(static_cast<float *>(col.weights) + e)) = make_float4(w[0], w[1], w[2], w[3]);
@@ -839,6 +853,11 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 wt[j] = p + j < ge ? L.wt[pl] : 0.f;
                 x[j] = *gp(reinterpret_cast<const float4 *>(gq + (int64_t)(L.bag[pl] - cB) * a.sumD));
             }
+            // every load of the batch lands before the row stores below
+#pragma unroll
+            for (int j = 0; j < U; j++) row_landed<OPT, BF>(pre[j]);
+#pragma unroll
+            for (int j = 0; j < U; j++) landed(x[j]);
 #pragma unroll
             for (int j = 0; j < U; j++) {
                 if (p + j < ge) {
@@ -1028,7 +1047,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     const int w = threadIdx.x / kWave, lane = lane_id();
     BwdLds &L = lds[w];
     BTile t;
-    t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
+    t.k = xcd_block(blockIdx.x, gridDim.x, a.xcd_chunk) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     const int nv = (int)*gp(a.misc);
     const int x0 = (int)min<int64_t>(t.k * a.T, nv), x1 = (int)min<int64_t>((t.k + 1) * a.T, nv);
@@ -1099,7 +1118,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         const int p = x0 + lane + kWave * i;
         if (p >= t.t0 && p < t.t1) {
             L.bag[p - t.t0] = bagr[i];
-            L.wt[p - t.t0] = 1.0f / (float)nr[i];   // mean weight; sum columns use 1
+            L.wt[p - t.t0] = __builtin_amdgcn_rcpf((float)nr[i]);   // mean weight; sum columns use 1
         }
     }
     if (lane == 0) L.njob = 0;
@@ -1250,7 +1269,13 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.any_mean = plan->any_mean ? 1 : 0;
     a.zero = 0;
     a.total_rows = plan->total_rows;
-    const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
+    // Sorted segments of a few long columns change cost along the tile range
+    // (hot rows: few segments; the cold tail: one row update per contributor):
+    // chunks spread them over the XCDs.  With many columns each contiguous XCD
+    // range mixes enough of them, and keeps one column's rows and gradient
+    // slices in one L2.
+    a.xcd_chunk = plan->n_cols >= 32 ? 0 : 16;
+    const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, a.xcd_chunk);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(kTileBlock);
     if (a.opt == EMB_OPT_EMIT)

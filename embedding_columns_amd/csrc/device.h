@@ -160,26 +160,65 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t v)
     return v;
 }
 
+// Wait here for loaded values (an empty asm that reads them and orders memory).
+// A loop that issues a batch of loads and then stores results in divergent
+// branches should let every load land before its first store: the one vector
+// memory counter retires loads and stores in order, so a load consumed after a
+// store would also wait for that store.
+__device__ __forceinline__ void landed(const float4 &v)
+{
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w) : "memory");
+}
+__device__ __forceinline__ void landed(const uint2 &v)
+{
+    asm volatile("" ::"v"(v.x), "v"(v.y) : "memory");
+}
+__device__ __forceinline__ void landed(uint32_t v)
+{
+    asm volatile("" ::"v"(v) : "memory");
+}
+__device__ __forceinline__ void landed(float v)
+{
+    asm volatile("" ::"v"(v) : "memory");
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet)
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// Block order over the 8 XCDs.  Hardware block b runs on XCD b mod 8, and each
+// XCD starts its blocks in order.
+//   chunk == 0: XCD x takes one contiguous range of tiles (x * nb / 8 ...).  Its
+//     L2 then holds the rows, offsets and gradient slices of few columns.
+//   chunk > 0: the i-th block of XCD x takes tile
+//     ((i / chunk) * 8 + x) * chunk + i mod chunk.  All XCDs move through the
+//     tile range together, so tiles whose cost changes along the range (hot
+//     and cold rows of a few long columns) are spread evenly over them.  The
+//     grid is padded to a multiple of 8 * chunk blocks; blocks past the last
+//     tile exit at once.
+__host__ __device__ __forceinline__ int64_t xcd_grid(int64_t ntiles, int chunk)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    const int64_t g = chunk ? 8 * (int64_t)chunk : 1;
+    return (ntiles + g - 1) / g * g;
 }
 
-// XCD-aware block order: consecutive hardware block ids go round-robin over
-// the 8 XCDs; map them so each XCD walks one contiguous range of tiles (its own
-// L2 then caches the rows of fewer columns).
-__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb, int chunk)
 {
     const int64_t x = b & 7, i = b >> 3;
-    const int64_t base = nb >> 3, rem = nb & 7;
-    return x * base + (x < rem ? x : rem) + i;
+    if (chunk == 0) {
+        const int64_t base = nb >> 3, rem = nb & 7;
+        return x * base + (x < rem ? x : rem) + i;
+    }
+    return ((i / chunk) * 8 + x) * chunk + i % chunk;
+}
+
+// fp32 pair -> packed bf16 pair (lo in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 }  // namespace emb

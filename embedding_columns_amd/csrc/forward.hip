@@ -124,7 +124,7 @@ __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int
     const int s = bag - c * a.B;
     if (qa) {
         float o[V];
-        const float sc = n == 0 ? 0.f : (col.pool == EMB_POOL_MEAN ? 1.0f / (float)n : 1.0f);
+        const float sc = n == 0 ? 0.f : (col.pool == EMB_POOL_MEAN ? __builtin_amdgcn_rcpf((float)n) : 1.0f);
 #pragma unroll
         for (int v = 0; v < V; v++) o[v] = acc[v] * sc;
         EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V));
@@ -241,33 +241,44 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             int r[U];
             RowRaw<BF> h[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) r[u] = (p + u < ge) ? L.rows[p + u - t.t0] : -1;
+            for (int u = 0; u < U; u++) {
+                const int x = L.rows[min(p + u, ge - 1) - t.t0];   // unconditional LDS reads
+                r[u] = (p + u < ge) ? x : -1;
+            }
 #pragma unroll
             for (int u = 0; u < U; u++)
-                h[u] = *gp(reinterpret_cast<const RowRaw<BF> *>(wbase + (int64_t)max(r[u], 0) * rstride));
+                h[u] = *gp(reinterpret_cast<const RowRaw<BF> *>(
+                    wbase + (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
+#pragma unroll
+            for (int u = 0; u < U; u++) landed(h[u]);   // before the bag-end stores below
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int pp = p + u;
+                if (pp < ge && pp == bend) {       // bag b ended just before pp
+                    if (before) {
+#pragma unroll
+                        for (int v = 0; v < V; v++) hacc[v] = acc[v];
+                        hcnt = cnt; hbag = b; hpass = false;
+                    } else {
+                        bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
+                    }
+#pragma unroll
+                    for (int v = 0; v < V; v++) acc[v] = 0.f;
+                    cnt = 0;
+                    b = next_bag<W>(a, L, t, b);
+                    bend = offw<W>(a, L, t, b + 1);
+                    before = false;
+                }
+                // every loaded row is consumed here, outside any branch: a load
+                // whose result is never read would make the next batch wait for
+                // every outstanding load and store before reusing its registers
+                const float4 w = row_f32(h[u]);
+                const bool use = pp < ge && r[u] >= 0;
+                acc[0] += use ? w.x : 0.f;
+                acc[1] += use ? w.y : 0.f;
+                acc[2] += use ? w.z : 0.f;
+                acc[3] += use ? w.w : 0.f;
                 if (pp < ge) {
-                    if (pp == bend) {              // bag b ended just before pp
-                        if (before) {
-#pragma unroll
-                            for (int v = 0; v < V; v++) hacc[v] = acc[v];
-                            hcnt = cnt; hbag = b; hpass = false;
-                        } else {
-                            bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
-                        }
-#pragma unroll
-                        for (int v = 0; v < V; v++) acc[v] = 0.f;
-                        cnt = 0;
-                        b = next_bag<W>(a, L, t, b);
-                        bend = offw<W>(a, L, t, b + 1);
-                        before = false;
-                    }
-                    if (r[u] >= 0) {
-                        const float4 w = row_f32(h[u]);
-                        acc[0] += w.x; acc[1] += w.y; acc[2] += w.z; acc[3] += w.w;
-                    }
                     cnt += (r[u] != -1);
                     if (q == 0) L.pbag[pp - t.t0] = b;
                 }
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     const int w = threadIdx.x / kWave, lane = lane_id();
     WaveLds &L = lds[w];
     TileCtx t;
-    t.k = xcd_block(blockIdx.x, gridDim.x) * kTileWaves + w;
+    t.k = xcd_block(blockIdx.x, gridDim.x, 0) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
     if (a.training && t.k == 0 && lane == 0) *gp(a.sort_flag) = 0u;
     const int N = (int)a.N, T = a.T, nbag = a.C * a.B;
@@ -659,7 +670,8 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     a.sort_flag = reinterpret_cast<uint32_t *>(ws + plan->ws.misc) + 2;
     a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
     if (training) plan->last_n = n_ids;
-    const int64_t blocks = (a.ntiles + kTileWaves - 1) / kTileWaves;
+    // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
+    const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
     hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kTileBlock), 0,
                        static_cast<hipStream_t>(stream), a);
     hipError_t e = hipGetLastError();
