@@ -263,18 +263,19 @@ class EmbeddingColumns:
         self.plan_mem = _u8(pb, self.device)
         self.workspace = _u8(wb, self.device, zero=True)
         self.plan = emb_plan_create(descs, self.batch, self.max_ids, self.opts, self.plan_mem)
+        self._destroy = lib().emb_plan_destroy   # still callable while the interpreter exits
         self.row_base = [0]
         for c in self.cols:
             self.row_base.append(self.row_base[-1] + c.rows)
 
     def __del__(self):
-        p = getattr(self, "plan", None)
-        if p:
+        p, destroy = getattr(self, "plan", None), getattr(self, "_destroy", None)
+        if p and destroy:
             try:
                 torch.cuda.synchronize(self.device)
             except Exception:
                 pass
-            lib().emb_plan_destroy(p)
+            destroy(p)
             self.plan = None
 
     def forward(self, offsets, ids=None, fvals=None, keyed_rows=None, training=True, stats=None,
@@ -321,15 +322,16 @@ class KeyedTable:
         self.mem = _u8(nbytes, self.device)
         self.table = emb_table_create(self.capacity, self.row_capacity, self.dim, threshold,
                                       init_std, self.mem)
+        self._destroy = lib().emb_table_destroy
         ptr = emb_table_rows(self.table)
         off = ptr - self.mem.data_ptr()
         self.rows = self.mem[off:off + 4 * self.row_capacity * self.dim].view(torch.float32).view(
             self.row_capacity, self.dim)
 
     def __del__(self):
-        t = getattr(self, "table", None)
-        if t:
-            lib().emb_table_destroy(t)
+        t, destroy = getattr(self, "table", None), getattr(self, "_destroy", None)
+        if t and destroy:
+            destroy(t)
             self.table = None
 
     def bulk_insert(self, keys, rows=None, stats=None):

@@ -92,21 +92,19 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDi
     return tot;
 }
 
-// per-block digit histogram; equal digits within a wavefront are added once
-__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
-                                                 int shift, uint32_t *__restrict__ hist,
-                                                 int64_t nblk, uint32_t *__restrict__ misc,
-                                                 const uint32_t *need)
+// digit histogram of one tile of kSortTile keys; equal digits within a
+// wavefront are added once
+__device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys, int64_t n, int shift,
+                                          uint32_t *__restrict__ hist, int64_t nblk,
+                                          uint32_t *__restrict__ misc, int64_t tile, uint32_t *h)
 {
-    if (need && *gp(need) == 0u) return;             // the column sort did everything
     // the first pass starts the count of valid contributors at n; the last
     // pass lowers it to the position of the first sentinel key
-    if (shift == 0 && blockIdx.x == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
-    __shared__ uint32_t h[kRadix];
+    if (shift == 0 && tile == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
     const int t = threadIdx.x, lane = lane_id();
     for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int64_t base = tile * kSortTile;
     uint32_t k[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
@@ -128,16 +126,25 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
         }
     }
     __syncthreads();
-    for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
+    for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + tile] = h[d];
+    __syncthreads();
 }
 
-// one block per digit: exclusive scan of hist[d][0..nblk) in place, total -> dtot[d]
-__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
-                                                 uint32_t *__restrict__ dtot, const uint32_t *need)
+__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
+                                                 int shift, uint32_t *__restrict__ hist,
+                                                 int64_t nblk, uint32_t *__restrict__ misc,
+                                                 const uint32_t *need)
 {
-    if (need && *gp(need) == 0u) return;
-    __shared__ uint32_t tmp[kWavesPerBlock];
-    uint32_t *h = hist + (int64_t)blockIdx.x * nblk;
+    if (need && *gp(need) == 0u) return;             // the column sort did everything
+    __shared__ uint32_t h[kRadix];
+    hist_tile(keys, n, shift, hist, nblk, misc, blockIdx.x, h);
+}
+
+// exclusive scan of one digit's block counts hist[d][0..nblk) in place, total -> dtot[d]
+__device__ __forceinline__ void scan_digit(uint32_t *__restrict__ hist, int64_t nblk,
+                                           uint32_t *__restrict__ dtot, int d, uint32_t *tmp)
+{
+    uint32_t *h = hist + (int64_t)d * nblk;
     uint32_t carry = 0;
     for (int64_t s = 0; s < nblk; s += kBlock) {
         const int64_t i = s + threadIdx.x;
@@ -147,7 +154,16 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, i
         if (i < nblk) h[i] = carry + ex;
         carry += tot;
     }
-    if (threadIdx.x == 0) dtot[blockIdx.x] = carry;
+    if (threadIdx.x == 0) dtot[d] = carry;
+}
+
+// one block per digit
+__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
+                                                 uint32_t *__restrict__ dtot, const uint32_t *need)
+{
+    if (need && *gp(need) == 0u) return;
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    scan_digit(hist, nblk, dtot, blockIdx.x, tmp);
 }
 
 struct SortLds {
@@ -159,19 +175,16 @@ struct SortLds {
     uint32_t tmp[kWavesPerBlock];
 };
 
-__global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict__ kin,
-                                                    const uint32_t *__restrict__ vin,
-                                                    uint32_t *__restrict__ kout,
-                                                    uint32_t *__restrict__ vout, int64_t n,
-                                                    int shift, const uint32_t *__restrict__ hist,
-                                                    const uint32_t *__restrict__ dtot, int64_t nblk,
-                                                    uint32_t sentinel, uint32_t *__restrict__ misc,
-                                                    const uint32_t *need)
+__device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
+                                             const uint32_t *__restrict__ vin,
+                                             uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                             int64_t n, int shift, const uint32_t *__restrict__ hist,
+                                             const uint32_t *__restrict__ dtot, int64_t nblk,
+                                             uint32_t sentinel, uint32_t *__restrict__ misc,
+                                             int64_t tile, SortLds &S)
 {
-    if (need && *gp(need) == 0u) return;
-    __shared__ SortLds S;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int64_t base = tile * kSortTile;
     const int cnt = (int)min<int64_t>(kSortTile, n - base);
 
     // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
 #pragma unroll
         for (int i = 0; i < kDigitsPerThread; i++) {
             const int d = t * kDigitsPerThread + i;
-            S.gbase[d] = ex[i] + hist[(int64_t)d * nblk + blockIdx.x];
+            S.gbase[d] = ex[i] + hist[(int64_t)d * nblk + tile];
         }
         for (int d = t; d < kRadix; d += kBlock)
             for (int i = 0; i < kWavesPerBlock; i++) S.run[i][d] = 0;
@@ -268,6 +281,21 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
         for (int o = 1; o < kWave; o <<= 1) first_sentinel = min(first_sentinel, (uint32_t)__shfl_xor((int)first_sentinel, o, kWave));
         if (lane == 0 && first_sentinel != 0xFFFFFFFFu) atomicMin(misc, first_sentinel);
     }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict__ kin,
+                                                    const uint32_t *__restrict__ vin,
+                                                    uint32_t *__restrict__ kout,
+                                                    uint32_t *__restrict__ vout, int64_t n,
+                                                    int shift, const uint32_t *__restrict__ hist,
+                                                    const uint32_t *__restrict__ dtot, int64_t nblk,
+                                                    uint32_t sentinel, uint32_t *__restrict__ misc,
+                                                    const uint32_t *need)
+{
+    if (need && *gp(need) == 0u) return;
+    __shared__ SortLds S;
+    scatter_tile(kin, vin, kout, vout, n, shift, hist, dtot, nblk, sentinel, misc, blockIdx.x, S);
 }
 
 // ------------------------------------------------ column-local sort in LDS
@@ -1057,25 +1085,31 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     // and of the short segment that may extend it, all loaded in one round
     constexpr int kPL = kSegSpan / kWave;
     int bagr[kPL], nr[kPL];
+    // (loads at clamped indices, issued by every lane: a load inside a per-lane
+    // branch makes the compiler wait for it before the next one)
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
         const int p = x0 + lane + kWave * i;
-        bagr[i] = p < nv ? (int)*gp(a.sval + p) : 0;
+        const int v = (int)*gp(a.sval + min(p, nv - 1));
+        bagr[i] = p < nv ? v : 0;
     }
     {
         uint32_t kv[kKeyWin / kWave];
 #pragma unroll
         for (int j = 0; j < kKeyWin / kWave; j++) {
             const int p = x0 - kSegShort + lane + kWave * j;
-            kv[j] = (p >= 0 && p < nv) ? *gp(a.skeys + p) : (p < 0 ? 0u : 0xFFFFFFFFu);
+            const uint32_t v = *gp(a.skeys + min(max(p, 0), nv - 1));
+            kv[j] = (p >= 0 && p < nv) ? v : (p < 0 ? 0u : 0xFFFFFFFFu);
         }
 #pragma unroll
         for (int j = 0; j < kKeyWin / kWave; j++) L.kw[lane + kWave * j] = kv[j];
     }
+    if (a.any_mean) {
 #pragma unroll
-    for (int i = 0; i < kPL; i++) {
-        const int p = x0 + lane + kWave * i;
-        nr[i] = (a.any_mean && p < nv) ? *gp(a.bag_n + bagr[i]) : 1;
+        for (int i = 0; i < kPL; i++) nr[i] = *gp(a.bag_n + bagr[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPL; i++) nr[i] = 1;
     }
     wave_sync();
     t.t0 = seg_boundary(L, x0, x0, nv, a.T);
@@ -1195,11 +1229,13 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     const bool from_keys = plan->opt != EMB_OPT_EMIT && !uniq_keys && !n_uniq && !stats;
     plan->seg_from_keys = from_keys;
     const int passes = sort_passes(plan);
-    // segments found from the keys can also come from the column sort, which
-    // leaves dropped / DEFAULT keys inside each column; the global passes then
-    // run only if a column was too large for it (misc[2], cleared by the forward)
+    // Segments found from the keys can come from the column sort, which leaves
+    // dropped / DEFAULT keys inside each column.  It can only succeed when every
+    // column fits (n <= C * kColCap at least); a column that does not raises
+    // misc[2] (cleared by the forward) and the global radix passes, which
+    // otherwise return at once, sort everything.
     const uint32_t *need = nullptr;
-    if (from_keys) {
+    if (from_keys && n <= (int64_t)plan->n_cols * kColCap) {
         uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
         hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, kf, vf,
                            n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,

@@ -174,10 +174,11 @@ def test_hot_row_segment_spanning_many_tiles_sgd(tile):
     check_rows_sgd(cols[0], host_w, to_np(st.gw[0]), oc.weights[0], urow, ub[:, :32], w.lr)
 
 
-@pytest.mark.parametrize("big", [12288, 12289, 20000])
+@pytest.mark.parametrize("big", [12288, 12289, 20000, 40000])
 def test_segments_from_keys_column_sort_capacity(big):
     # the column-local sort takes columns of up to 12288 positions; one larger
-    # column sends the whole step to the global radix passes
+    # column sends the whole step to the global radix passes (behind the column
+    # sort while n <= 3 * 12288, without it beyond)
     cols = [W.Column(W.HASH, W.SUM, W.F32, 300, 16, 0, 1 << 40),
             W.Column(W.IDENTITY, W.MEAN, W.F32, 5000, 8),
             W.Column(W.HASH, W.MEAN, W.F32, 40, 32, 0, 1 << 40)]
