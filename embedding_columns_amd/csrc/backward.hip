@@ -132,10 +132,8 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys, int
 
 __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
                                                  int shift, uint32_t *__restrict__ hist,
-                                                 int64_t nblk, uint32_t *__restrict__ misc,
-                                                 const uint32_t *need)
+                                                 int64_t nblk, uint32_t *__restrict__ misc)
 {
-    if (need && *gp(need) == 0u) return;             // the column sort did everything
     __shared__ uint32_t h[kRadix];
     hist_tile(keys, n, shift, hist, nblk, misc, blockIdx.x, h);
 }
@@ -159,9 +157,8 @@ __device__ __forceinline__ void scan_digit(uint32_t *__restrict__ hist, int64_t 
 
 // one block per digit
 __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
-                                                 uint32_t *__restrict__ dtot, const uint32_t *need)
+                                                 uint32_t *__restrict__ dtot)
 {
-    if (need && *gp(need) == 0u) return;
     __shared__ uint32_t tmp[kWavesPerBlock];
     scan_digit(hist, nblk, dtot, blockIdx.x, tmp);
 }
@@ -290,10 +287,8 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
                                                     uint32_t *__restrict__ vout, int64_t n,
                                                     int shift, const uint32_t *__restrict__ hist,
                                                     const uint32_t *__restrict__ dtot, int64_t nblk,
-                                                    uint32_t sentinel, uint32_t *__restrict__ misc,
-                                                    const uint32_t *need)
+                                                    uint32_t sentinel, uint32_t *__restrict__ misc)
 {
-    if (need && *gp(need) == 0u) return;
     __shared__ SortLds S;
     scatter_tile(kin, vin, kout, vout, n, shift, hist, dtot, nblk, sentinel, misc, blockIdx.x, S);
 }
@@ -302,12 +297,10 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
 //
 // Positions are column-major and a column's keys (row_base_c + row) lie in its
 // own key range, so sorting all keys equals sorting each column's positions in
-// place.  When every column has at most kColCap positions, one workgroup per
-// column sorts them entirely in LDS (a stable LSD radix sort on the row within
-// the column, 7-bit digits), with dropped / DEFAULT keys last inside the
-// column instead of at the end of the array.  A larger column raises a flag in
-// misc[2] and the global radix passes, which otherwise return at once, sort
-// everything.
+// place.  One workgroup per column sorts a column of at most kColCap positions
+// entirely in LDS (a stable LSD radix sort on the row within the column, 7-bit
+// digits), with dropped / DEFAULT keys last inside the column instead of at the
+// end of the array; a larger column goes through global memory in chunks.
 
 constexpr int kCSWaves = 16;
 constexpr int kCSBlock = kCSWaves * kWave;
@@ -322,13 +315,136 @@ struct ColSortLds {
     uint32_t key[2][kColCap];          // local keys, ping-pong
     uint16_t idx[2][kColCap];          // position within the column
     uint32_t run[kCSWaves][kCSRadix];  // per-wave digit counts, then destinations
-    uint32_t dpre[kCSRadix];
+    uint32_t dpre[kCSRadix + 1];       // digit offsets (chunked sort); [kCSRadix]: a scan carry
 };
 
-__global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict__ kin,
-                                                    const uint32_t *__restrict__ vin,
-                                                    uint32_t *kout, uint32_t *vout, int64_t n,
-                                                    const uint32_t *__restrict__ cstart,
+// Digit-major destinations of one ranking round: thread d < kCSRadix reads
+// digit d's per-wave counts S.run[k][d], and S.run[k][d] becomes base[d] plus
+// the counts of digit d in waves before k (base: the digit starts).  Returns
+// digit d's total to thread d.
+__device__ __forceinline__ uint32_t cs_digit_bases(ColSortLds &S, bool chunk_bases)
+{
+    const int t = threadIdx.x, lane = lane_id();
+    uint32_t cw[kCSWaves], incl = 0, tot = 0;
+    if (t < kCSRadix) {
+#pragma unroll
+        for (int k = 0; k < kCSWaves; k++) {
+            cw[k] = S.run[k][t];
+            tot += cw[k];
+        }
+        incl = tot;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += y;
+        }
+        incl -= tot;                                   // exclusive within the wave
+        if (t == kWave - 1) S.dpre[kCSRadix] = incl + tot;   // digits 0..63 in total
+    }
+    __syncthreads();
+    if (t < kCSRadix) {
+        // in-LDS sort: digit starts from the scan; chunked sort: running
+        // per-digit offsets of the column, kept in S.dpre
+        uint32_t base = chunk_bases ? S.dpre[t] : incl + (t >= kWave ? S.dpre[kCSRadix] : 0u);
+#pragma unroll
+        for (int k = 0; k < kCSWaves; k++) {
+            S.run[k][t] = base;
+            base += cw[k];
+        }
+    }
+    __syncthreads();
+    return tot;
+}
+
+// A column of more than kColCap positions, sorted by its workgroup through
+// global memory: per pass (7-bit digit of the local key) a digit histogram of
+// the column, then chunks of kColCap keys ranked stably in LDS and scattered to
+// running per-digit offsets, ping-ponging between the column's ranges of the
+// two key / bag arrays (A holds the input).  The result ends in kout / vout.
+__device__ void col_sort_big(ColSortLds &S, uint32_t *kA, uint32_t *vA, uint32_t *kB, uint32_t *vB,
+                             uint32_t *kout, uint32_t *vout, int P0, int cnt, uint32_t rb,
+                             uint32_t rows, uint32_t total_rows, int passes)
+{
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    auto lkey = [&](uint32_t k) { return k < total_rows ? k - rb : rows + (k - total_rows); };
+    for (int pass = 0; pass < passes; pass++) {
+        const int shift = pass * kCSBits;
+        uint32_t *ks = (pass & 1) ? kB : kA, *vs = (pass & 1) ? vB : vA;
+        uint32_t *kd = (pass & 1) ? kA : kB, *vd = (pass & 1) ? vA : vB;
+        // digit histogram of the whole column -> running offsets S.dpre[d]
+        if (t < kCSRadix) S.dpre[t] = 0u;
+        __syncthreads();
+        for (int i = t; i < cnt; i += kCSBlock)
+            atomicAdd(&S.dpre[(lkey(*gp(ks + P0 + i)) >> shift) & (kCSRadix - 1)], 1u);
+        __syncthreads();
+        if (t < kCSRadix) {
+            const uint32_t v = S.dpre[t];
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += y;
+            }
+            if (t == kWave - 1) S.dpre[kCSRadix] = incl;
+            S.run[0][t] = incl - v;
+        }
+        __syncthreads();
+        if (t < kCSRadix) S.dpre[t] = S.run[0][t] + (t >= kWave ? S.dpre[kCSRadix] : 0u);
+        __syncthreads();
+        for (int c0 = 0; c0 < cnt; c0 += kColCap) {
+            const int m = min(kColCap, cnt - c0);
+            const int per = ((m + kCSWaves * kWave - 1) / (kCSWaves * kWave)) * kWave;
+            for (int d = lane; d < kCSRadix; d += kWave) S.run[w][d] = 0;
+            wave_sync();
+            uint32_t rank[kCSItems], dig[kCSItems], prev[kCSItems], key[kCSItems];
+            int lead[kCSItems];
+#pragma unroll
+            for (int j = 0; j < kCSItems; j++) {
+                const int i = w * per + j * kWave + lane;
+                key[j] = (j * kWave < per && i < m) ? *gp(ks + P0 + c0 + i) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < kCSItems; j++) {
+                const int i = w * per + j * kWave + lane;
+                const bool in = j * kWave < per && i < m;
+                const uint32_t d = in ? (lkey(key[j]) >> shift) & (kCSRadix - 1) : 0u;
+                const uint64_t peers = match_digit<kCSBits>(d, in);
+                lead[j] = in ? __ffsll((unsigned long long)peers) - 1 : lane;
+                rank[j] = (uint32_t)__popcll(peers & lt_mask);
+                dig[j] = d;
+                prev[j] = 0u;
+                if (in && lead[j] == lane) prev[j] = atomicAdd(&S.run[w][d], (uint32_t)__popcll(peers));
+            }
+#pragma unroll
+            for (int j = 0; j < kCSItems; j++) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
+            __syncthreads();
+            const uint32_t tot = cs_digit_bases(S, true);
+#pragma unroll
+            for (int j = 0; j < kCSItems; j++) {
+                const int i = w * per + j * kWave + lane;
+                if (j * kWave < per && i < m) {
+                    const uint32_t o = S.run[w][dig[j]] + rank[j];
+                    *gp(kd + P0 + o) = key[j];
+                    *gp(vd + P0 + o) = *gp(vs + P0 + c0 + i);
+                }
+            }
+            if (t < kCSRadix) S.dpre[t] += tot;
+            __syncthreads();
+        }
+    }
+    uint32_t *kr = (passes & 1) ? kB : kA, *vr = (passes & 1) ? vB : vA;
+    if (kr != kout) {
+        for (int i = t; i < cnt; i += kCSBlock) {
+            *gp(kout + P0 + i) = *gp(kr + P0 + i);
+            *gp(vout + P0 + i) = *gp(vr + P0 + i);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vin, uint32_t *kspare,
+                                                    uint32_t *vspare, uint32_t *kout, uint32_t *vout,
+                                                    int64_t n, const uint32_t *__restrict__ cstart,
                                                     const uint32_t *__restrict__ row_base,
                                                     uint32_t total_rows, uint32_t *misc)
 {
@@ -338,14 +454,14 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict_
     if (c == 0 && t == 0) *gp(misc) = (uint32_t)n;   // every position is a contributor slot
     // the column's positions, recorded by the forward
     const int P0 = (int)cstart[c], cnt = (int)cstart[c + 1] - P0;
-    if (cnt > kColCap) {
-        if (t == 0) *gp(misc + 2) = 1u;               // the global passes take over
-        return;
-    }
     if (cnt == 0) return;
     const uint32_t rb = row_base[c], rows = row_base[c + 1] - rb;
     const int bits = 32 - __clz((int)(rows + 1));
     const int passes = (bits + kCSBits - 1) / kCSBits;
+    if (cnt > kColCap) {
+        col_sort_big(S, kin, vin, kspare, vspare, kout, vout, P0, cnt, rb, rows, total_rows, passes);
+        return;
+    }
 
     // local key: the row, or rows / rows + 1 for dropped / DEFAULT
     {
@@ -398,36 +514,8 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(const uint32_t *__restrict_
 #pragma unroll
         for (int j = 0; j < kCSItems; j++) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
         __syncthreads();
-        // destinations, digit-major over (digit, wave): thread d < 128 holds
-        // digit d's per-wave counts; a scan over the two waves of digits gives
-        // each digit's start
-        uint32_t cw[kCSWaves], incl = 0;
-        if (t < kCSRadix) {
-            uint32_t tot = 0;
-#pragma unroll
-            for (int k = 0; k < kCSWaves; k++) {
-                cw[k] = S.run[k][t];
-                tot += cw[k];
-            }
-            incl = tot;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o, kWave);
-                if (lane >= o) incl += y;
-            }
-            incl -= tot;                                   // exclusive within the wave
-            if (t == kWave - 1) S.dpre[0] = incl + tot;    // digits 0..63 in total
-        }
-        __syncthreads();
-        if (t < kCSRadix) {
-            uint32_t base = incl + (t >= kWave ? S.dpre[0] : 0u);
-#pragma unroll
-            for (int k = 0; k < kCSWaves; k++) {
-                S.run[k][t] = base;
-                base += cw[k];
-            }
-        }
-        __syncthreads();
+        // destinations, digit-major over (digit, wave)
+        cs_digit_bases(S, false);
 #pragma unroll
         for (int j = 0; j < kCSItems; j++) {
             const int i = w * per + j * kWave + lane;
@@ -1229,26 +1317,26 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     const bool from_keys = plan->opt != EMB_OPT_EMIT && !uniq_keys && !n_uniq && !stats;
     plan->seg_from_keys = from_keys;
     const int passes = sort_passes(plan);
-    // Segments found from the keys can come from the column sort, which leaves
-    // dropped / DEFAULT keys inside each column.  It can only succeed when every
-    // column fits (n <= C * kColCap at least); a column that does not raises
-    // misc[2] (cleared by the forward) and the global radix passes, which
-    // otherwise return at once, sort everything.
-    const uint32_t *need = nullptr;
+    // Segments found from the keys come from the column sort when the average
+    // column fits its LDS (n <= C * kColCap; a larger column is sorted by its
+    // workgroup through global memory); the sort leaves dropped / DEFAULT keys
+    // inside each column.  Otherwise the global radix passes sort everything.
     if (from_keys && n <= (int64_t)plan->n_cols * kColCap) {
         uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
-        hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, kf, vf,
-                           n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,
+        hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, k1, v1,
+                           kf, vf, n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,
                            plan->total_rows, misc);
-        need = misc + 2;
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("col_sort launch: ") + hipGetErrorString(e));
+        return EMB_OK;
     }
     for (int p = 0; p < passes; p++) {
         const int shift = p * kRadixBits;
-        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc, need);
-        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot, need);
+        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
+        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
         hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
                            shift, hist, dtot, nblk, plan->total_rows,
-                           (from_keys && p == passes - 1) ? misc : nullptr, need);
+                           (from_keys && p == passes - 1) ? misc : nullptr);
         std::swap(k0, k1);
         std::swap(v0, v1);
     }

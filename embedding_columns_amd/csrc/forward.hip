@@ -47,7 +47,6 @@ struct FwdArgs {
     uint32_t *tick;
     int64_t *stats;
     uint32_t total_rows;
-    uint32_t *sort_flag;     // set by the backward's column sort when a column is too large
     uint32_t *cstart;        // training: first position of each column, [C + 1]
 };
 
@@ -440,7 +439,6 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     TileCtx t;
     t.k = xcd_block(blockIdx.x, gridDim.x, 0) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
-    if (a.training && t.k == 0 && lane == 0) *gp(a.sort_flag) = 0u;
     const int N = (int)a.N, T = a.T, nbag = a.C * a.B;
     // nominal range [k T, (k+1) T); the real one moves each end to the end of a
     // short bag that the nominal boundary cuts
@@ -667,7 +665,6 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
     a.stats = stats;
     a.total_rows = plan->total_rows;
-    a.sort_flag = reinterpret_cast<uint32_t *>(ws + plan->ws.misc) + 2;
     a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
     if (training) plan->last_n = n_ids;
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
