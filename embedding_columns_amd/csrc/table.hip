@@ -3,9 +3,9 @@
 // Monolith (Sec. 2.1 "Hash Table") keeps every distinct ID in its own slot (no two
 // IDs share an embedding) and admits an ID only once its occurrence count reaches
 // a tunable threshold.  Here the table is GPU open addressing over a power-of-two
-// slot array (linear probing from splitmix64(key) & (capacity-1), insertion by
-// 64-bit compare-and-swap on the slot key) instead of Monolith's CPU cuckoo
-// table; slot placement never shows in results.
+// slot array (buckets of 16 slots probed with a per-key odd stride from
+// splitmix64(key), insertion by 64-bit compare-and-swap on the slot key) instead
+// of Monolith's CPU cuckoo table; slot placement never shows in results.
 //
 // One lookup-or-insert step is three launches so that admission is decided on
 // the whole batch's counts (every occurrence of a key in the step sees the same
@@ -82,74 +82,99 @@ __device__ __forceinline__ int64_t probe_insert_slots(const TabArgs &a, unsigned
     return -1;
 }
 
-// The same probe sequence read 16 slots (two 64-byte lines) per round: the line
-// holding the home slot and the next one, so that nearly every probe sequence
-// ends after one round trip instead of one per slot.  Plain loads may see an
-// empty slot that another thread has just filled; the compare-and-swap then
-// returns the real key.  Keys never change once placed.
-constexpr int kLineSlots = 8;
+// Tables of at least kBucketSlots slots probe whole buckets of 16 slots (128
+// bytes of keys, read as eight 16-byte loads in flight): the home bucket
+// b0 = splitmix64(key) mod nb, then b0 + i * step with an odd step taken from the
+// hash's high bits, so every bucket is visited once in nb steps.  Linear probing
+// from a home slot builds long runs of full slots at the 0.75-0.8 load of a
+// prepopulated table, and the slowest probe of a step set its time; stepping
+// over buckets by a per-key stride keeps every probe sequence short.  Within a
+// bucket the first empty slot takes the key by compare-and-swap; plain loads may
+// see a slot empty that another thread has just filled, and the CAS then returns
+// the real key.  Keys never change once placed, so a key is never placed twice.
+constexpr int kBucketSlots = 16;
+
+__device__ __forceinline__ void bucket_start(const TabArgs &a, unsigned long long key, uint64_t &b,
+                                             uint64_t &step, uint64_t &nbm)
+{
+    const uint64_t h = splitmix64(key);
+    nbm = (uint64_t)a.cap / kBucketSlots - 1;
+    b = h & nbm;
+    step = ((h >> 32) & nbm) | 1u;
+}
+
+__device__ __forceinline__ void bucket_keys(const TabArgs &a, uint64_t b, unsigned long long (&kk)[kBucketSlots])
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(a.keys + b * kBucketSlots);
+    uint4 v[kBucketSlots / 2];
+#pragma unroll
+    for (int j = 0; j < kBucketSlots / 2; j++) v[j] = *gp(q + j);
+#pragma unroll
+    for (int j = 0; j < kBucketSlots / 2; j++) {
+        kk[2 * j] = ((unsigned long long)v[j].y << 32) | v[j].x;
+        kk[2 * j + 1] = ((unsigned long long)v[j].w << 32) | v[j].z;
+    }
+}
 
 __device__ __forceinline__ int64_t probe_insert(const TabArgs &a, unsigned long long key,
                                                 bool &inserted, int64_t &probes)
 {
-    if (a.cap < 2 * kLineSlots) return probe_insert_slots(a, key, inserted, probes);
-    const uint64_t mask = (uint64_t)a.cap - 1;
-    uint64_t h = splitmix64(key) & mask;
+    if (a.cap < kBucketSlots) return probe_insert_slots(a, key, inserted, probes);
+    uint64_t b, step, nbm;
+    bucket_start(a, key, b, step, nbm);
     inserted = false;
-    int64_t scanned = 0;
-    while (scanned < a.cap) {
-        const uint64_t l0 = h & ~(uint64_t)(kLineSlots - 1);
-        const uint64_t l1 = (l0 + kLineSlots) & mask;
-        const int first = (int)(h - l0);
-        unsigned long long kk[2 * kLineSlots];
-        const uint4 *q0 = reinterpret_cast<const uint4 *>(a.keys + l0);
-        const uint4 *q1 = reinterpret_cast<const uint4 *>(a.keys + l1);
-        uint4 v[kLineSlots];
+    for (uint64_t i = 0; i <= nbm; i++) {
+        unsigned long long kk[kBucketSlots];
+        bucket_keys(a, b, kk);
 #pragma unroll
-        for (int j = 0; j < kLineSlots / 2; j++) {
-            v[j] = *gp(q0 + j);
-            v[kLineSlots / 2 + j] = *gp(q1 + j);
-        }
-#pragma unroll
-        for (int j = 0; j < kLineSlots; j++) {
-            kk[2 * j] = ((unsigned long long)v[j].y << 32) | v[j].x;
-            kk[2 * j + 1] = ((unsigned long long)v[j].w << 32) | v[j].z;
-        }
-#pragma unroll
-        for (int j = 0; j < 2 * kLineSlots; j++) {
-            if (j < first) continue;
-            const uint64_t s = j < kLineSlots ? l0 + j : l1 + (j - kLineSlots);
+        for (int j = 0; j < kBucketSlots; j++) {
+            const uint64_t s = b * kBucketSlots + j;
             unsigned long long k = kk[j];
             if (k == 0ull) {
                 k = atomicCAS(&a.keys[s], 0ull, key);
                 if (k == 0ull) {
                     inserted = true;
-                    probes = scanned + (j - first) + 1;
+                    probes = (int64_t)(i * kBucketSlots + j + 1);
                     return (int64_t)s;
                 }
             }
             if (k == key) {
-                probes = scanned + (j - first) + 1;
+                probes = (int64_t)(i * kBucketSlots + j + 1);
                 return (int64_t)s;
             }
         }
-        scanned += 2 * kLineSlots - first;
-        h = (l1 + kLineSlots) & mask;
+        b = (b + step) & nbm;
     }
     probes = a.cap;
     return -1;
 }
 
-// read-only probe: slot of key, or -1
+// read-only probe: slot of key, or -1 (the same sequence; the first empty slot
+// ends it)
 __device__ __forceinline__ int64_t probe_find(const TabArgs &a, unsigned long long key)
 {
-    const uint64_t mask = (uint64_t)a.cap - 1;
-    uint64_t h = splitmix64(key) & mask;
-    for (int64_t i = 0; i < a.cap; i++) {
-        const unsigned long long k = __hip_atomic_load(&a.keys[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (k == key) return (int64_t)h;
-        if (k == 0ull) return -1;
-        h = (h + 1) & mask;
+    if (a.cap < kBucketSlots) {
+        const uint64_t mask = (uint64_t)a.cap - 1;
+        uint64_t h = splitmix64(key) & mask;
+        for (int64_t i = 0; i < a.cap; i++) {
+            const unsigned long long k = __hip_atomic_load(&a.keys[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (k == key) return (int64_t)h;
+            if (k == 0ull) return -1;
+            h = (h + 1) & mask;
+        }
+        return -1;
+    }
+    uint64_t b, step, nbm;
+    bucket_start(a, key, b, step, nbm);
+    for (uint64_t i = 0; i <= nbm; i++) {
+        unsigned long long kk[kBucketSlots];
+        bucket_keys(a, b, kk);
+#pragma unroll
+        for (int j = 0; j < kBucketSlots; j++) {
+            if (kk[j] == key) return (int64_t)(b * kBucketSlots + j);
+            if (kk[j] == 0ull) return -1;
+        }
+        b = (b + step) & nbm;
     }
     return -1;
 }

@@ -150,3 +150,27 @@ def test_table_full_refuses_without_hanging():
     assert s[E.STAT_NAMES.index("table_full")] == 200 - cap
     assert s[E.STAT_NAMES.index("table_inserted")] == cap
     assert np.all(to_np(T.rows[:cap]) == 0)                 # init_std = 0 -> zero rows
+
+
+def test_table_high_load_probing():
+    # 3900 distinct keys in 4096 slots (load 0.95): every probe sequence still
+    # finds its key, distinct keys keep distinct rows, absent keys are not found
+    cap = 1 << 12
+    T = E.KeyedTable(cap, cap, 8, threshold=1, init_std=0.01, device=DEV)
+    rng = np.random.default_rng(77)
+    keys = np.unique(rng.integers(1, 1 << 62, size=4000, dtype=np.int64))[:3900]
+    rng.shuffle(keys)
+    kt = torch.from_numpy(keys).to(DEV)
+    # inserted in two halves, the second probing past the first's keys
+    r1 = to_np(T.lookup_or_insert(kt[:1950]))
+    r2 = to_np(T.lookup_or_insert(kt[1950:]))
+    rows = np.concatenate([r1, r2])
+    assert np.all(rows >= 0) and np.unique(rows).size == keys.size
+    fr, fc = T.find(kt)
+    assert np.array_equal(to_np(fr), rows)
+    assert np.all(to_np(fc) == 1)
+    absent = np.setdiff1d(rng.integers(1, 1 << 62, size=500, dtype=np.int64), keys)
+    ar, _ = T.find(torch.from_numpy(absent).to(DEV))
+    assert np.all(to_np(ar) == E.ROW_DROPPED)
+    gk, gc, gr = (to_np(x) for x in T.export())
+    assert set(gk.tolist()) == set(keys.tolist())
