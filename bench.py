@@ -161,10 +161,10 @@ def run(args):
     krows = torch.empty(n_pool, max_ids, dtype=torch.int32, device=dev) if keyed else None
     kinds = {c.kind for c in w.cols}
 
-    # the keyed table's counters (admissions, a full table) are always kept; the
-    # forward / backward counters only with --stats (their atomics cost time)
+    # device counters only with --stats (their atomics cost time); they are then
+    # reported summed over the timed steps
     tstats = stats if args.stats else None
-    kstats = stats if (args.stats or keyed) else None
+    kstats = stats if args.stats else None
 
     def step(i, ev=None):
         d = dbat[i % len(dbat)]
@@ -281,6 +281,8 @@ def run(args):
                      "algorithmic_bytes": dk["algorithmic_bytes"], "launch_us": dk["launch_us"]},
         "kernels": kernels,
     }
+    if args.stats:
+        out["counters"] = {n: int(v) for n, v in zip(E.STAT_NAMES, st)}
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

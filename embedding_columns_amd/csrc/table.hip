@@ -256,9 +256,16 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
         }
     }
     if (stats) {
-        atomicAdd(&lstat[0], (unsigned long long)ins);
-        atomicAdd(&lstat[1], (unsigned long long)full);
-        atomicMax(&lstat[2], (unsigned long long)probes);
+        // one LDS update per wavefront
+        const int64_t si = wave_sum_i64(ins), sf = wave_sum_i64(full);
+        int64_t mp = probes;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mp = max(mp, (int64_t)__shfl_xor(mp, o, 64));
+        if (lane_id() == 0) {
+            if (si) atomicAdd(&lstat[0], (unsigned long long)si);
+            if (sf) atomicAdd(&lstat[1], (unsigned long long)sf);
+            if (mp) atomicMax(&lstat[2], (unsigned long long)mp);
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < kLdsSlots; i += kCountTile)
