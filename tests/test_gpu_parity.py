@@ -75,6 +75,38 @@ def test_many_tiny_columns_segments_from_keys():
     run_dense_case(w, seed=3014, tile=64, ask_unique=False)
 
 
+@pytest.mark.parametrize("ask_unique", [True, False])
+def test_mixed_dtypes_sgd(ask_unique):
+    # fp32 and bf16 columns in one plan, SGD (bf16 rows rounded to nearest even)
+    w = W.config(2, n_cols=16, batch=300, rows_range=(100, 5000))
+    for c, col in enumerate(w.cols):
+        if c % 2:
+            col.dtype = W.BF16
+    run_dense_case(w, seed=2022, tile=128, ask_unique=ask_unique)
+
+
+@pytest.mark.parametrize("ask_unique", [True, False])
+def test_training_front_end_adagrad_fp32(ask_unique):
+    # Adagrad on fp32 tables (the long-sequence workload has bf16 ones)
+    w = W.config(2, n_cols=12, batch=256, rows_range=(100, 3000), opt=W.OPT_ADAGRAD, lr=0.05,
+                 eps=1e-8)
+    run_dense_case(w, seed=2032, tile=256, ask_unique=ask_unique)
+
+
+def test_bucket_boundaries_beyond_lds():
+    # more boundaries than the LDS stage holds: the search reads them from memory
+    rng = np.random.default_rng(303)
+    bnd = np.sort(rng.normal(size=300).astype(np.float32))
+    cols = [W.Column(W.BUCKET, W.SUM, W.F32, 301, 8, boundaries=bnd),
+            W.Column(W.BUCKET, W.MEAN, W.F32, 301, 16, boundaries=bnd[:200].copy())]
+    lens = rng.integers(0, 6, size=2 * 120)
+    n = int(lens.sum())
+    fv = rng.normal(scale=1.5, size=n).astype(np.float32)
+    fv[::17] = bnd[rng.integers(0, 200, size=fv[::17].size)]      # exact ties
+    w, b = _custom(cols, lens, fvals=fv)
+    _run_custom(w, b, 64)
+
+
 def test_deterministic_across_runs():
     w = W.config(2, n_cols=12, batch=256, rows_range=(50, 2000), opt=W.OPT_EMIT)
     a = run_dense_case(w, seed=5, tile=64)
