@@ -190,7 +190,8 @@ emb_status emb_plan_workspace_view(emb_plan *plan, void *workspace, emb_workspac
 
 /* ------------------------------------------------------------------------
  * Collisionless keyed table (Monolith, Sec. 2.1): open addressing over a
- * power-of-two slot array, linear probing from splitmix64(key) & (capacity-1),
+ * power-of-two slot array (buckets of 16 slots from splitmix64(key), then a
+ * per-key odd stride over the buckets; tables under 16 slots probe slot by slot),
  * insertion by atomic compare-and-swap on the slot key, an occurrence count per
  * slot and a frequency filter: a key gets a row from the row pool once its count
  * reaches `threshold`.  Distinct keys never share a row.  Valid keys are >= 1.
