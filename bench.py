@@ -178,7 +178,12 @@ def run(args):
                       plan.workspace, training, tstats)
         if ev is not None:
             ev[1].record()
-        if training:
+        if training and args.atomic_backward:
+            # the pages' backward (atomic adds, no sort), for comparison
+            if ev is not None:
+                ev[2].record()
+            E.emb_backward_atomic(plan.plan, G, plan.workspace)
+        elif training:
             E.emb_backward_dedup(plan.plan, plan.workspace, None, None, tstats)
             if ev is not None:
                 ev[2].record()
@@ -247,11 +252,13 @@ def run(args):
     apply_avg = float(np.mean(apply_ms))
     kernels = {"fwd_kernel": {"launch_us": round(1000 * fwd_avg, 2), "algorithmic_bytes": int(fb),
                               "gbs": round(fb / (fwd_avg * 1e-3) / 1e9, 1)}}
+    akern = "atomic_apply" if args.atomic_backward else "seg_apply"
     if training:
-        kernels["seg_apply"] = {"launch_us": round(1000 * apply_avg, 2), "algorithmic_bytes": int(ub),
-                                "gbs": round(ub / (apply_avg * 1e-3) / 1e9, 1)}
-        kernels["dedup_sort_unique"] = {"us": round(1000 * float(np.mean(dedup_ms)), 2)}
-    dom = "fwd_kernel" if (not training or fwd_avg >= apply_avg) else "seg_apply"
+        kernels[akern] = {"launch_us": round(1000 * apply_avg, 2), "algorithmic_bytes": int(ub),
+                          "gbs": round(ub / (apply_avg * 1e-3) / 1e9, 1)}
+        if not args.atomic_backward:
+            kernels["dedup_sort_unique"] = {"us": round(1000 * float(np.mean(dedup_ms)), 2)}
+    dom = "fwd_kernel" if (not training or fwd_avg >= apply_avg) else akern
     dk = kernels[dom]
     achieved = dk["gbs"]
     traffic = measured_traffic(dom, w.name)
@@ -272,6 +279,7 @@ def run(args):
                    "positions_per_step": int(np.mean([batches[j].n for j in idx])),
                    "valid_lookups_per_step": int(lookups / args.steps),
                    "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
+                   "backward": ("atomic" if args.atomic_backward else "sorted") if training else "none",
                    "tile": plan.opts.tile or 256, "fwd_launches_per_step": 1},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "fwd_ms": round(fwd_avg, 4),
@@ -336,6 +344,8 @@ def main():
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true", help="collect the device counters while timing")
+    ap.add_argument("--atomic-backward", action="store_true",
+                    help="SGD by atomic scatter (no sort) instead of the sorted segment apply")
     ap.add_argument("--inference", action="store_true", help="forward only (no backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) to scale HBM counters")

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
     "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_backward",
-    "emb_backward_dedup", "emb_backward_apply",
+    "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
     "emb_table_rows", "emb_table_bulk_insert", "emb_table_lookup_or_insert", "emb_table_find",
     "emb_table_export", "emb_last_error", "EmbeddingColumns", "KeyedTable",
@@ -73,6 +73,7 @@ _SIGS = {
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
+    "emb_backward_atomic": [_VP, _VP, _VP, _VP],
     "emb_plan_workspace_view": [_VP, _VP, C.POINTER(WorkspaceView)],
     "emb_table_query": [_I64, _I64, _I32, C.POINTER(C.c_size_t)],
     "emb_table_create": [_I64, _I64, _I32, _I32, _F, _VP, _VP, C.POINTER(_VP)],
@@ -172,6 +173,10 @@ def emb_backward_dedup(plan, workspace, uniq_keys=None, n_uniq=None, stats=None,
 def emb_backward_apply(plan, grad_out, workspace, uniq_grads=None, stream=None):
     _check(lib().emb_backward_apply(plan, _ptr(grad_out), _ptr(workspace), _ptr(uniq_grads),
                                     _stream(stream)))
+
+
+def emb_backward_atomic(plan, grad_out, workspace, stream=None):
+    _check(lib().emb_backward_atomic(plan, _ptr(grad_out), _ptr(workspace), _stream(stream)))
 
 
 def emb_plan_workspace_view(plan, workspace):
@@ -300,6 +305,10 @@ class EmbeddingColumns:
         nu = torch.zeros(1, dtype=torch.int64, device=self.device) if want_count else None
         emb_backward(self.plan, grad_out.contiguous(), self.workspace, keys, grads, nu, stats)
         return keys, grads, nu
+
+    def backward_atomic(self, grad_out):
+        """SGD by atomic scatter of every contribution (no sort; not bit-reproducible)."""
+        emb_backward_atomic(self.plan, grad_out.contiguous(), self.workspace)
 
     def workspace_view(self, n_ids):
         v = emb_plan_workspace_view(self.plan, self.workspace)

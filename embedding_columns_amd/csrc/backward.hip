@@ -1270,6 +1270,102 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
     for (int j = 0; j < nj; j++) bwd_job<OPT>(a, L, t, j);
 }
 
+// ------------------------------------------ atomic scatter (RecIS's backward)
+//
+// The pages' own backward (RecIS Sec. 3.2, Algorithm 1, backward half) sends
+// each contribution w_r G[s(r), :] to its row with atomic adds instead of
+// grouping contributors by a sort.  For SGD the update is linear, so every
+// contribution can be applied to the row directly: E[u] -= lr w_r G[s(r), :].
+// Positions are taken in forward order (so G slices are read nearly in order),
+// 4 per lane group in flight; contributions of the same row within one batch of
+// a group are merged first.  The rounding depends on the order of the atomic
+// adds, so results are not bit-reproducible (they agree within the sum of
+// |terms| bound used for the sorted path).
+struct AtomArgs {
+    const DevCol *cols;
+    int32_t C, B, sumD, T;
+    float lr;
+    int64_t n, ntiles;
+    const float *G;
+    const uint32_t *keys;       // forward: row key per position (>= total_rows: no row)
+    const int32_t *bags;        // forward: bag per position
+    const int32_t *bag_n;
+    const uint32_t *cstart;     // forward: first position of each column [C + 1]
+    uint32_t total_rows;
+};
+
+__global__ __launch_bounds__(kTileBlock, 4) void atomic_apply(AtomArgs a)
+{
+    const int lane = lane_id();
+    const int64_t k = (int64_t)blockIdx.x;
+    if (k >= a.ntiles) return;
+    const int x0 = (int)(k * a.T), x1 = (int)min<int64_t>((k + 1) * a.T, a.n);
+    // the columns of this tile: the last column starting at or before x0, then on
+    int c = (int)wave_upper_bound(a.cstart, (int64_t)a.C + 1, (uint32_t)x0) - 1;
+    int p = x0;
+    while (p < x1) {
+        c = uniform(c);
+        const int cend = min(x1, (int)*gp(a.cstart + c + 1));
+        if (cend <= p) { c++; continue; }
+        const DevCol col = a.cols[c];
+        const int P = col.glanes, lp = __ffs(P) - 1, G = kWave >> lp;
+        const int g = lane >> lp, q = lane & (P - 1);
+        const bool qa = q < col.dim / 4;
+        const int qq = qa ? q : 0;
+        const bool mean = col.pool == EMB_POOL_MEAN;
+        float *w = static_cast<float *>(col.weights);
+        const float *gq = a.G + col.out_off + qq * 4;
+        const int cB = c * a.B;
+        constexpr int U = 4;
+        // group g takes positions p + g, p + g + G, ...: consecutive groups read
+        // consecutive keys and bags
+        for (int b0 = p; b0 < cend; b0 += G * U) {
+            uint32_t key[U];
+            int bag[U], nb[U];
+            float4 x[U];
+#pragma unroll
+            for (int j = 0; j < U; j++) {
+                const int pp = min(b0 + j * G + g, cend - 1);
+                key[j] = b0 + j * G + g < cend ? *gp(a.keys + pp) : a.total_rows;
+                bag[j] = *gp(a.bags + pp);
+            }
+#pragma unroll
+            for (int j = 0; j < U; j++) {
+                nb[j] = mean ? *gp(a.bag_n + bag[j]) : 1;
+                x[j] = *gp(reinterpret_cast<const float4 *>(gq + (int64_t)(bag[j] - cB) * a.sumD));
+            }
+            // merge repeats of one row inside the lane group's batch
+            float s[U][4];
+#pragma unroll
+            for (int j = 0; j < U; j++) {
+                const float wt = (mean ? __builtin_amdgcn_rcpf((float)nb[j]) : 1.0f) * -a.lr;
+                s[j][0] = wt * x[j].x; s[j][1] = wt * x[j].y; s[j][2] = wt * x[j].z; s[j][3] = wt * x[j].w;
+            }
+#pragma unroll
+            for (int j = 1; j < U; j++) {
+#pragma unroll
+                for (int i = 0; i < j; i++) {
+                    if (key[i] == key[j]) {
+#pragma unroll
+                        for (int v = 0; v < 4; v++) { s[i][v] += s[j][v]; s[j][v] = 0.f; }
+                        key[j] = a.total_rows;     // merged: nothing left to send
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < U; j++) {
+                if (qa && key[j] < a.total_rows) {
+                    float *dst = w + (int64_t)(key[j] - col.row_base) * col.dim + q * 4;
+#pragma unroll
+                    for (int v = 0; v < 4; v++) __builtin_amdgcn_global_atomic_fadd_f32(gp(dst + v), s[j][v]);
+                }
+            }
+        }
+        p = cend;
+        c++;
+    }
+}
+
 }  // namespace emb
 
 using namespace emb;
@@ -1429,4 +1525,38 @@ extern "C" emb_status emb_backward(emb_plan *plan, const float *grad_out, void *
     s = emb_backward_dedup(plan, workspace, uniq_keys, n_uniq, stats, stream);
     if (s != EMB_OK) return s;
     return emb_backward_apply(plan, grad_out, workspace, uniq_grads, stream);
+}
+
+extern "C" emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out, void *workspace,
+                                          void *stream)
+{
+    emb_status s = bwd_check(plan, workspace);
+    if (s != EMB_OK) return s;
+    if (plan->opt != EMB_OPT_SGD) return fail(EMB_ERR_UNSUPPORTED, "the atomic backward is for SGD only");
+    for (int32_t c = 0; c < plan->n_cols; c++)
+        if (plan->hcols[c].dtype != EMB_F32) return fail(EMB_ERR_UNSUPPORTED, "the atomic backward needs fp32 tables");
+    if (!grad_out || !aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned device memory");
+    const int64_t n = plan->last_n;
+    if (n == 0) return EMB_OK;
+    char *ws = static_cast<char *>(workspace);
+    AtomArgs a{};
+    a.cols = plan->dcols;
+    a.C = plan->n_cols;
+    a.B = plan->batch;
+    a.sumD = plan->sum_dim;
+    a.T = plan->tile;
+    a.lr = plan->lr;
+    a.n = n;
+    a.ntiles = (n + plan->tile - 1) / plan->tile;
+    a.G = grad_out;
+    a.keys = reinterpret_cast<const uint32_t *>(ws + plan->ws.keys);
+    a.bags = reinterpret_cast<const int32_t *>(ws + plan->ws.bags);
+    a.bag_n = reinterpret_cast<const int32_t *>(ws + plan->ws.bag_n);
+    a.cstart = reinterpret_cast<const uint32_t *>(ws + plan->ws.cstart);
+    a.total_rows = plan->total_rows;
+    hipLaunchKernelGGL(atomic_apply, dim3((unsigned)a.ntiles), dim3(kTileBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("atomic_apply launch: ") + hipGetErrorString(e));
+    return EMB_OK;
 }

@@ -177,6 +177,16 @@ emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32_t *uniq_ke
 emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, void *workspace,
                               float *uniq_grads, void *stream);
 
+/* SGD backward by atomic scatter, the pages' own design (RecIS Sec. 3.2,
+ * Algorithm 1): every contribution -lr w_r grad_out[s(r), off_c:off_c+dim] is
+ * added to its row with fp32 atomic adds, with no sort and no unique-row list
+ * (repeats of a row inside a small batch are merged first).  Needs the SGD
+ * optimizer and fp32 tables (EMB_ERR_UNSUPPORTED otherwise).  The order of the
+ * adds is not fixed, so the updated rows are not bit-reproducible; they agree
+ * with emb_backward within the rounding of the sums.  Kept for comparison with
+ * the sorted path. */
+emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out, void *workspace, void *stream);
+
 /* Device views into a workspace after a training forward (parity checks):
  * keys uint32 [n_ids] (row_base_c + row; sum(rows) for a dropped position,
  * sum(rows)+1 for a DEFAULT one), bags int32 [n_ids] (bag index c*B+s),

@@ -117,3 +117,4 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert "plan" in L.emb_last_error()
     assert L.lib().emb_backward_dedup(None, None, None, None, None, None) == 1
     assert L.lib().emb_backward_apply(None, None, None, None, None) == 1
+    assert L.lib().emb_backward_atomic(None, None, None, None) == 1

@@ -107,6 +107,60 @@ def test_bucket_boundaries_beyond_lds():
     _run_custom(w, b, 64)
 
 
+def _atomic_sgd_case(w, b, seed):
+    """The atomic-scatter SGD backward against the oracle's sorted sums.
+
+    The row ends as E + sum_i t_i (t_i = -lr w_i g_i) added one term at a time in
+    an unknown order.  Recursive fp32 summation of m terms onto E in any order is
+    within (m + 2) u (|E| + sum |t_i|) of the exact sum (u = 2^-24; the extra 2 u
+    cover the rounding of each t_i), on top of the sorted path's tolerance."""
+    wts, sts = W.make_tables(w, seed=seed, device="cpu")
+    G = W.make_grad(w, seed=seed, device="cpu")
+    st = Step(w, b, wts, sts, tile=256)
+    st.forward(training=True)
+    st.cols.backward_atomic(G.to("cuda"))
+    torch.cuda.synchronize()
+    host_w = [to_np(t) for t in wts]
+    oc = oracle_columns(w, [x.copy() for x in host_w])
+    _, _, _, rows = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals)
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
+                                         opt=w.opt, lr=w.lr)
+    from gpu_harness import positions_columns, as_f64
+    _, pcol = positions_columns(b.offsets, len(w.cols), w.batch)
+    for c, col in enumerate(w.cols):
+        sel = ucol == c
+        touched = urow[sel]
+        m = np.bincount(rows[(pcol == c) & (rows >= 0)].astype(np.int64), minlength=col.rows)[touched]
+        before, after, ref = host_w[c], to_np(st.gw[c]), oc.weights[c]
+        untouched = np.setdiff1d(np.arange(col.rows), touched)
+        assert np.array_equal(after[untouched], before[untouched]), "untouched rows changed"
+        e0 = as_f64(col, before[touched])
+        gb = ub[sel][:, :col.dim]
+        tol = (w.lr * 1e-5 * gb + 2.0 ** -22 * (np.abs(ref[touched]) + np.abs(e0))
+               + (m[:, None] + 2) * 2.0 ** -24 * (np.abs(e0) + w.lr * gb) + 1e-30)
+        d = np.abs(as_f64(col, after[touched]) - ref[touched].astype(np.float64))
+        assert np.all(d <= tol), f"rows differ: max {d.max()} tol {tol[d > tol][:3]}"
+
+
+def test_atomic_backward_sgd():
+    # the pages' backward (atomic adds, no sort) on the training front end's shape
+    w = W.config(2, n_cols=24, batch=512, rows_range=(1e2, 1e4))
+    _atomic_sgd_case(w, W.make_batch(w, seed=2042), 2042)
+
+
+def test_atomic_backward_hot_row():
+    # 5000 contributions to one row (mean bags): the unordered fp32 adds stay
+    # inside the tolerance of the sorted sums
+    cols = [W.Column(W.IDENTITY, W.MEAN, W.F32, 50, 32)]
+    lens = [3, 2500, 0, 2500, 1, 4]
+    n = sum(lens)
+    ids = np.full(n, 7, dtype=np.int64)
+    ids[:3] = [1, 2, 7]
+    ids[-5:] = [49, 0, 7, 3, 3]
+    w, b = _custom(cols, lens, ids=ids, opt=W.OPT_SGD, lr=0.01)
+    _atomic_sgd_case(w, b, 12)
+
+
 def test_deterministic_across_runs():
     w = W.config(2, n_cols=12, batch=256, rows_range=(50, 2000), opt=W.OPT_EMIT)
     a = run_dense_case(w, seed=5, tile=64)
