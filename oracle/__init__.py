@@ -39,7 +39,8 @@ class _Col(C.Structure):
     _fields_ = [("kind", C.c_int32), ("pool", C.c_int32), ("dtype", C.c_int32),
                 ("dim", C.c_int32), ("rows", C.c_int64), ("id_lo", C.c_int64),
                 ("id_hi", C.c_int64), ("boundaries", C.c_void_p), ("n_boundaries", C.c_int64),
-                ("weights", C.c_void_p), ("state", C.c_void_p)]
+                ("weights", C.c_void_p), ("state", C.c_void_p), ("seq_max", C.c_int32),
+                ("seq_keep_last", C.c_int32)]
 
 
 _lib = None
@@ -64,9 +65,9 @@ def lib():
         L.oracle_row.restype = C.c_int64
         L.oracle_row.argtypes = [C.POINTER(_Col), C.c_int64, C.c_float, C.c_int32]
         L.oracle_forward.restype = C.c_int64
-        L.oracle_forward.argtypes = [C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 8
+        L.oracle_forward.argtypes = [C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 9
         L.oracle_backward.restype = C.c_int64
-        L.oracle_backward.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 5
+        L.oracle_backward.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 6
                                       + [C.c_int32, C.c_double, C.c_double]
                                       + [C.c_void_p] * 4 + [C.c_int64])
         L.oracle_init_row.argtypes = [C.c_int64, C.c_int32, C.c_double, C.c_void_p]
@@ -154,14 +155,21 @@ class Columns:
                 assert w.dtype == (np.uint16 if c.dtype == 1 else np.float32)
             arr[i] = _Col(c.kind, c.pool, c.dtype, c.dim, c.rows, c.id_lo, c.id_hi,
                           _p(self.bounds[i]), 0 if self.bounds[i] is None else self.bounds[i].size,
-                          _p(w), _p(self.states[i]))
+                          _p(w), _p(self.states[i]), getattr(c, "seq_max", 0),
+                          getattr(c, "seq_keep_last", 0))
         self.arr = arr
         self.sum_dim = int(sum(c.dim for c in cols))
         self.max_dim = int(max(c.dim for c in cols))
 
 
-def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=None):
-    """Returns (Y fp32 [B, sumD], Ybound fp64 [B, sumD], bag_n int32 [C*B], rows int32 [N])."""
+def _mask(mask):
+    return None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+
+
+def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=None, mask=None):
+    """Returns (Y fp32 [B, sumD], Ybound fp64 [B, sumD], bag_n int32 [C*B], rows int32 [N]).
+    mask: uint8 [N] or None (positions with 0 are dropped)."""
+    mask = _mask(mask)
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     n = int(offsets[-1])
     ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int64)
@@ -172,12 +180,12 @@ def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=Non
     bag_n = np.zeros(len(cols.cols) * B, dtype=np.int32)
     rows = np.zeros(max(n, 1), dtype=np.int32)
     lib().oracle_forward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
-                         _p(keyed_rows), _p(Y), _p(Yb), _p(bag_n), _p(rows))
+                         _p(keyed_rows), _p(mask), _p(Y), _p(Yb), _p(bag_n), _p(rows))
     return Y, Yb, bag_n, rows[:n]
 
 
 def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows=None,
-             opt: int = 0, lr: float = 0.0, eps: float = 0.0):
+             opt: int = 0, lr: float = 0.0, eps: float = 0.0, mask=None):
     """Gradient w.r.t. touched rows and the row update `opt` (applied in place to
     cols.weights / cols.states).  Returns (ucol int32 [U], urow int64 [U],
     ugrad fp64 [U, maxD], ubound fp64 [U, maxD])."""
@@ -188,13 +196,14 @@ def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows
     keyed_rows = None if keyed_rows is None else np.ascontiguousarray(keyed_rows, dtype=np.int32)
     G = np.ascontiguousarray(G, dtype=np.float32)
     assert G.shape == (B, cols.sum_dim)
+    mask = _mask(mask)
     cap = max(n, 1)
     ucol = np.zeros(cap, dtype=np.int32)
     urow = np.zeros(cap, dtype=np.int64)
     ug = np.zeros((cap, cols.max_dim), dtype=np.float64)
     ub = np.zeros((cap, cols.max_dim), dtype=np.float64)
     U = lib().oracle_backward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
-                              _p(keyed_rows), _p(G), opt, lr, eps, _p(ucol), _p(urow), _p(ug),
+                              _p(keyed_rows), _p(mask), _p(G), opt, lr, eps, _p(ucol), _p(urow), _p(ug),
                               _p(ub), cap)
     assert U >= 0
     return ucol[:U], urow[:U], ug[:U], ub[:U]

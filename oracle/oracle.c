@@ -51,6 +51,8 @@ typedef struct {
     int64_t n_boundaries;
     void *weights;  /* [rows, dim], fp32 or bf16 (raw uint16 bits) */
     float *state;   /* Adagrad accumulator [rows, dim] fp32, or NULL */
+    int32_t seq_max;        /* SeqTrunc: keep at most this many positions per bag (0 = all) */
+    int32_t seq_keep_last;  /* ... the last seq_max (1) or the first seq_max (0) */
 } oracle_col;
 
 /* ---------------------------------------------------------------- hashing */
@@ -169,6 +171,25 @@ static int64_t position_row(const oracle_col *col, int64_t p, const int64_t *ids
                       keyed_rows ? keyed_rows[p] : ROW_DROPPED);
 }
 
+/* Sequence truncation and masking (RecIS Sec. 3.1 and Figure 2, where SeqTrunc and
+ * masking are two of the per-field transformations, SeqTrunc ordered before Hash).
+ * Both act on the raw positions before the transform: position p of the bag
+ * [start, end) survives iff its
+ * mask byte is nonzero (no mask: all survive) and, when the column truncates,
+ * its index in the bag is among the first seq_max (or the last seq_max).  A
+ * position that does not survive is dropped: no row, not counted in a mean. */
+static int position_kept(const oracle_col *col, int64_t p, int64_t start, int64_t end,
+                         const uint8_t *mask)
+{
+    if (mask && mask[p] == 0) return 0;
+    if (col->seq_max > 0) {
+        int64_t i = p - start, len = end - start;
+        if (col->seq_keep_last) return i >= len - col->seq_max;
+        return i < col->seq_max;
+    }
+    return 1;
+}
+
 /* ---------------------------------------------------------------- forward */
 
 /*
@@ -180,7 +201,8 @@ static int64_t position_row(const oracle_col *col, int64_t p, const int64_t *ids
  */
 int64_t oracle_forward(const oracle_col *cols, int32_t C, int32_t B, const int32_t *offsets,
                        const int64_t *ids, const float *fvals, const int32_t *keyed_rows,
-                       float *Y, double *Ybound, int32_t *bag_n, int32_t *rows)
+                       const uint8_t *mask, float *Y, double *Ybound, int32_t *bag_n,
+                       int32_t *rows)
 {
     int64_t sumD = 0;
     for (int32_t c = 0; c < C; c++) sumD += cols[c].dim;
@@ -196,7 +218,8 @@ int64_t oracle_forward(const oracle_col *cols, int32_t C, int32_t B, const int32
             memset(acc, 0, sizeof(double) * D);
             memset(mag, 0, sizeof(double) * D);
             for (int64_t p = offsets[b]; p < offsets[b + 1]; p++) {
-                int64_t r = position_row(col, p, ids, fvals, keyed_rows);
+                int64_t r = position_kept(col, p, offsets[b], offsets[b + 1], mask)
+                                ? position_row(col, p, ids, fvals, keyed_rows) : ROW_DROPPED;
                 if (rows) rows[p] = (int32_t)r;
                 if (r == ROW_DROPPED) continue;
                 n++;
@@ -258,7 +281,7 @@ double oracle_adagrad_elem(double e, double a, double g, double lr, double eps, 
  */
 int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int32_t *offsets,
                         const int64_t *ids, const float *fvals, const int32_t *keyed_rows,
-                        const float *G, int32_t opt, double lr, double eps,
+                        const uint8_t *mask, const float *G, int32_t opt, double lr, double eps,
                         int32_t *uniq_col, int64_t *uniq_row, double *uniq_grad,
                         double *uniq_bound, int64_t max_uniq)
 {
@@ -280,7 +303,8 @@ int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int3
         for (int32_t s = 0; s < B; s++) {
             int64_t b = (int64_t)c * B + s;
             for (int64_t p = offsets[b]; p < offsets[b + 1]; p++) {
-                int64_t r = position_row(col, p, ids, fvals, keyed_rows);
+                int64_t r = position_kept(col, p, offsets[b], offsets[b + 1], mask)
+                                ? position_row(col, p, ids, fvals, keyed_rows) : ROW_DROPPED;
                 bag_of_pos[p - a] = s;
                 if (r == ROW_DROPPED) continue;
                 n_of_bag[s]++;

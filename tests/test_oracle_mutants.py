@@ -29,6 +29,10 @@ MUTANTS = {
     "adagrad-eps-inside": ("return e - lr * g / (sqrt(a2) + eps);", "return e - lr * g / sqrt(a2 + eps);"),
     "bf16-truncate": ("r = ldexp(rint(ldexp(m, 8)), e - 8);", "r = ldexp(floor(ldexp(m, 8)), e - 8);"),
     "init-shift": ("(double)(z >> 40), -24)", "(double)(z >> 41), -24)"),
+    "trunc-last-off-by-one": ("return i >= len - col->seq_max;", "return i > len - col->seq_max;"),
+    "trunc-first-inclusive": ("return i < col->seq_max;", "return i <= col->seq_max;"),
+    "trunc-ends-swapped": ("if (col->seq_keep_last) return", "if (!col->seq_keep_last) return"),
+    "mask-ignored": ("if (mask && mask[p] == 0) return 0;", "if (mask && mask[p] == 2) return 0;"),
 }
 
 

@@ -288,6 +288,82 @@ def test_reduce_id_worked_example():
         assert rebuilt == sorted(ids.tolist())
 
 
+# ------------------------------------------------- truncation and masking
+
+def _kept_positions(B, offsets, seq, mask):
+    """Brute force: the raw positions that survive a per-column (seq_max, keep_last)
+    truncation and a per-position mask, listed bag by bag."""
+    keep = np.zeros(int(offsets[-1]), bool)
+    for b in range(len(offsets) - 1):
+        seq_max, last = seq[b // B]
+        a, e = int(offsets[b]), int(offsets[b + 1])
+        idx = list(range(a, e))
+        if seq_max > 0:
+            idx = idx[-seq_max:] if last else idx[:seq_max]
+        for p in idx:
+            keep[p] = mask is None or mask[p] != 0
+    return keep
+
+
+def _sliced(B, offsets, keep, *arrays):
+    """The same batch with the non-surviving positions removed (new offsets)."""
+    kept_before = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
+    return (kept_before[offsets],) + tuple(None if x is None else x[keep] for x in arrays)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("use_mask", [False, True])
+def test_truncation_and_mask_equal_the_sliced_batch(seed, use_mask):
+    """A truncated / masked batch pools and trains exactly like the batch with the
+    dropped positions cut out; the kept set is listed by brute force."""
+    rng = np.random.default_rng(700 + seed)
+    cols, B, off, ids, fv, weights = _tiny_case(rng, kinds=(W.HASH, W.IDENTITY, W.BUCKET, W.KEYED),
+                                                C=5, max_len=9)
+    seq = [(0, 0), (3, 0), (3, 1), (1, 1), (2, 0)]
+    for col, (m, last) in zip(cols, seq):
+        col.seq_max, col.seq_keep_last = m, last
+    N = int(off[-1])
+    keyed = rng.choice([-2, -1, 0, 1, 2], size=N).astype(np.int32)
+    mask = (rng.random(N) < 0.7).astype(np.uint8) if use_mask else None
+    keep = _kept_positions(B, off, seq, mask)
+    off2, ids2, fv2, keyed2 = _sliced(B, off, keep, ids, fv, keyed)
+    plain = [W.Column(c.kind, c.pool, c.dtype, c.rows, c.dim, c.id_lo, c.id_hi, c.boundaries)
+             for c in cols]
+
+    Y, Yb, n, rows = oracle.forward(oracle.Columns(cols, weights), B, off, ids, fv, keyed, mask)
+    Y2, Yb2, n2, rows2 = oracle.forward(oracle.Columns(plain, weights), B, off2, ids2, fv2, keyed2)
+    assert np.array_equal(Y, Y2) and np.array_equal(Yb, Yb2) and np.array_equal(n, n2)
+    assert np.all(rows[~keep] == oracle.ROW_DROPPED) and np.array_equal(rows[keep], rows2)
+
+    G = rng.normal(size=Y.shape).astype(np.float32)
+    wa, wb = [w.copy() for w in weights], [w.copy() for w in weights]
+    ca, cb = oracle.Columns(cols, wa), oracle.Columns(plain, wb)
+    ra = oracle.backward(ca, B, off, G, ids, fv, keyed, opt=W.OPT_SGD, lr=0.1, mask=mask)
+    rb = oracle.backward(cb, B, off2, G, ids2, fv2, keyed2, opt=W.OPT_SGD, lr=0.1)
+    for x, y in zip(ra, rb):
+        assert np.array_equal(x, y)
+    for x, y in zip(wa, wb):
+        assert np.array_equal(x, y)
+
+
+def test_truncation_keeps_first_or_last_closed_form():
+    """Bag [0..9] of an IDENTITY sum column: keeping the first 3 sums rows 0..2, the
+    last 3 sums rows 7..9, a limit above the length keeps all 10; a mask that zeroes
+    the even positions halves what is left."""
+    Wt = np.eye(10, 4, dtype=np.float32) + np.arange(10, dtype=np.float32)[:, None]
+    off = np.array([0, 10], dtype=np.int32)
+    ids = np.arange(10, dtype=np.int64)
+    for m, last, want in [(3, 0, [0, 1, 2]), (3, 1, [7, 8, 9]), (12, 1, list(range(10))),
+                          (0, 0, list(range(10)))]:
+        col = W.Column(W.IDENTITY, W.SUM, W.F32, 10, 4, seq_max=m, seq_keep_last=last)
+        Y, _, n, _ = oracle.forward(oracle.Columns([col], [Wt]), 1, off, ids)
+        assert n[0] == len(want) and np.array_equal(Y[0], Wt[want].sum(axis=0))
+        odd = (np.arange(10) % 2).astype(np.uint8)
+        Y, _, n, _ = oracle.forward(oracle.Columns([col], [Wt]), 1, off, ids, mask=odd)
+        got = [i for i in want if i % 2]
+        assert n[0] == len(got) and np.array_equal(Y[0], Wt[got].sum(axis=0))
+
+
 # ------------------------------------------------------------ optimizers
 
 @pytest.mark.parametrize("opt,big_eps", [(W.OPT_SGD, False), (W.OPT_ADAGRAD, False),

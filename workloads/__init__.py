@@ -46,6 +46,8 @@ class Column:
     id_lo: int = 0
     id_hi: int = 0
     boundaries: Optional[np.ndarray] = None  # fp32, sorted, BUCKET only
+    seq_max: int = 0                         # SeqTrunc: keep at most this many positions per bag
+    seq_keep_last: int = 0                   # keep the last seq_max (1) or the first (0)
 
 
 @dataclass
