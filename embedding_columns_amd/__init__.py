@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
-    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_backward",
+    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_masked",
+    "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
     "emb_table_rows", "emb_table_bulk_insert", "emb_table_lookup_or_insert", "emb_table_find",
@@ -31,7 +32,7 @@ OPT_EMIT, OPT_SGD, OPT_ADAGRAD = 0, 1, 2
 ROW_DROPPED, ROW_DEFAULT = -1, -2
 STAT_COUNT = 16
 STAT_NAMES = ["ids", "valid", "dropped", "default", "zero_bags", "unique", "table_inserted",
-              "table_admitted", "table_full", "max_probe"]
+              "table_admitted", "table_full", "max_probe", "filtered"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -50,7 +51,8 @@ class ColumnDesc(C.Structure):
     _fields_ = [("kind", C.c_int32), ("pool", C.c_int32), ("dtype", C.c_int32), ("dim", C.c_int32),
                 ("rows", C.c_int64), ("id_lo", C.c_int64), ("id_hi", C.c_int64),
                 ("boundaries", C.c_void_p), ("n_boundaries", C.c_int64),
-                ("weights", C.c_void_p), ("opt_state", C.c_void_p)]
+                ("weights", C.c_void_p), ("opt_state", C.c_void_p), ("seq_max", C.c_int32),
+                ("seq_keep_last", C.c_int32)]
 
 
 class PlanOpts(C.Structure):
@@ -70,6 +72,7 @@ _SIGS = {
                         C.POINTER(_VP)],
     "emb_plan_destroy": [_VP],
     "emb_forward": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
+    "emb_forward_masked": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
@@ -159,6 +162,13 @@ def emb_forward(plan, offsets, ids, fvals, keyed_rows, n_ids, out, workspace, tr
                              _stream(stream)))
 
 
+def emb_forward_masked(plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out, workspace,
+                       training, stats=None, stream=None):
+    _check(lib().emb_forward_masked(plan, _ptr(offsets), _ptr(ids), _ptr(fvals), _ptr(keyed_rows),
+                                    _ptr(mask), n_ids, _ptr(out), _ptr(workspace),
+                                    1 if training else 0, _ptr(stats), _stream(stream)))
+
+
 def emb_backward(plan, grad_out, workspace, uniq_keys=None, uniq_grads=None, n_uniq=None,
                  stats=None, stream=None):
     _check(lib().emb_backward(plan, _ptr(grad_out), _ptr(workspace), _ptr(uniq_keys),
@@ -237,7 +247,7 @@ class EmbeddingColumns:
     """A plan over columns with caller-owned tables (torch tensors on the GPU).
 
     cols: objects with kind, pool, dtype, rows, dim, id_lo, id_hi and optional
-    boundaries (fp32 array-like); weights[c]: [rows, dim] fp32/bf16 tensor (for a
+    boundaries (fp32 array-like), seq_max and seq_keep_last; weights[c]: [rows, dim] fp32/bf16 tensor (for a
     KEYED column, the table's row pool); states[c]: fp32 Adagrad accumulator."""
 
     def __init__(self, cols, weights, states=None, batch=1, max_ids=0, opt=OPT_EMIT, lr=0.0,
@@ -259,7 +269,8 @@ class EmbeddingColumns:
             descs[i] = ColumnDesc(c.kind, c.pool, c.dtype, c.dim, c.rows, getattr(c, "id_lo", 0),
                                   getattr(c, "id_hi", 0), _ptr(bt) if bt is not None else None,
                                   0 if bt is None else bt.numel(), _ptr(w),
-                                  _ptr(s) if s is not None else None)
+                                  _ptr(s) if s is not None else None, getattr(c, "seq_max", 0),
+                                  getattr(c, "seq_keep_last", 0))
         self.descs = descs
         self.opts = PlanOpts(opt, lr, eps, tile)
         self.sum_dim = sum(c.dim for c in self.cols)
@@ -284,13 +295,19 @@ class EmbeddingColumns:
             self.plan = None
 
     def forward(self, offsets, ids=None, fvals=None, keyed_rows=None, training=True, stats=None,
-                out=None):
+                out=None, mask=None):
+        """mask: uint8 [n_ids] device tensor (0 removes a position) or None."""
         n = (ids if ids is not None else fvals if fvals is not None else keyed_rows)
         n_ids = 0 if n is None else n.numel()
         if out is None:
             out = torch.empty(self.batch, self.sum_dim, dtype=torch.float32, device=self.device)
-        emb_forward(self.plan, offsets, ids, fvals, keyed_rows, n_ids, out, self.workspace,
-                    training, stats)
+        if mask is None:
+            emb_forward(self.plan, offsets, ids, fvals, keyed_rows, n_ids, out, self.workspace,
+                        training, stats)
+        else:
+            assert mask.dtype == torch.uint8 and mask.numel() >= n_ids
+            emb_forward_masked(self.plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out,
+                               self.workspace, training, stats)
         self._n = n_ids
         return out
 

@@ -38,6 +38,7 @@ struct FwdArgs {
     const int64_t *ids;
     const float *fvals;
     const int32_t *krows;
+    const uint8_t *mask;     // per-position keep byte, or NULL
     float *Y;
     uint32_t *keys;
     int32_t *bags;
@@ -370,9 +371,28 @@ struct TileIn {
     int32_t kr[kPL];
 };
 
+// Sequence truncation and masking remove raw positions before the transform
+// (RecIS Sec. 3.1 / Figure 2: SeqTrunc precedes Hash).  A removed position
+// becomes a dropped one (-1): no row, not counted in a mean, no gradient.
+__device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L,
+                                              const TileCtx &t, const DevCol &col, int p)
+{
+    bool keep = true;
+    if (a.mask) keep = *gp(a.mask + p) != 0;
+    if (col.seq_max > 0) {
+        const int b = bag_of<false>(a, L, t, p);
+        const int bs = offat(a, L, t, b), be = offat(a, L, t, b + 1);
+        const int j = p - bs;
+        keep = keep && (col.seq_keep_last ? j >= be - bs - col.seq_max : j < col.seq_max);
+    }
+    return keep;
+}
+
+// FILTER: the column is truncated or the call has a mask
+template <bool FILTER>
 __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
-                                              const TileIn &in, int32_t (&cnt)[4])
+                                              const TileIn &in, int32_t (&cnt)[5])
 {
     const int lane = lane_id();
     const int nbd = col.n_bnd;
@@ -402,10 +422,14 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
             const int kr = in.kr[i];
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
+        // removed positions are counted apart from the transform's drops
+        const bool removed = FILTER && !position_kept(a, L, t, col, p);
+        cnt[2] += (r == -1 && !removed);
+        cnt[4] += removed;
+        if (removed) r = -1;
         L.rows[p - t.t0] = r;
         cnt[0] += 1;
         cnt[1] += (r >= 0);
-        cnt[2] += (r == -1);
         cnt[3] += (r == -2);
         if (a.training)
             *gp(a.keys + p) = r >= 0 ? col.row_base + (uint32_t)r
@@ -431,6 +455,9 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const 
     return min(t.t1, win ? offw<true>(a, L, t, (c + 1) * a.B) : offat(a, L, t, (c + 1) * a.B));
 }
 
+// FILTER: some column truncates or the call has a mask (a separate instance, so
+// that the plain forward carries none of that code)
+template <bool FILTER>
 __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 {
     __shared__ WaveLds lds[kTileWaves];
@@ -538,7 +565,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         if (last && lane == 0) *gp(a.cstart + a.C) = (uint32_t)N;
     }
 
-    int32_t cnt[4] = {0, 0, 0, 0};   // per lane: at most kPL positions, kWave bags
+    int32_t cnt[5] = {0, 0, 0, 0, 0};   // per lane: at most kPL positions, kWave bags
     int32_t zero_bags = 0;
     if (t.t0 < t.t1) {
         const int c_first = t.bf / a.B, c_last = t.bl / a.B;
@@ -553,7 +580,9 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            fwd_transform(a, L, t, col, s0, s1, in, cnt);
+            if (FILTER && (a.mask || col.seq_max > 0))
+                fwd_transform<true>(a, L, t, col, s0, s1, in, cnt);
+            else fwd_transform<false>(a, L, t, col, s0, s1, in, cnt);
         }
         for (int c = c_first; c <= c_last; c++) {
             const int cu = uniform(c);
@@ -612,13 +641,14 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     if (a.stats) {
         const int64_t s0 = wave_sum_i64(cnt[0]), s1 = wave_sum_i64(cnt[1]);
         const int64_t s2 = wave_sum_i64(cnt[2]), s3 = wave_sum_i64(cnt[3]);
-        const int64_t s4 = wave_sum_i64(zero_bags);
+        const int64_t s4 = wave_sum_i64(zero_bags), s5 = wave_sum_i64(cnt[4]);
         if (lane == 0) {
             if (s0) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_IDS], (unsigned long long)s0);
             if (s1) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_VALID], (unsigned long long)s1);
             if (s2) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_DROPPED], (unsigned long long)s2);
             if (s3) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_DEFAULT], (unsigned long long)s3);
             if (s4) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_ZERO_BAGS], (unsigned long long)s4);
+            if (s5) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_FILTERED], (unsigned long long)s5);
         }
     }
 }
@@ -627,10 +657,10 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 
 using namespace emb;
 
-extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
-                                  const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
-                                  float *out, void *workspace, int32_t training, int64_t *stats,
-                                  void *stream)
+static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                               const float *fvals, const int32_t *keyed_rows, const uint8_t *mask,
+                               int64_t n_ids, float *out, void *workspace, int32_t training,
+                               int64_t *stats, void *stream)
 {
     if (!plan) return fail(EMB_ERR_INVALID_ARG, "plan is NULL");
     if (!offsets || !out || !workspace) return fail(EMB_ERR_INVALID_ARG, "offsets, out and workspace are required");
@@ -656,6 +686,7 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     a.ids = ids;
     a.fvals = fvals;
     a.krows = keyed_rows;
+    a.mask = mask;
     a.Y = out;
     a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
     a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
@@ -669,9 +700,32 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
     if (training) plan->last_n = n_ids;
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
-    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                       static_cast<hipStream_t>(stream), a);
+    if (mask || plan->has_trunc)
+        hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           static_cast<hipStream_t>(stream), a);
+    else
+        hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           static_cast<hipStream_t>(stream), a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));
     return EMB_OK;
+}
+
+extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                  const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
+                                  float *out, void *workspace, int32_t training, int64_t *stats,
+                                  void *stream)
+{
+    return forward_impl(plan, offsets, ids, fvals, keyed_rows, nullptr, n_ids, out, workspace,
+                        training, stats, stream);
+}
+
+extern "C" emb_status emb_forward_masked(emb_plan *plan, const int32_t *offsets,
+                                         const int64_t *ids, const float *fvals,
+                                         const int32_t *keyed_rows, const uint8_t *mask,
+                                         int64_t n_ids, float *out, void *workspace,
+                                         int32_t training, int64_t *stats, void *stream)
+{
+    return forward_impl(plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out, workspace,
+                        training, stats, stream);
 }

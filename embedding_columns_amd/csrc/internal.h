@@ -50,8 +50,10 @@ struct DevCol {
     int32_t lanes;           // lanes per row, 4 elements each: pow2 >= dim / 4
     int32_t vec;             // elements per lane (4)
     int32_t glanes;          // lanes per gradient row (same as lanes)
+    int32_t seq_max;         // keep at most this many positions per bag (0: all)
+    int32_t seq_keep_last;   // ... the last seq_max (1) or the first (0)
 };
-static_assert(sizeof(DevCol) == 96, "DevCol layout");
+static_assert(sizeof(DevCol) == 104, "DevCol layout");
 static_assert(kOffCap % kWave == 0, "window loads are unrolled per lane");
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
@@ -81,6 +83,7 @@ struct emb_plan {
     int64_t sort_blocks = 0;       // radix blocks of the largest batch
     int64_t uq_blocks = 0;         // unique-row blocks of the largest batch
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
+    bool has_trunc = false;        // some column truncates its bags
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
     bool seg_from_keys = false;    // the last dedup skipped the unique list (see emb_backward_dedup)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata

@@ -76,6 +76,9 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
             if (d.rows < d.n_boundaries + 1) return fail(EMB_ERR_INVALID_ARG, at + "rows must be >= n_boundaries + 1");
             if (d.n_boundaries > (int64_t(1) << 30)) return fail(EMB_ERR_UNSUPPORTED, at + "too many boundaries");
         }
+        if (d.seq_max < 0) return fail(EMB_ERR_INVALID_ARG, at + "seq_max must be >= 0");
+        if (d.seq_keep_last != 0 && d.seq_keep_last != 1)
+            return fail(EMB_ERR_INVALID_ARG, at + "seq_keep_last must be 0 or 1");
         if (!d.weights) return fail(EMB_ERR_INVALID_ARG, at + "weights is NULL");
         if (!aligned(d.weights, 16)) return fail(EMB_ERR_INVALID_ARG, at + "weights must be 16-byte aligned");
         if (opts->opt == EMB_OPT_ADAGRAD && (!d.opt_state || !aligned(d.opt_state, 16)))
@@ -171,6 +174,8 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         h.vec = 4;
         h.lanes = pow2_ceil(d.dim / 4);
         h.glanes = pow2_ceil(d.dim / 4);
+        h.seq_max = d.seq_max;
+        h.seq_keep_last = d.seq_keep_last;
         row_base += (uint64_t)d.rows;
         off += d.dim;
         maxd = std::max(maxd, d.dim);
@@ -178,6 +183,7 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         P.has_bucket |= d.kind == EMB_COL_BUCKET;
         P.has_keyed |= d.kind == EMB_COL_KEYED;
         P.any_mean |= d.pool == EMB_POOL_MEAN;
+        P.has_trunc |= d.seq_max > 0;
     }
     P.total_rows = (uint32_t)row_base;
     P.hrow_base = new (std::nothrow) uint32_t[n_cols + 1];

@@ -85,6 +85,7 @@ typedef enum {
 #define EMB_STAT_TABLE_ADMITTED 7  /* keys that received a row (admission)           */
 #define EMB_STAT_TABLE_FULL     8  /* key occurrences refused: no free slot or row   */
 #define EMB_STAT_MAX_PROBE      9  /* longest probe sequence seen (max, not sum)     */
+#define EMB_STAT_FILTERED      10  /* positions removed by sequence truncation or the mask */
 #define EMB_STAT_COUNT         16
 
 /* One embedding column (host struct), in output order.  Row-major tables. */
@@ -99,6 +100,13 @@ typedef struct emb_column_desc {
     int64_t n_boundaries;      /* BUCKET: rows >= n_boundaries + 1                      */
     void *weights;             /* device [rows, dim] in dtype; updated in place by emb_backward */
     float *opt_state;          /* ADAGRAD: device fp32 [rows, dim], zero before the first step  */
+    int32_t seq_max;           /* sequence truncation: keep at most seq_max positions of  */
+                               /* each bag (0 = keep all), counted on the raw positions   */
+                               /* before the transform (RecIS Sec. 3.1 and Figure 2:      */
+                               /* SeqTrunc is a per-field step ordered before Hash)      */
+    int32_t seq_keep_last;     /* 1: keep a bag's last seq_max positions, 0: its first. */
+                               /* KEYED: the table lookup before the forward still sees */
+                               /* (and counts) every key; truncation acts on pooling.   */
 } emb_column_desc;
 
 typedef struct emb_plan_opts {
@@ -146,6 +154,23 @@ emb_status emb_plan_destroy(emb_plan *plan);
 emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
                        const float *fvals, const int32_t *keyed_rows, int64_t n_ids, float *out,
                        void *workspace, int32_t training, int64_t *stats, void *stream);
+
+/*
+ * emb_forward with a per-position mask (masking, one of the per-field
+ * transformations of RecIS Sec. 3.1 / Figure 2; the pages give no detail, so a
+ * mask here is one byte per position).
+ *   mask     uint8 [n_ids]: a position whose byte is 0 is removed before the
+ *            transform, like a truncated one: it reads no row, does not count in a
+ *            mean and gets no gradient.  Nonzero keeps it.  NULL = emb_forward.
+ * A position survives iff the mask keeps it AND its column's truncation keeps it
+ * (both look at raw positions, so their order does not matter).  The matching
+ * emb_backward needs no mask: the forward records the removed positions.
+ * Arguments, layout, ownership and errors otherwise as emb_forward.
+ */
+emb_status emb_forward_masked(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                              const float *fvals, const int32_t *keyed_rows, const uint8_t *mask,
+                              int64_t n_ids, float *out, void *workspace, int32_t training,
+                              int64_t *stats, void *stream);
 
 /*
  * Backward of the last training forward on this workspace: deduplicates the

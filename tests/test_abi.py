@@ -61,7 +61,7 @@ def _query(L, cols, batch=8, max_ids=100, opt=0, lr=0.0, eps=0.0, tile=0):
 def test_plan_query_accepts_a_valid_plan(L):
     s, pb, wb, _ = _query(L, [_col(L), _col(L, kind=L.BUCKET, boundaries=8192, n_boundaries=64,
                                           rows=65, dim=4)])
-    assert s == 0 and pb >= 2 * 96 and wb > 0
+    assert s == 0 and pb >= 2 * 104 and wb > 0
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -79,6 +79,8 @@ def test_plan_query_accepts_a_valid_plan(L):
     (dict(kind=2, boundaries=8192, n_boundaries=64, rows=64), 1, "n_boundaries + 1"),
     (dict(kind=2, boundaries=None, n_boundaries=3, rows=64), 1, "boundaries"),
     (dict(kind=3, dtype=1, dim=16), 2, "fp32"),
+    (dict(seq_max=-1), 1, "seq_max"),
+    (dict(seq_max=4, seq_keep_last=2), 1, "seq_keep_last"),
 ])
 def test_plan_query_rejects_bad_columns(L, kw, status, msg):
     s, _, _, err = _query(L, [_col(L), _col(L, **kw)])
@@ -118,3 +120,5 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_backward_dedup(None, None, None, None, None, None) == 1
     assert L.lib().emb_backward_apply(None, None, None, None, None) == 1
     assert L.lib().emb_backward_atomic(None, None, None, None) == 1
+    assert L.lib().emb_forward_masked(None, None, None, None, None, None, 0, None, None, 0, None,
+                                      None) == 1

@@ -316,6 +316,12 @@ def make_batch(w: Workload, seed: int) -> Batch:
     return Batch(offsets.astype(np.int32), ids, fvals, invalid, forced, N)
 
 
+def make_mask(n: int, seed: int, keep: float = 0.8) -> np.ndarray:
+    """A per-position keep mask, uint8 [n]: 1 with probability `keep`, else 0."""
+    rng = np.random.default_rng(seed + 7919)
+    return (rng.random(n) < keep).astype(np.uint8)
+
+
 def make_tables(w: Workload, seed: int, device="cpu"):
     """Per-column weight tensors ~ N(0, init_std) (bf16 columns rounded from fp32)
     and zeroed fp32 Adagrad accumulators.  Drawn with torch's generator on
