@@ -65,9 +65,9 @@ def lib():
         L.oracle_row.restype = C.c_int64
         L.oracle_row.argtypes = [C.POINTER(_Col), C.c_int64, C.c_float, C.c_int32]
         L.oracle_forward.restype = C.c_int64
-        L.oracle_forward.argtypes = [C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 9
+        L.oracle_forward.argtypes = [C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 10
         L.oracle_backward.restype = C.c_int64
-        L.oracle_backward.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 6
+        L.oracle_backward.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 7
                                       + [C.c_int32, C.c_double, C.c_double]
                                       + [C.c_void_p] * 4 + [C.c_int64])
         L.oracle_init_row.argtypes = [C.c_int64, C.c_int32, C.c_double, C.c_void_p]
@@ -166,10 +166,16 @@ def _mask(mask):
     return None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
 
 
-def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=None, mask=None):
+def _pw(pweights):
+    return None if pweights is None else np.ascontiguousarray(pweights, dtype=np.float32)
+
+
+def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=None, mask=None,
+            pweights=None):
     """Returns (Y fp32 [B, sumD], Ybound fp64 [B, sumD], bag_n int32 [C*B], rows int32 [N]).
-    mask: uint8 [N] or None (positions with 0 are dropped)."""
-    mask = _mask(mask)
+    mask: uint8 [N] or None (positions with 0 are dropped); pweights: fp32 [N]
+    per-position weights or None (all 1)."""
+    mask, pweights = _mask(mask), _pw(pweights)
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     n = int(offsets[-1])
     ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int64)
@@ -180,12 +186,13 @@ def forward(cols: Columns, B: int, offsets, ids=None, fvals=None, keyed_rows=Non
     bag_n = np.zeros(len(cols.cols) * B, dtype=np.int32)
     rows = np.zeros(max(n, 1), dtype=np.int32)
     lib().oracle_forward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
-                         _p(keyed_rows), _p(mask), _p(Y), _p(Yb), _p(bag_n), _p(rows))
+                         _p(keyed_rows), _p(mask), _p(pweights), _p(Y), _p(Yb), _p(bag_n),
+                         _p(rows))
     return Y, Yb, bag_n, rows[:n]
 
 
 def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows=None,
-             opt: int = 0, lr: float = 0.0, eps: float = 0.0, mask=None):
+             opt: int = 0, lr: float = 0.0, eps: float = 0.0, mask=None, pweights=None):
     """Gradient w.r.t. touched rows and the row update `opt` (applied in place to
     cols.weights / cols.states).  Returns (ucol int32 [U], urow int64 [U],
     ugrad fp64 [U, maxD], ubound fp64 [U, maxD])."""
@@ -196,14 +203,15 @@ def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows
     keyed_rows = None if keyed_rows is None else np.ascontiguousarray(keyed_rows, dtype=np.int32)
     G = np.ascontiguousarray(G, dtype=np.float32)
     assert G.shape == (B, cols.sum_dim)
-    mask = _mask(mask)
+    mask, pweights = _mask(mask), _pw(pweights)
     cap = max(n, 1)
     ucol = np.zeros(cap, dtype=np.int32)
     urow = np.zeros(cap, dtype=np.int64)
     ug = np.zeros((cap, cols.max_dim), dtype=np.float64)
     ub = np.zeros((cap, cols.max_dim), dtype=np.float64)
     U = lib().oracle_backward(cols.arr, len(cols.cols), B, _p(offsets), _p(ids), _p(fvals),
-                              _p(keyed_rows), _p(mask), _p(G), opt, lr, eps, _p(ucol), _p(urow), _p(ug),
+                              _p(keyed_rows), _p(mask), _p(pweights), _p(G), opt, lr, eps,
+                              _p(ucol), _p(urow), _p(ug),
                               _p(ub), cap)
     assert U >= 0
     return ucol[:U], urow[:U], ug[:U], ub[:U]

@@ -17,8 +17,10 @@
  *              KEYED     row handed in by the keyed-table step (or DEFAULT / dropped)
  *   forward    Y[s, p] = sum over the bag's valid positions r of w_r * E[i_r, p]
  *              (RecIS Sec. 3.2 "Index-aware segment reduction", Algorithm 1,
- *              forward half); w_r = 1 (sum) or 1/n (mean), n = valid positions
- *              including DEFAULT ones; an empty bag gives the zero vector.
+ *              forward half); w_r = v_r (sum) or v_r / n (mean), with v_r the
+ *              caller's per-position weight (1 when none is given) and n the
+ *              valid positions including DEFAULT ones; an empty bag gives the
+ *              zero vector.
  *   backward   dE[u] = sum over contributors r with i_r = u of w_r * G[s(r), :]
  *              (same section, Algorithm 1 backward half), over the distinct rows
  *              u touched in the step, then a sparse row update.
@@ -194,6 +196,7 @@ static int position_kept(const oracle_col *col, int64_t p, int64_t start, int64_
 
 /*
  * Y      [B, sumD] fp32   pooled output, columns concatenated in order
+ * pweights [N] fp32       per-position weights v_r, or NULL (all 1)
  * Ybound [B, sumD] fp64   sum |w_r E[i_r, d]| (may be NULL)
  * bag_n  [C*B]            valid positions per bag (may be NULL)
  * rows   [N]              transformed row per position (may be NULL)
@@ -201,8 +204,8 @@ static int position_kept(const oracle_col *col, int64_t p, int64_t start, int64_
  */
 int64_t oracle_forward(const oracle_col *cols, int32_t C, int32_t B, const int32_t *offsets,
                        const int64_t *ids, const float *fvals, const int32_t *keyed_rows,
-                       const uint8_t *mask, float *Y, double *Ybound, int32_t *bag_n,
-                       int32_t *rows)
+                       const uint8_t *mask, const float *pweights, float *Y, double *Ybound,
+                       int32_t *bag_n, int32_t *rows)
 {
     int64_t sumD = 0;
     for (int32_t c = 0; c < C; c++) sumD += cols[c].dim;
@@ -224,8 +227,9 @@ int64_t oracle_forward(const oracle_col *cols, int32_t C, int32_t B, const int32
                 if (r == ROW_DROPPED) continue;
                 n++;
                 if (r == ROW_DEFAULT) continue;      /* the zero row: counted, adds nothing */
+                double v = pweights ? (double)pweights[p] : 1.0;
                 for (int32_t d = 0; d < D; d++) {
-                    double e = weight_at(col, r, d);
+                    double e = v * weight_at(col, r, d);   /* exact: 24 x 24 bits */
                     acc[d] += e;
                     mag[d] += fabs(e);
                 }
@@ -281,7 +285,8 @@ double oracle_adagrad_elem(double e, double a, double g, double lr, double eps, 
  */
 int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int32_t *offsets,
                         const int64_t *ids, const float *fvals, const int32_t *keyed_rows,
-                        const uint8_t *mask, const float *G, int32_t opt, double lr, double eps,
+                        const uint8_t *mask, const float *pweights, const float *G, int32_t opt,
+                        double lr, double eps,
                         int32_t *uniq_col, int64_t *uniq_row, double *uniq_grad,
                         double *uniq_bound, int64_t max_uniq)
 {
@@ -325,6 +330,7 @@ int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int3
             for (; j < L && list[j].row == list[i].row; j++) {
                 int32_t s = bag_of_pos[list[j].pos - a];
                 double w = (col->pool == O_MEAN) ? 1.0 / (double)n_of_bag[s] : 1.0;
+                if (pweights) w *= (double)pweights[list[j].pos];
                 for (int32_t d = 0; d < D; d++) {
                     double t = w * (double)G[s * sumD + off_c + d];
                     g[d] += t;

@@ -33,6 +33,11 @@ MUTANTS = {
     "trunc-first-inclusive": ("return i < col->seq_max;", "return i <= col->seq_max;"),
     "trunc-ends-swapped": ("if (col->seq_keep_last) return", "if (!col->seq_keep_last) return"),
     "mask-ignored": ("if (mask && mask[p] == 0) return 0;", "if (mask && mask[p] == 2) return 0;"),
+    "weight-ignored-in-backward": ("if (pweights) w *= (double)pweights[list[j].pos];",
+                                   "if (0) w *= (double)pweights[list[j].pos];"),
+    "weight-bag-relative-index": ("(double)pweights[p] : 1.0;", "(double)pweights[p - offsets[b]] : 1.0;"),
+    "weight-column-relative-index": ("w *= (double)pweights[list[j].pos];",
+                                     "w *= (double)pweights[list[j].pos - a];"),
 }
 
 

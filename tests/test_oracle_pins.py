@@ -58,9 +58,11 @@ def _as_f64(col, w):
     return w.astype(np.float64)
 
 
-def _torch_forward_and_grad(cols, weights, B, offsets, rows, G):
+def _torch_forward_and_grad(cols, weights, B, offsets, rows, G, pw=None):
     """embedding_bag per column on the oracle's row indices (a library routine),
-    and autograd for the dense gradient of sum(Y * G)."""
+    and autograd for the dense gradient of sum(Y * G).  With per-position
+    weights pw, a sum bag is embedding_bag's per_sample_weights sum, and a mean
+    bag the same sum divided by the bag's kept count."""
     Ys, grads = [], []
     off_c = 0
     for c, col in enumerate(cols):
@@ -76,8 +78,17 @@ def _torch_forward_and_grad(cols, weights, B, offsets, rows, G):
         for s in range(B):
             starts.append(kept_before[offsets[c * B + s] - a])
         mode = "mean" if col.pool == W.MEAN else "sum"
-        y = torch.nn.functional.embedding_bag(torch.tensor(idx, dtype=torch.long), W64,
-                                              torch.tensor(starts, dtype=torch.long), mode=mode)
+        if pw is None:
+            y = torch.nn.functional.embedding_bag(torch.tensor(idx, dtype=torch.long), W64,
+                                                  torch.tensor(starts, dtype=torch.long), mode=mode)
+        else:
+            psw = torch.tensor(pw[a:e][keep], dtype=torch.float64)
+            y = torch.nn.functional.embedding_bag(torch.tensor(idx, dtype=torch.long), W64,
+                                                  torch.tensor(starts, dtype=torch.long), mode="sum",
+                                                  per_sample_weights=psw)
+            if col.pool == W.MEAN:
+                n = np.diff(np.concatenate([starts, [int(keep.sum())]]))
+                y = y / torch.tensor(np.maximum(n, 1), dtype=torch.float64)[:, None]
         Gc = torch.tensor(G[:, off_c:off_c + col.dim], dtype=torch.float64)
         (y * Gc).sum().backward()
         Ys.append(y.detach().numpy())
@@ -362,6 +373,49 @@ def test_truncation_keeps_first_or_last_closed_form():
         Y, _, n, _ = oracle.forward(oracle.Columns([col], [Wt]), 1, off, ids, mask=odd)
         got = [i for i in want if i % 2]
         assert n[0] == len(got) and np.array_equal(Y[0], Wt[got].sum(axis=0))
+
+
+# ----------------------------------------------------- per-position weights
+
+@pytest.mark.parametrize("seed", range(6))
+def test_weighted_forward_and_backward_match_autograd(seed):
+    """Per-position weights v (RecIS Sec. 3.2: Y_s = sum_r w_r E[i_r]; each
+    contributor sends w_r G[s(r)] back): embedding_bag's per_sample_weights for
+    sum bags, that sum over the kept count for mean bags, autograd for dE."""
+    rng = np.random.default_rng(800 + seed)
+    cols, B, off, ids, fv, weights = _tiny_case(rng, kinds=(W.HASH, W.IDENTITY, W.BUCKET))
+    N = int(off[-1])
+    pw = rng.normal(size=N).astype(np.float32)
+    cs = oracle.Columns(cols, [w.copy() for w in weights])
+    Y, Yb, bag_n, rows = oracle.forward(cs, B, off, ids, fv, pweights=pw)
+    G = rng.normal(size=Y.shape).astype(np.float32)
+    Yt, grads = _torch_forward_and_grad(cols, weights, B, off, rows, G, pw=pw)
+    assert np.allclose(Y, Yt, rtol=0, atol=1e-6 * (1 + np.abs(Yt).max()))
+    assert np.all(Yb + 1e-12 >= np.abs(Y) * (1 - 1e-6))
+    ucol, urow, ug, ub = oracle.backward(cs, B, off, G, ids, fv, opt=W.OPT_EMIT, pweights=pw)
+    for c, col in enumerate(cols):
+        sel = ucol == c
+        assert np.allclose(ug[sel][:, :col.dim], grads[c][urow[sel]], rtol=1e-12, atol=1e-12)
+        assert np.all(ub[sel][:, :col.dim] + 1e-12 >= np.abs(ug[sel][:, :col.dim]))
+
+
+def test_unit_and_power_of_two_weights():
+    """All-one weights give the unweighted results bit for bit; weights of 2 give
+    exactly twice the outputs and gradients."""
+    rng = np.random.default_rng(850)
+    cols, B, off, ids, fv, weights = _tiny_case(rng)
+    N = int(off[-1])
+    cs = oracle.Columns(cols, weights)
+    G = rng.normal(size=(B, cs.sum_dim)).astype(np.float32)
+    base = oracle.forward(cs, B, off, ids, fv)
+    one = oracle.forward(cs, B, off, ids, fv, pweights=np.ones(N, np.float32))
+    two = oracle.forward(cs, B, off, ids, fv, pweights=np.full(N, 2, np.float32))
+    for x, y in zip(base, one):
+        assert np.array_equal(x, y)
+    assert np.array_equal(two[0], 2 * base[0])
+    gb = oracle.backward(cs, B, off, G, ids, fv)
+    g2 = oracle.backward(cs, B, off, G, ids, fv, pweights=np.full(N, 2, np.float32))
+    assert np.array_equal(gb[1], g2[1]) and np.array_equal(2 * gb[2], g2[2])
 
 
 # ------------------------------------------------------------ optimizers
