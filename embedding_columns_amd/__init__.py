@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
-    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_masked",
+    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex",
     "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
@@ -72,7 +72,7 @@ _SIGS = {
                         C.POINTER(_VP)],
     "emb_plan_destroy": [_VP],
     "emb_forward": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
-    "emb_forward_masked": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
+    "emb_forward_ex": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
@@ -162,11 +162,11 @@ def emb_forward(plan, offsets, ids, fvals, keyed_rows, n_ids, out, workspace, tr
                              _stream(stream)))
 
 
-def emb_forward_masked(plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out, workspace,
-                       training, stats=None, stream=None):
-    _check(lib().emb_forward_masked(plan, _ptr(offsets), _ptr(ids), _ptr(fvals), _ptr(keyed_rows),
-                                    _ptr(mask), n_ids, _ptr(out), _ptr(workspace),
-                                    1 if training else 0, _ptr(stats), _stream(stream)))
+def emb_forward_ex(plan, offsets, ids, fvals, keyed_rows, pweights, mask, n_ids, out, workspace,
+                   training, stats=None, stream=None):
+    _check(lib().emb_forward_ex(plan, _ptr(offsets), _ptr(ids), _ptr(fvals), _ptr(keyed_rows),
+                                _ptr(pweights), _ptr(mask), n_ids, _ptr(out), _ptr(workspace),
+                                1 if training else 0, _ptr(stats), _stream(stream)))
 
 
 def emb_backward(plan, grad_out, workspace, uniq_keys=None, uniq_grads=None, n_uniq=None,
@@ -295,19 +295,21 @@ class EmbeddingColumns:
             self.plan = None
 
     def forward(self, offsets, ids=None, fvals=None, keyed_rows=None, training=True, stats=None,
-                out=None, mask=None):
-        """mask: uint8 [n_ids] device tensor (0 removes a position) or None."""
+                out=None, weights=None, mask=None):
+        """weights: fp32 [n_ids] per-position weights or None; mask: uint8 [n_ids]
+        (0 removes a position) or None.  Device tensors."""
         n = (ids if ids is not None else fvals if fvals is not None else keyed_rows)
         n_ids = 0 if n is None else n.numel()
         if out is None:
             out = torch.empty(self.batch, self.sum_dim, dtype=torch.float32, device=self.device)
-        if mask is None:
+        if mask is None and weights is None:
             emb_forward(self.plan, offsets, ids, fvals, keyed_rows, n_ids, out, self.workspace,
                         training, stats)
         else:
-            assert mask.dtype == torch.uint8 and mask.numel() >= n_ids
-            emb_forward_masked(self.plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out,
-                               self.workspace, training, stats)
+            assert mask is None or (mask.dtype == torch.uint8 and mask.numel() >= n_ids)
+            assert weights is None or (weights.dtype == torch.float32 and weights.numel() >= n_ids)
+            emb_forward_ex(self.plan, offsets, ids, fvals, keyed_rows, weights, mask, n_ids, out,
+                           self.workspace, training, stats)
         self._n = n_ids
         return out
 

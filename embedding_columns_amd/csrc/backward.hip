@@ -672,7 +672,9 @@ struct BwdArgs {
     float lr, eps;
     int64_t ntiles;
     const float *G;
-    const uint32_t *sval;       // sorted bags
+    const uint32_t *sval;       // sorted bags (PW: sorted positions)
+    const int32_t *pbags;       // PW: bag of each position
+    const float *pw;            // PW: weight of each position
     const int32_t *bag_n;
     const uint32_t *seg;        // [U + 1]
     const uint32_t *ukeys;      // [U]
@@ -1156,7 +1158,9 @@ __device__ __forceinline__ int seg_boundary(const BwdLds &L, int x, int x0, int 
     return x;
 }
 
-template <int OPT, bool KM>
+// PW: the forward had per-position weights; the sort then carried positions, and
+// each contributor's bag and weight are read through its position
+template <int OPT, bool KM, bool PW>
 __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 {
     __shared__ BwdLds lds[kTileWaves];
@@ -1192,7 +1196,21 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 #pragma unroll
         for (int j = 0; j < kKeyWin / kWave; j++) L.kw[lane + kWave * j] = kv[j];
     }
-    if (a.any_mean) {
+    float vw[kPL];
+    if (PW) {
+        // bagr holds positions here (< N: the sorted entries are positions)
+#pragma unroll
+        for (int i = 0; i < kPL; i++) {
+            vw[i] = *gp(a.pw + bagr[i]);
+            bagr[i] = *gp(a.pbags + bagr[i]);
+        }
+        // the mean weight is folded in here, per contributor's column
+#pragma unroll
+        for (int i = 0; i < kPL; i++) {
+            const bool mean = *gp(&a.cols[bagr[i] / a.B].pool) == EMB_POOL_MEAN;
+            nr[i] = mean ? *gp(a.bag_n + bagr[i]) : 1;
+        }
+    } else if (a.any_mean) {
 #pragma unroll
         for (int i = 0; i < kPL; i++) nr[i] = *gp(a.bag_n + bagr[i]);
     } else {
@@ -1240,7 +1258,9 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         const int p = x0 + lane + kWave * i;
         if (p >= t.t0 && p < t.t1) {
             L.bag[p - t.t0] = bagr[i];
-            L.wt[p - t.t0] = __builtin_amdgcn_rcpf((float)nr[i]);   // mean weight; sum columns use 1
+            // mean weight; sum columns use 1 (PW: times the contributor's weight)
+            L.wt[p - t.t0] = PW ? vw[i] * __builtin_amdgcn_rcpf((float)nr[i])
+                                : __builtin_amdgcn_rcpf((float)nr[i]);
         }
     }
     if (lane == 0) L.njob = 0;
@@ -1257,7 +1277,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         }
         const int s1 = uniform(lo);
         const DevCol col = a.cols[c];
-        if (col.pool != EMB_POOL_MEAN) {
+        if (!PW && col.pool != EMB_POOL_MEAN) {
             for (int q = p + lane; q < s1; q += kWave) L.wt[q - t.t0] = 1.0f;
             wave_sync();
         }
@@ -1291,6 +1311,7 @@ struct AtomArgs {
     const int32_t *bags;        // forward: bag per position
     const int32_t *bag_n;
     const uint32_t *cstart;     // forward: first position of each column [C + 1]
+    const float *pw;            // forward: weight of each position, or NULL (all 1)
     uint32_t total_rows;
 };
 
@@ -1323,11 +1344,13 @@ __global__ __launch_bounds__(kTileBlock, 4) void atomic_apply(AtomArgs a)
             uint32_t key[U];
             int bag[U], nb[U];
             float4 x[U];
+            float vw[U];
 #pragma unroll
             for (int j = 0; j < U; j++) {
                 const int pp = min(b0 + j * G + g, cend - 1);
                 key[j] = b0 + j * G + g < cend ? *gp(a.keys + pp) : a.total_rows;
                 bag[j] = *gp(a.bags + pp);
+                vw[j] = a.pw ? *gp(a.pw + pp) : 1.0f;
             }
 #pragma unroll
             for (int j = 0; j < U; j++) {
@@ -1338,7 +1361,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void atomic_apply(AtomArgs a)
             float s[U][4];
 #pragma unroll
             for (int j = 0; j < U; j++) {
-                const float wt = (mean ? __builtin_amdgcn_rcpf((float)nb[j]) : 1.0f) * -a.lr;
+                const float wt = (mean ? __builtin_amdgcn_rcpf((float)nb[j]) : 1.0f) * vw[j] * -a.lr;
                 s[j][0] = wt * x[j].x; s[j][1] = wt * x[j].y; s[j][2] = wt * x[j].z; s[j][3] = wt * x[j].w;
             }
 #pragma unroll
@@ -1378,6 +1401,21 @@ static emb_status bwd_check(emb_plan *plan, void *workspace)
     return EMB_OK;
 }
 
+template <bool PW>
+static void launch_apply(const emb_plan *plan, const BwdArgs &a, dim3 grid, dim3 block, hipStream_t st)
+{
+    if (a.opt == EMB_OPT_EMIT)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_EMIT, false, PW>), grid, block, 0, st, a);
+    else if (a.opt == EMB_OPT_SGD && plan->seg_from_keys)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, true, PW>), grid, block, 0, st, a);
+    else if (a.opt == EMB_OPT_SGD)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, false, PW>), grid, block, 0, st, a);
+    else if (plan->seg_from_keys)
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, true, PW>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, false, PW>), grid, block, 0, st, a);
+}
+
 static int sort_passes(const emb_plan *plan) { return (plan->key_bits + kRadixBits - 1) / kRadixBits; }
 
 extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32_t *uniq_keys,
@@ -1390,7 +1428,9 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     const int64_t n = plan->last_n;
     const WsLayout &W = plan->ws;
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + W.keys);
-    uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + W.bags);
+    // the sort's values: the bag of each position, or with per-position weights
+    // the position itself (the apply then reads bag and weight through it)
+    uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + (plan->last_weighted ? W.posid : W.bags));
     uint32_t *k1 = reinterpret_cast<uint32_t *>(ws + W.keys2);
     uint32_t *v1 = reinterpret_cast<uint32_t *>(ws + W.vals2);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + W.hist);
@@ -1476,7 +1516,10 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.ntiles = std::max<int64_t>(1, (n + plan->tile - 1) / plan->tile);
     a.G = grad_out;
     // the sorted bags sit in the buffer the last radix pass wrote
-    a.sval = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.vals2 : W.bags));
+    a.sval = reinterpret_cast<const uint32_t *>(
+        ws + (sort_passes(plan) % 2 ? W.vals2 : (plan->last_weighted ? W.posid : W.bags)));
+    a.pbags = reinterpret_cast<const int32_t *>(ws + W.bags);
+    a.pw = reinterpret_cast<const float *>(ws + W.pw);
     a.skeys = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.keys2 : W.keys));
     a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
     a.seg = reinterpret_cast<const uint32_t *>(ws + W.seg);
@@ -1498,16 +1541,8 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, a.xcd_chunk);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(kTileBlock);
-    if (a.opt == EMB_OPT_EMIT)
-        hipLaunchKernelGGL((seg_apply<EMB_OPT_EMIT, false>), grid, block, 0, st, a);
-    else if (a.opt == EMB_OPT_SGD && plan->seg_from_keys)
-        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, true>), grid, block, 0, st, a);
-    else if (a.opt == EMB_OPT_SGD)
-        hipLaunchKernelGGL((seg_apply<EMB_OPT_SGD, false>), grid, block, 0, st, a);
-    else if (plan->seg_from_keys)
-        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, true>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, false>), grid, block, 0, st, a);
+    if (plan->last_weighted) launch_apply<true>(plan, a, grid, block, st);
+    else launch_apply<false>(plan, a, grid, block, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("seg_apply launch: ") + hipGetErrorString(e));
     return EMB_OK;
@@ -1553,6 +1588,7 @@ extern "C" emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out,
     a.bags = reinterpret_cast<const int32_t *>(ws + plan->ws.bags);
     a.bag_n = reinterpret_cast<const int32_t *>(ws + plan->ws.bag_n);
     a.cstart = reinterpret_cast<const uint32_t *>(ws + plan->ws.cstart);
+    a.pw = plan->last_weighted ? reinterpret_cast<const float *>(ws + plan->ws.pw) : nullptr;
     a.total_rows = plan->total_rows;
     hipLaunchKernelGGL(atomic_apply, dim3((unsigned)a.ntiles), dim3(kTileBlock), 0,
                        static_cast<hipStream_t>(stream), a);

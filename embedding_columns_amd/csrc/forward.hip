@@ -39,6 +39,9 @@ struct FwdArgs {
     const float *fvals;
     const int32_t *krows;
     const uint8_t *mask;     // per-position keep byte, or NULL
+    const float *pw_in;      // per-position weight, or NULL (all 1)
+    float *pw_save;          // training with weights: the weights, for the backward
+    uint32_t *posid;         // ... and each position's own index (the sort's values)
     float *Y;
     uint32_t *keys;
     int32_t *bags;
@@ -61,6 +64,7 @@ constexpr int kSpan = kTileMax + kShort;
 struct WaveLds {
     int32_t rows[kSpan];             // transformed row of each tile position
     int32_t pbag[kSpan];             // bag of each tile position (training)
+    float wt[kSpan];                 // weight of each tile position (extended forward)
     int32_t off[kOffCap];            // window of CSR offsets
     union {
         float part[kWave][4];        // per-lane partial sum of each run's first bag
@@ -206,7 +210,7 @@ __device__ __forceinline__ float4 row_f32(const uint2 &v)
 // one column segment [s0, s1) of the tile.  A row is read by P lanes (a power
 // of two), 4 elements per lane: 16-byte loads for fp32 rows (BF false), 8-byte
 // for bf16.
-template <bool BF, bool W>
+template <bool BF, bool W, bool EXT>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
                                             int32_t &zero_bags)
@@ -239,11 +243,13 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             // every load is issued (dropped / default / past-the-run positions read
             // row 0), so that the single wait below covers exactly these loads
             int r[U];
+            float vw[U];
             RowRaw<BF> h[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int x = L.rows[min(p + u, ge - 1) - t.t0];   // unconditional LDS reads
                 r[u] = (p + u < ge) ? x : -1;
+                vw[u] = EXT ? L.wt[min(p + u, ge - 1) - t.t0] : 1.0f;
             }
 #pragma unroll
             for (int u = 0; u < U; u++)
@@ -274,10 +280,17 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                 // every outstanding load and store before reusing its registers
                 const float4 w = row_f32(h[u]);
                 const bool use = pp < ge && r[u] >= 0;
-                acc[0] += use ? w.x : 0.f;
-                acc[1] += use ? w.y : 0.f;
-                acc[2] += use ? w.z : 0.f;
-                acc[3] += use ? w.w : 0.f;
+                if (EXT) {
+                    acc[0] += use ? vw[u] * w.x : 0.f;
+                    acc[1] += use ? vw[u] * w.y : 0.f;
+                    acc[2] += use ? vw[u] * w.z : 0.f;
+                    acc[3] += use ? vw[u] * w.w : 0.f;
+                } else {
+                    acc[0] += use ? w.x : 0.f;
+                    acc[1] += use ? w.y : 0.f;
+                    acc[2] += use ? w.z : 0.f;
+                    acc[3] += use ? w.w : 0.f;
+                }
                 if (pp < ge) {
                     cnt += (r[u] != -1);
                     if (q == 0) L.pbag[pp - t.t0] = b;
@@ -388,8 +401,8 @@ __device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L
     return keep;
 }
 
-// FILTER: the column is truncated or the call has a mask
-template <bool FILTER>
+// EXT: the extended forward (truncation, mask or per-position weights)
+template <bool EXT>
 __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
                                               const TileIn &in, int32_t (&cnt)[5])
@@ -423,11 +436,19 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
         // removed positions are counted apart from the transform's drops
-        const bool removed = FILTER && !position_kept(a, L, t, col, p);
+        const bool removed = EXT && !position_kept(a, L, t, col, p);
         cnt[2] += (r == -1 && !removed);
         cnt[4] += removed;
         if (removed) r = -1;
         L.rows[p - t.t0] = r;
+        if (EXT) {
+            const float v = a.pw_in ? *gp(a.pw_in + p) : 1.0f;
+            L.wt[p - t.t0] = v;
+            if (a.training && a.pw_in) {
+                *gp(a.pw_save + p) = v;
+                *gp(a.posid + p) = (uint32_t)p;
+            }
+        }
         cnt[0] += 1;
         cnt[1] += (r >= 0);
         cnt[3] += (r == -2);
@@ -455,9 +476,9 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const 
     return min(t.t1, win ? offw<true>(a, L, t, (c + 1) * a.B) : offat(a, L, t, (c + 1) * a.B));
 }
 
-// FILTER: some column truncates or the call has a mask (a separate instance, so
-// that the plain forward carries none of that code)
-template <bool FILTER>
+// EXT: some column truncates, or the call has a mask or per-position weights (a
+// separate instance, so that the plain forward carries none of that code)
+template <bool EXT>
 __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 {
     __shared__ WaveLds lds[kTileWaves];
@@ -580,8 +601,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            if (FILTER && (a.mask || col.seq_max > 0))
-                fwd_transform<true>(a, L, t, col, s0, s1, in, cnt);
+            if (EXT) fwd_transform<true>(a, L, t, col, s0, s1, in, cnt);
             else fwd_transform<false>(a, L, t, col, s0, s1, in, cnt);
         }
         for (int c = c_first; c <= c_last; c++) {
@@ -590,11 +610,11 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
             if (win) {
-                if (col.dtype == EMB_BF16) fwd_segment<true, true>(a, L, t, col, cu, s0, s1, zero_bags);
-                else fwd_segment<false, true>(a, L, t, col, cu, s0, s1, zero_bags);
+                if (col.dtype == EMB_BF16) fwd_segment<true, true, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, true, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
             } else {
-                if (col.dtype == EMB_BF16) fwd_segment<true, false>(a, L, t, col, cu, s0, s1, zero_bags);
-                else fwd_segment<false, false>(a, L, t, col, cu, s0, s1, zero_bags);
+                if (col.dtype == EMB_BF16) fwd_segment<true, false, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, false, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
             }
         }
         if (a.training) {
@@ -658,9 +678,9 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 using namespace emb;
 
 static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
-                               const float *fvals, const int32_t *keyed_rows, const uint8_t *mask,
-                               int64_t n_ids, float *out, void *workspace, int32_t training,
-                               int64_t *stats, void *stream)
+                               const float *fvals, const int32_t *keyed_rows, const float *pweights,
+                               const uint8_t *mask, int64_t n_ids, float *out, void *workspace,
+                               int32_t training, int64_t *stats, void *stream)
 {
     if (!plan) return fail(EMB_ERR_INVALID_ARG, "plan is NULL");
     if (!offsets || !out || !workspace) return fail(EMB_ERR_INVALID_ARG, "offsets, out and workspace are required");
@@ -687,6 +707,9 @@ static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int
     a.fvals = fvals;
     a.krows = keyed_rows;
     a.mask = mask;
+    a.pw_in = pweights;
+    a.pw_save = reinterpret_cast<float *>(ws + plan->ws.pw);
+    a.posid = reinterpret_cast<uint32_t *>(ws + plan->ws.posid);
     a.Y = out;
     a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
     a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
@@ -697,10 +720,13 @@ static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int
     a.stats = stats;
     a.total_rows = plan->total_rows;
     a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
-    if (training) plan->last_n = n_ids;
+    if (training) {
+        plan->last_n = n_ids;
+        plan->last_weighted = pweights != nullptr;
+    }
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
-    if (mask || plan->has_trunc)
+    if (mask || pweights || plan->has_trunc)
         hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
                            static_cast<hipStream_t>(stream), a);
     else
@@ -716,16 +742,16 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
                                   float *out, void *workspace, int32_t training, int64_t *stats,
                                   void *stream)
 {
-    return forward_impl(plan, offsets, ids, fvals, keyed_rows, nullptr, n_ids, out, workspace,
-                        training, stats, stream);
+    return forward_impl(plan, offsets, ids, fvals, keyed_rows, nullptr, nullptr, n_ids, out,
+                        workspace, training, stats, stream);
 }
 
-extern "C" emb_status emb_forward_masked(emb_plan *plan, const int32_t *offsets,
-                                         const int64_t *ids, const float *fvals,
-                                         const int32_t *keyed_rows, const uint8_t *mask,
-                                         int64_t n_ids, float *out, void *workspace,
-                                         int32_t training, int64_t *stats, void *stream)
+extern "C" emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                     const float *fvals, const int32_t *keyed_rows,
+                                     const float *pweights, const uint8_t *mask, int64_t n_ids,
+                                     float *out, void *workspace, int32_t training, int64_t *stats,
+                                     void *stream)
 {
-    return forward_impl(plan, offsets, ids, fvals, keyed_rows, mask, n_ids, out, workspace,
-                        training, stats, stream);
+    return forward_impl(plan, offsets, ids, fvals, keyed_rows, pweights, mask, n_ids, out,
+                        workspace, training, stats, stream);
 }

@@ -65,6 +65,7 @@ struct WsLayout {
     size_t seg, ukeys, ucnt, uscan, misc;     // unique rows: segment starts, keys, block counts
     size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
     size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
+    size_t pw, posid;                         // weighted forward -> backward: weight and index per position
     size_t total;
 };
 
@@ -84,6 +85,7 @@ struct emb_plan {
     int64_t uq_blocks = 0;         // unique-row blocks of the largest batch
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
     bool has_trunc = false;        // some column truncates its bags
+    bool last_weighted = false;    // the last training forward had per-position weights
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
     bool seg_from_keys = false;    // the last dedup skipped the unique list (see emb_backward_dedup)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata

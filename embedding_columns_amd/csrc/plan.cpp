@@ -121,6 +121,8 @@ void plan_layout(emb_plan &P)
     L.bcnt = take(4 * 2 * P.max_tiles);
     L.btick = take(4 * P.max_tiles);
     L.cstart = take(4 * ((size_t)P.n_cols + 1));
+    L.pw = take(4 * N);
+    L.posid = take(4 * N);
     L.total = o;
 }
 

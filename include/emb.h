@@ -156,21 +156,29 @@ emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const int64_t *id
                        void *workspace, int32_t training, int64_t *stats, void *stream);
 
 /*
- * emb_forward with a per-position mask (masking, one of the per-field
- * transformations of RecIS Sec. 3.1 / Figure 2; the pages give no detail, so a
- * mask here is one byte per position).
- *   mask     uint8 [n_ids]: a position whose byte is 0 is removed before the
- *            transform, like a truncated one: it reads no row, does not count in a
- *            mean and gets no gradient.  Nonzero keeps it.  NULL = emb_forward.
+ * emb_forward with optional per-position inputs (all device memory, caller-owned):
+ *   pweights fp32 [n_ids] or NULL: the weight w_r of each contributor in
+ *            RecIS Sec. 3.2 ("Index-aware segment reduction": Y_s is the sum of
+ *            w_r E[i_r] over the bag, and each contributor sends w_r G[s(r)]
+ *            back).  A sum bag pools sum v_r E[i_r]; a mean bag divides that sum
+ *            by its count of valid positions (DEFAULT ones included, as without
+ *            weights).  NULL: all weights 1.
+ *   mask     uint8 [n_ids] or NULL: masking, one of the per-field
+ *            transformations of RecIS Sec. 3.1 / Figure 2 (the pages give no
+ *            detail, so a mask here is one byte per position).  A position whose
+ *            byte is 0 is removed before the transform, like a truncated one: it
+ *            reads no row, does not count in a mean and gets no gradient.
  * A position survives iff the mask keeps it AND its column's truncation keeps it
  * (both look at raw positions, so their order does not matter).  The matching
- * emb_backward needs no mask: the forward records the removed positions.
- * Arguments, layout, ownership and errors otherwise as emb_forward.
+ * emb_backward needs neither input again: a training call records the removed
+ * positions and copies the weights into the workspace.  With both NULL and no
+ * truncating column this is emb_forward.  Arguments, layout, ownership and errors
+ * otherwise as emb_forward.
  */
-emb_status emb_forward_masked(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
-                              const float *fvals, const int32_t *keyed_rows, const uint8_t *mask,
-                              int64_t n_ids, float *out, void *workspace, int32_t training,
-                              int64_t *stats, void *stream);
+emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                          const float *fvals, const int32_t *keyed_rows, const float *pweights,
+                          const uint8_t *mask, int64_t n_ids, float *out, void *workspace,
+                          int32_t training, int64_t *stats, void *stream);
 
 /*
  * Backward of the last training forward on this workspace: deduplicates the

@@ -54,8 +54,9 @@ class Step:
         self.kr = keyed_rows
         self.stats = torch.zeros(E.STAT_COUNT, dtype=torch.int64, device=self.dev)
 
-    def forward(self, training=True, mask=None):
-        """mask: uint8 numpy [N] or None (then the unmasked entry point runs)."""
+    def forward(self, training=True, mask=None, pweights=None):
+        """mask: uint8 numpy [N], pweights: fp32 numpy [N], or None (with both None
+        the plain entry point runs)."""
         kinds = {c.kind for c in self.w.cols}
         n = self.b.n
         ids = self.ids[:n] if n else None
@@ -64,13 +65,16 @@ class Step:
         args = (ids if (kinds & {W.HASH, W.IDENTITY}) and n else None,
                 fv if W.BUCKET in kinds and n else None,
                 self.kr if W.KEYED in kinds and n else None)
-        if mask is None:
+        if mask is None and pweights is None:
             E.emb_forward(self.cols.plan, self.off, *args, n, Y, self.cols.workspace, training,
                           self.stats)
         else:
-            m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(self.dev)
-            E.emb_forward_masked(self.cols.plan, self.off, *args, m if n else None, n, Y,
-                                 self.cols.workspace, training, self.stats)
+            m = None if mask is None or not n else torch.from_numpy(
+                np.ascontiguousarray(mask, dtype=np.uint8)).to(self.dev)
+            v = None if pweights is None or not n else torch.from_numpy(
+                np.ascontiguousarray(pweights, dtype=np.float32)).to(self.dev)
+            E.emb_forward_ex(self.cols.plan, self.off, *args, v, m, n, Y, self.cols.workspace,
+                             training, self.stats)
         self.cols._n = n
         return Y
 
@@ -171,32 +175,34 @@ def check_rows_adagrad(col, before, st_before, after_gpu, st_gpu, g_ref, gbound,
 
 
 def run_dense_case(w, seed, tile=0, training=True, device="cuda", check_bwd=True, ask_unique=True,
-                   mask_keep=None):
+                   mask_keep=None, weighted=False):
     """Full parity of one step for HASH / IDENTITY / BUCKET workloads.  With
     ask_unique=False the backward returns nothing (the benchmark's path) and only
     the updated rows are compared.  mask_keep: run the masked forward with a
-    random mask that keeps each position with this probability."""
+    random mask that keeps each position with this probability.  weighted: pass
+    random per-position weights."""
     b = W.make_batch(w, seed=seed)
     mask = None if mask_keep is None else W.make_mask(b.n, seed, mask_keep)
+    pw = W.make_position_weights(b.n, seed) if weighted else None
     wts, sts = W.make_tables(w, seed=seed, device="cpu")
     G = W.make_grad(w, seed=seed, device="cpu")
     st = Step(w, b, wts, sts, tile=tile, device=device)
-    Y = st.forward(training=training, mask=mask)
+    Y = st.forward(training=training, mask=mask, pweights=pw)
     ws = st.cols.workspace_view(max(b.n, 1)) if training else None
     ws = (ws[0][:b.n], ws[1][:b.n], ws[2]) if ws is not None else None
     host_w = [to_np(t) for t in wts]
     host_s = [None if s is None else to_np(s) for s in sts]
     oc = oracle_columns(w, [x.copy() for x in host_w], [None if s is None else s.copy() for s in host_s])
-    ref = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals, mask=mask)
+    ref = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals, mask=mask, pweights=pw)
     torch.cuda.synchronize()
     check_forward(w, b, Y, ws, ref, training)
-    out = {"Y": Y, "step": st, "batch": b, "ref": ref, "mask": mask}
+    out = {"Y": Y, "step": st, "batch": b, "ref": ref, "mask": mask, "pweights": pw}
     if not (training and check_bwd):
         return out
     ukeys, ugrads, nu = st.backward(G, ask_unique=ask_unique)
     torch.cuda.synchronize()
     ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
-                                         opt=w.opt, lr=w.lr, eps=w.eps, mask=mask)
+                                         opt=w.opt, lr=w.lr, eps=w.eps, mask=mask, pweights=pw)
     if ask_unique:
         check_unique(w, ukeys, nu, ucol, urow)
     if w.opt == W.OPT_EMIT:

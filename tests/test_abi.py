@@ -120,5 +120,5 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_backward_dedup(None, None, None, None, None, None) == 1
     assert L.lib().emb_backward_apply(None, None, None, None, None) == 1
     assert L.lib().emb_backward_atomic(None, None, None, None) == 1
-    assert L.lib().emb_forward_masked(None, None, None, None, None, None, 0, None, None, 0, None,
-                                      None) == 1
+    assert L.lib().emb_forward_ex(None, None, None, None, None, None, None, 0, None, None, 0, None,
+                                  None) == 1

@@ -107,7 +107,7 @@ def test_bucket_boundaries_beyond_lds():
     _run_custom(w, b, 64)
 
 
-def _atomic_sgd_case(w, b, seed):
+def _atomic_sgd_case(w, b, seed, pweights=None):
     """The atomic-scatter SGD backward against the oracle's sorted sums.
 
     The row ends as E + sum_i t_i (t_i = -lr w_i g_i) added one term at a time in
@@ -117,14 +117,14 @@ def _atomic_sgd_case(w, b, seed):
     wts, sts = W.make_tables(w, seed=seed, device="cpu")
     G = W.make_grad(w, seed=seed, device="cpu")
     st = Step(w, b, wts, sts, tile=256)
-    st.forward(training=True)
+    st.forward(training=True, pweights=pweights)
     st.cols.backward_atomic(G.to("cuda"))
     torch.cuda.synchronize()
     host_w = [to_np(t) for t in wts]
     oc = oracle_columns(w, [x.copy() for x in host_w])
-    _, _, _, rows = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals)
+    _, _, _, rows = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals, pweights=pweights)
     ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
-                                         opt=w.opt, lr=w.lr)
+                                         opt=w.opt, lr=w.lr, pweights=pweights)
     from gpu_harness import positions_columns, as_f64
     _, pcol = positions_columns(b.offsets, len(w.cols), w.batch)
     for c, col in enumerate(w.cols):
@@ -146,6 +146,13 @@ def test_atomic_backward_sgd():
     # the pages' backward (atomic adds, no sort) on the training front end's shape
     w = W.config(2, n_cols=24, batch=512, rows_range=(1e2, 1e4))
     _atomic_sgd_case(w, W.make_batch(w, seed=2042), 2042)
+
+
+def test_atomic_backward_weighted():
+    # per-position weights reach the atomic backward through the workspace
+    w = W.config(2, n_cols=16, batch=400, rows_range=(1e2, 1e4))
+    b = W.make_batch(w, seed=2043)
+    _atomic_sgd_case(w, b, 2043, pweights=W.make_position_weights(b.n, 2043))
 
 
 def test_atomic_backward_hot_row():

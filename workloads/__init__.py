@@ -322,6 +322,12 @@ def make_mask(n: int, seed: int, keep: float = 0.8) -> np.ndarray:
     return (rng.random(n) < keep).astype(np.uint8)
 
 
+def make_position_weights(n: int, seed: int) -> np.ndarray:
+    """Per-position weights, fp32 [n]: uniform in [-1, 2) (signs of both kinds)."""
+    rng = np.random.default_rng(seed + 104729)
+    return rng.uniform(-1.0, 2.0, size=n).astype(np.float32)
+
+
 def make_tables(w: Workload, seed: int, device="cpu"):
     """Per-column weight tensors ~ N(0, init_std) (bf16 columns rounded from fp32)
     and zeroed fp32 Adagrad accumulators.  Drawn with torch's generator on
