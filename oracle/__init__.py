@@ -40,7 +40,7 @@ class _Col(C.Structure):
                 ("dim", C.c_int32), ("rows", C.c_int64), ("id_lo", C.c_int64),
                 ("id_hi", C.c_int64), ("boundaries", C.c_void_p), ("n_boundaries", C.c_int64),
                 ("weights", C.c_void_p), ("state", C.c_void_p), ("seq_max", C.c_int32),
-                ("seq_keep_last", C.c_int32)]
+                ("seq_keep_last", C.c_int32), ("default_row", C.c_int64)]
 
 
 _lib = None
@@ -156,7 +156,7 @@ class Columns:
             arr[i] = _Col(c.kind, c.pool, c.dtype, c.dim, c.rows, c.id_lo, c.id_hi,
                           _p(self.bounds[i]), 0 if self.bounds[i] is None else self.bounds[i].size,
                           _p(w), _p(self.states[i]), getattr(c, "seq_max", 0),
-                          getattr(c, "seq_keep_last", 0))
+                          getattr(c, "seq_keep_last", 0), getattr(c, "default_row", -1))
         self.arr = arr
         self.sum_dim = int(sum(c.dim for c in cols))
         self.max_dim = int(max(c.dim for c in cols))

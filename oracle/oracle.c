@@ -19,8 +19,12 @@
  *              (RecIS Sec. 3.2 "Index-aware segment reduction", Algorithm 1,
  *              forward half); w_r = v_r (sum) or v_r / n (mean), with v_r the
  *              caller's per-position weight (1 when none is given) and n the
- *              valid positions including DEFAULT ones; an empty bag gives the
- *              zero vector.
+ *              valid positions including DEFAULT ones.  A bag with no valid
+ *              position (a missing feature) gives the zero vector, or, when the
+ *              column names a default row, that row (RECom explainer: a default
+ *              fills in a missing feature, and RECom merges this empty-row filling
+ *              into the lookup): the bag then reads as one position at that row
+ *              with weight 1, in the forward and in the backward.
  *   backward   dE[u] = sum over contributors r with i_r = u of w_r * G[s(r), :]
  *              (same section, Algorithm 1 backward half), over the distinct rows
  *              u touched in the step, then a sparse row update.
@@ -55,6 +59,7 @@ typedef struct {
     float *state;   /* Adagrad accumulator [rows, dim] fp32, or NULL */
     int32_t seq_max;        /* SeqTrunc: keep at most this many positions per bag (0 = all) */
     int32_t seq_keep_last;  /* ... the last seq_max (1) or the first seq_max (0) */
+    int64_t default_row;    /* row that fills a bag with no valid position, or -1 (zero vector) */
 } oracle_col;
 
 /* ---------------------------------------------------------------- hashing */
@@ -240,6 +245,9 @@ int64_t oracle_forward(const oracle_col *cols, int32_t C, int32_t B, const int32
                 if (n > 0) {
                     y = (col->pool == O_MEAN) ? acc[d] / (double)n : acc[d];
                     m = (col->pool == O_MEAN) ? mag[d] / (double)n : mag[d];
+                } else if (col->default_row >= 0) {
+                    y = weight_at(col, col->default_row, d);
+                    m = fabs(y);
                 }
                 Y[s * sumD + off_c + d] = (float)y;
                 if (Ybound) Ybound[s * sumD + off_c + d] = m;
@@ -303,7 +311,9 @@ int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int3
         /* pass 1: valid count per bag (the mean's denominator) */
         int32_t *n_of_bag = (int32_t *)calloc((size_t)B, sizeof(int32_t));
         int32_t *bag_of_pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)(e - a + 1));
-        rowpos *list = (rowpos *)malloc(sizeof(rowpos) * (size_t)(e - a + 1));
+        /* contributors: the valid non-DEFAULT positions, then one pseudo position
+         * e + s per empty bag s when the column has a default row */
+        rowpos *list = (rowpos *)malloc(sizeof(rowpos) * (size_t)(e - a + B + 1));
         int64_t L = 0;
         for (int32_t s = 0; s < B; s++) {
             int64_t b = (int64_t)c * B + s;
@@ -319,6 +329,14 @@ int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int3
                 L++;
             }
         }
+        if (col->default_row >= 0) {
+            for (int32_t s = 0; s < B; s++) {
+                if (n_of_bag[s] > 0) continue;
+                list[L].row = col->default_row;
+                list[L].pos = e + s;
+                L++;
+            }
+        }
         /* pass 2: sort contributors by (row, position) and sum each run */
         qsort(list, (size_t)L, sizeof(rowpos), cmp_rowpos);
         double *g = (double *)malloc(sizeof(double) * (size_t)D);
@@ -328,9 +346,16 @@ int64_t oracle_backward(const oracle_col *cols, int32_t C, int32_t B, const int3
             memset(g, 0, sizeof(double) * D);
             memset(m, 0, sizeof(double) * D);
             for (; j < L && list[j].row == list[i].row; j++) {
-                int32_t s = bag_of_pos[list[j].pos - a];
-                double w = (col->pool == O_MEAN) ? 1.0 / (double)n_of_bag[s] : 1.0;
-                if (pweights) w *= (double)pweights[list[j].pos];
+                int32_t s;
+                double w;
+                if (list[j].pos >= e) {          /* an empty bag's default row: weight 1 */
+                    s = (int32_t)(list[j].pos - e);
+                    w = 1.0;
+                } else {
+                    s = bag_of_pos[list[j].pos - a];
+                    w = (col->pool == O_MEAN) ? 1.0 / (double)n_of_bag[s] : 1.0;
+                    if (pweights) w *= (double)pweights[list[j].pos];
+                }
                 for (int32_t d = 0; d < D; d++) {
                     double t = w * (double)G[s * sumD + off_c + d];
                     g[d] += t;

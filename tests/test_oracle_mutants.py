@@ -36,6 +36,11 @@ MUTANTS = {
     "weight-ignored-in-backward": ("if (pweights) w *= (double)pweights[list[j].pos];",
                                    "if (0) w *= (double)pweights[list[j].pos];"),
     "weight-bag-relative-index": ("(double)pweights[p] : 1.0;", "(double)pweights[p - offsets[b]] : 1.0;"),
+    "default-row-not-read": ("} else if (col->default_row >= 0) {", "} else if (0) {"),
+    "default-row-no-gradient": ("        if (col->default_row >= 0) {\n            for (int32_t s = 0; s < B; s++) {",
+                                "        if (0) {\n            for (int32_t s = 0; s < B; s++) {"),
+    "default-row-mean-weight": ("                    w = 1.0;\n                } else {",
+                                "                    w = (col->pool == O_MEAN) ? 0.5 : 1.0;\n                } else {"),
     "weight-column-relative-index": ("w *= (double)pweights[list[j].pos];",
                                      "w *= (double)pweights[list[j].pos - a];"),
 }

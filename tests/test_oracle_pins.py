@@ -418,6 +418,65 @@ def test_unit_and_power_of_two_weights():
     assert np.array_equal(gb[1], g2[1]) and np.array_equal(2 * gb[2], g2[2])
 
 
+# ------------------------------------------------------------- default row
+
+@pytest.mark.parametrize("seed", range(4))
+def test_default_row_equals_filling_empty_bags(seed):
+    """A column with a default row d behaves like the same batch with the ID d
+    inserted into every bag that has no valid ID (TF-style empty-row filling,
+    which RECom merges into the lookup), forward and backward."""
+    rng = np.random.default_rng(900 + seed)
+    C, B = 3, 8
+    cols, weights = [], []
+    for c in range(C):
+        rows, dim = int(rng.integers(5, 12)), int(rng.choice([4, 8]))
+        cols.append(W.Column(W.IDENTITY, (W.SUM, W.MEAN)[c % 2], W.F32, rows, dim,
+                             default_row=int(rng.integers(0, rows))))
+        weights.append(rng.normal(size=(rows, dim)).astype(np.float32))
+    lens = rng.integers(0, 4, size=C * B)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ids = rng.integers(-3, 14, size=int(off[-1])).astype(np.int64)
+    # the filled batch, built by hand: bag b of column c gets d_c appended when none
+    # of its IDs is in [0, rows_c)
+    f_ids, f_lens = [], []
+    for b in range(C * B):
+        col = cols[b // B]
+        seg = list(ids[off[b]:off[b + 1]])
+        if not any(0 <= x < col.rows for x in seg):
+            seg.append(col.default_row)
+        f_ids += seg
+        f_lens.append(len(seg))
+    f_off = np.concatenate([[0], np.cumsum(f_lens)]).astype(np.int32)
+    f_ids = np.array(f_ids, dtype=np.int64)
+    plain = [W.Column(c.kind, c.pool, c.dtype, c.rows, c.dim) for c in cols]
+
+    Y, Yb, _, _ = oracle.forward(oracle.Columns(cols, weights), B, off, ids)
+    Y2, Yb2, _, _ = oracle.forward(oracle.Columns(plain, weights), B, f_off, f_ids)
+    assert np.array_equal(Y, Y2) and np.array_equal(Yb, Yb2)
+    G = rng.normal(size=Y.shape).astype(np.float32)
+    wa, wb = [w.copy() for w in weights], [w.copy() for w in weights]
+    ra = oracle.backward(oracle.Columns(cols, wa), B, off, G, ids, opt=W.OPT_SGD, lr=0.1)
+    rb = oracle.backward(oracle.Columns(plain, wb), B, f_off, G, f_ids, opt=W.OPT_SGD, lr=0.1)
+    assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
+    assert np.allclose(ra[2], rb[2], rtol=1e-12, atol=1e-15)
+    for x, y in zip(wa, wb):
+        assert np.allclose(x, y, rtol=1e-6, atol=1e-7)
+
+
+def test_default_row_closed_form():
+    """Every bag empty: each output is row d, and d's gradient is the sum of all G rows."""
+    rng = np.random.default_rng(950)
+    Wt = rng.normal(size=(6, 4)).astype(np.float32)
+    col = W.Column(W.HASH, W.MEAN, W.F32, 6, 4, id_lo=0, id_hi=10, default_row=4)
+    off = np.array([0, 0, 2, 2, 3], dtype=np.int32)          # two empty, two all-invalid
+    ids = np.array([-1, 10, 99], dtype=np.int64)
+    Y, _, n, _ = oracle.forward(oracle.Columns([col], [Wt]), 4, off, ids)
+    assert list(n) == [0, 0, 0, 0] and np.array_equal(Y, np.tile(Wt[4], (4, 1)))
+    G = rng.normal(size=(4, 4)).astype(np.float32)
+    ucol, urow, ug, _ = oracle.backward(oracle.Columns([col], [Wt]), 4, off, G, ids)
+    assert list(urow) == [4] and np.allclose(ug[0], G.astype(np.float64).sum(axis=0), rtol=1e-15)
+
+
 # ------------------------------------------------------------ optimizers
 
 @pytest.mark.parametrize("opt,big_eps", [(W.OPT_SGD, False), (W.OPT_ADAGRAD, False),

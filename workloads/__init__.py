@@ -48,6 +48,7 @@ class Column:
     boundaries: Optional[np.ndarray] = None  # fp32, sorted, BUCKET only
     seq_max: int = 0                         # SeqTrunc: keep at most this many positions per bag
     seq_keep_last: int = 0                   # keep the last seq_max (1) or the first (0)
+    default_row: int = -1                    # row filling an empty bag (-1: zero vector)
 
 
 @dataclass
