@@ -23,8 +23,8 @@ MUTANTS = {
     "mean-on-sum": ("y = (col->pool == O_MEAN) ? acc[d] / (double)n : acc[d];",
                     "y = acc[d] / (double)n;"),
     "grad-wrong-sample": ("G[s * sumD + off_c + d]", "G[s * sumD + d]"),
-    "grad-no-mean-weight": ("double w = (col->pool == O_MEAN) ? 1.0 / (double)n_of_bag[s] : 1.0;",
-                            "double w = 1.0;"),
+    "grad-no-mean-weight": ("w = (col->pool == O_MEAN) ? 1.0 / (double)n_of_bag[s] : 1.0;",
+                            "w = 1.0;"),
     "sgd-sign": ("weight_store(col, r, d, w0 - lr * g[d]);", "weight_store(col, r, d, w0 + lr * g[d]);"),
     "adagrad-eps-inside": ("return e - lr * g / (sqrt(a2) + eps);", "return e - lr * g / sqrt(a2 + eps);"),
     "bf16-truncate": ("r = ldexp(rint(ldexp(m, 8)), e - 8);", "r = ldexp(floor(ldexp(m, 8)), e - 8);"),
