@@ -52,7 +52,7 @@ class ColumnDesc(C.Structure):
                 ("rows", C.c_int64), ("id_lo", C.c_int64), ("id_hi", C.c_int64),
                 ("boundaries", C.c_void_p), ("n_boundaries", C.c_int64),
                 ("weights", C.c_void_p), ("opt_state", C.c_void_p), ("seq_max", C.c_int32),
-                ("seq_keep_last", C.c_int32)]
+                ("seq_keep_last", C.c_int32), ("default_row", C.c_int64)]
 
 
 class PlanOpts(C.Structure):
@@ -247,7 +247,7 @@ class EmbeddingColumns:
     """A plan over columns with caller-owned tables (torch tensors on the GPU).
 
     cols: objects with kind, pool, dtype, rows, dim, id_lo, id_hi and optional
-    boundaries (fp32 array-like), seq_max and seq_keep_last; weights[c]: [rows, dim] fp32/bf16 tensor (for a
+    boundaries (fp32 array-like), seq_max, seq_keep_last and default_row; weights[c]: [rows, dim] fp32/bf16 tensor (for a
     KEYED column, the table's row pool); states[c]: fp32 Adagrad accumulator."""
 
     def __init__(self, cols, weights, states=None, batch=1, max_ids=0, opt=OPT_EMIT, lr=0.0,
@@ -270,7 +270,7 @@ class EmbeddingColumns:
                                   getattr(c, "id_hi", 0), _ptr(bt) if bt is not None else None,
                                   0 if bt is None else bt.numel(), _ptr(w),
                                   _ptr(s) if s is not None else None, getattr(c, "seq_max", 0),
-                                  getattr(c, "seq_keep_last", 0))
+                                  getattr(c, "seq_keep_last", 0), getattr(c, "default_row", -1))
         self.descs = descs
         self.opts = PlanOpts(opt, lr, eps, tile)
         self.sum_dim = sum(c.dim for c in self.cols)
@@ -317,7 +317,8 @@ class EmbeddingColumns:
         """Returns (uniq_keys, uniq_grads, n_uniq) device tensors (None where not asked).
         With nothing asked (no keys, grads, count or stats) and SGD / Adagrad, the
         library skips building the unique-row list."""
-        n = max(getattr(self, "_n", 0), 1)
+        n_def = sum(1 for c in self.cols if getattr(c, "default_row", -1) >= 0)
+        n = max(getattr(self, "_n", 0) + n_def, 1)
         keys = torch.empty(n, dtype=torch.int32, device=self.device) if want_keys else None
         grads = (torch.empty(n, self.max_dim, dtype=torch.float32, device=self.device)
                  if want_grads else None)

@@ -1208,11 +1208,13 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < kPL; i++) {
             const bool mean = *gp(&a.cols[bagr[i] / a.B].pool) == EMB_POOL_MEAN;
-            nr[i] = mean ? *gp(a.bag_n + bagr[i]) : 1;
+            nr[i] = mean ? max(*gp(a.bag_n + bagr[i]), 1) : 1;
         }
     } else if (a.any_mean) {
 #pragma unroll
-        for (int i = 0; i < kPL; i++) nr[i] = *gp(a.bag_n + bagr[i]);
+        // (a bag with no valid position reaches here only through its default
+        // row's entry, whose weight is 1)
+        for (int i = 0; i < kPL; i++) nr[i] = max(*gp(a.bag_n + bagr[i]), 1);
     } else {
 #pragma unroll
         for (int i = 0; i < kPL; i++) nr[i] = 1;
@@ -1416,6 +1418,13 @@ static void launch_apply(const emb_plan *plan, const BwdArgs &a, dim3 grid, dim3
         hipLaunchKernelGGL((seg_apply<EMB_OPT_ADAGRAD, false, PW>), grid, block, 0, st, a);
 }
 
+// entries the backward sorts: the positions of the last training forward, plus
+// one per bag when a column has a default row
+static int64_t sort_n(const emb_plan *plan)
+{
+    return plan->last_n + (plan->has_default ? (int64_t)plan->n_cols * plan->batch : 0);
+}
+
 static int sort_passes(const emb_plan *plan) { return (plan->key_bits + kRadixBits - 1) / kRadixBits; }
 
 extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32_t *uniq_keys,
@@ -1425,7 +1434,7 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     if (s != EMB_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    const int64_t n = plan->last_n;
+    const int64_t n = sort_n(plan);
     const WsLayout &W = plan->ws;
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + W.keys);
     // the sort's values: the bag of each position, or with per-position weights
@@ -1456,8 +1465,9 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     // Segments found from the keys come from the column sort when the average
     // column fits its LDS (n <= C * kColCap; a larger column is sorted by its
     // workgroup through global memory); the sort leaves dropped / DEFAULT keys
-    // inside each column.  Otherwise the global radix passes sort everything.
-    if (from_keys && n <= (int64_t)plan->n_cols * kColCap) {
+    // inside each column.  Otherwise the global radix passes sort everything;
+    // they also take the default-row entries, which sit after the N positions.
+    if (from_keys && !plan->has_default && n <= (int64_t)plan->n_cols * kColCap) {
         uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
         hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, k1, v1,
                            kf, vf, n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,
@@ -1498,7 +1508,7 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     if (!grad_out || !aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned device memory");
     if (uniq_grads && (plan->opt != EMB_OPT_EMIT || !aligned(uniq_grads, 16)))
         return fail(EMB_ERR_INVALID_ARG, "uniq_grads needs the EMIT optimizer and 16-byte alignment");
-    const int64_t n = plan->last_n;
+    const int64_t n = sort_n(plan);
     if (n == 0) return EMB_OK;
     char *ws = static_cast<char *>(workspace);
     const WsLayout &W = plan->ws;
@@ -1568,6 +1578,7 @@ extern "C" emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out,
     emb_status s = bwd_check(plan, workspace);
     if (s != EMB_OK) return s;
     if (plan->opt != EMB_OPT_SGD) return fail(EMB_ERR_UNSUPPORTED, "the atomic backward is for SGD only");
+    if (plan->has_default) return fail(EMB_ERR_UNSUPPORTED, "the atomic backward has no default rows");
     for (int32_t c = 0; c < plan->n_cols; c++)
         if (plan->hcols[c].dtype != EMB_F32) return fail(EMB_ERR_UNSUPPORTED, "the atomic backward needs fp32 tables");
     if (!grad_out || !aligned(grad_out, 16)) return fail(EMB_ERR_INVALID_ARG, "grad_out must be 16-byte aligned device memory");

@@ -42,6 +42,7 @@ struct FwdArgs {
     const float *pw_in;      // per-position weight, or NULL (all 1)
     float *pw_save;          // training with weights: the weights, for the backward
     uint32_t *posid;         // ... and each position's own index (the sort's values)
+    int32_t has_default;     // training entries N + bag record the default-row fills
     float *Y;
     uint32_t *keys;
     int32_t *bags;
@@ -120,30 +121,62 @@ __device__ __forceinline__ int next_bag(const FwdArgs &a, const WaveLds &L, cons
     return nb;
 }
 
-template <int V>
+// A bag with no valid position in a column with a default row: sort entry N + bag
+// gives that row the bag's gradient; other bags leave a sentinel there.  Written
+// by the bag's one writer (lane q == 0 of bag_out, or the empty-bag pass).
+__device__ __forceinline__ void default_entry(const FwdArgs &a, const DevCol &col, int bag, int n)
+{
+    const int64_t x = a.N + bag;
+    *gp(a.keys + x) = (n == 0 && col.default_row >= 0) ? col.row_base + (uint32_t)col.default_row
+                                                       : a.total_rows;
+    *gp(a.bags + x) = bag;
+    if (a.pw_in) {
+        *gp(a.pw_save + x) = 1.0f;
+        *gp(a.posid + x) = (uint32_t)x;
+    }
+}
+
+// 4 elements (q * 4 ...) of row r of the column's table as fp32
+__device__ __forceinline__ float4 row_slice(const DevCol &col, int64_t r, int q)
+{
+    if (col.dtype == EMB_BF16) {
+        const uint2 v = *gp(reinterpret_cast<const uint2 *>(
+            static_cast<const uint16_t *>(col.weights) + r * col.dim + q * 4));
+        return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+    }
+    return *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + r * col.dim + q * 4));
+}
+
+template <int V, bool EXT>
 __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int c, int bag,
                                         const float (&acc)[V], int n, int q, bool qa,
                                         int32_t &zero_bags)
 {
+    static_assert(V == 4, "one 4-element slice per lane");
     const int s = bag - c * a.B;
     if (qa) {
         float o[V];
         const float sc = n == 0 ? 0.f : (col.pool == EMB_POOL_MEAN ? __builtin_amdgcn_rcpf((float)n) : 1.0f);
 #pragma unroll
         for (int v = 0; v < V; v++) o[v] = acc[v] * sc;
+        if (EXT && n == 0 && col.default_row >= 0) {
+            const float4 d = row_slice(col, col.default_row, q);
+            o[0] = d.x; o[1] = d.y; o[2] = d.z; o[3] = d.w;
+        }
         EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V));
 #pragma unroll
         for (int v = 0; v < V; v += 4) y[v / 4] = make_float4(o[v], o[v + 1], o[v + 2], o[v + 3]);
     }
     if (q == 0) {
         if (a.training) *gp(a.bag_n + bag) = n;
+        if (EXT && a.training && a.has_default) default_entry(a, col, bag, n);
         zero_bags += (n == 0);
     }
 }
 
 // a piece of a bag that crosses a tile boundary: publish it, and if this is the
 // last piece to arrive, sum all pieces in tile order and write the bag
-template <int V, bool W>
+template <int V, bool W, bool EXT>
 __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t,
                                            const DevCol &col, int c, int side, int bag,
                                            const float (&sum)[V], int n, int leader, int q, bool qa,
@@ -191,7 +224,7 @@ __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, c
                 for (int v = 0; v < V; v++) tot[v] += x[r][v];
             }
         }
-        bag_out<V>(a, col, c, bag, tot, tn, q, qa, zero_bags);
+        bag_out<V, EXT>(a, col, c, bag, tot, tn, q, qa, zero_bags);
         if (q == 0) st_agent(&a.tick[k0], 0u);   // ready for the next call
     }
 }
@@ -266,7 +299,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                         for (int v = 0; v < V; v++) hacc[v] = acc[v];
                         hcnt = cnt; hbag = b; hpass = false;
                     } else {
-                        bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
+                        bag_out<V, EXT>(a, col, c, b, acc, cnt, q, qa, zero_bags);
                     }
 #pragma unroll
                     for (int v = 0; v < V; v++) acc[v] = 0.f;
@@ -304,7 +337,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                 for (int v = 0; v < V; v++) hacc[v] = acc[v];
                 hcnt = cnt; hbag = b; hpass = false;
             } else {
-                bag_out<V>(a, col, c, b, acc, cnt, q, qa, zero_bags);
+                bag_out<V, EXT>(a, col, c, b, acc, cnt, q, qa, zero_bags);
             }
         } else if (before) {
 #pragma unroll
@@ -339,8 +372,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             n += L.hcnt[g2];
             if (!L.hpass[g2]) { ended = true; break; }
         }
-        if (ended) bag_out<V>(a, col, c, tbag, sum, n, q, qa, zero_bags);
-        else tile_piece<V, W>(a, L, t, col, c, 1, tbag, sum, n, g * P, q, qa, zero_bags);
+        if (ended) bag_out<V, EXT>(a, col, c, tbag, sum, n, q, qa, zero_bags);
+        else tile_piece<V, W, EXT>(a, L, t, col, c, 1, tbag, sum, n, g * P, q, qa, zero_bags);
     }
     // the bag that came in from the previous tile
     if (g == 0 && hbag >= 0) {
@@ -356,7 +389,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             n += L.hcnt[g2];
             pass = L.hpass[g2];
         }
-        tile_piece<V, W>(a, L, t, col, c, 0, hbag, sum, n, 0, q, qa, zero_bags);
+        tile_piece<V, W, EXT>(a, L, t, col, c, 0, hbag, sum, n, 0, q, qa, zero_bags);
     }
     wave_sync();
 }
@@ -634,7 +667,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     const bool zfast = t.t0 < t.t1 && own_lo >= t.wb && own_hi < t.wb + t.wn &&
                        own_lo / a.B >= c_base && (own_hi - 1) / a.B <= t.bl / a.B &&
                        (own_hi - 1) / a.B - c_base < kColCache;
-    if (zfast) {
+    if (zfast && !(EXT && a.has_default)) {
         for (int b = own_lo + lane; b < own_hi; b += kWave) {
             if (L.off[b - t.wb] != L.off[b + 1 - t.wb]) continue;
             const int c = b / a.B;
@@ -652,8 +685,15 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(
                 a.Y + (int64_t)(b - c * a.B) * a.sumD + *gp(&a.cols[c].out_off)));
             const int dim = *gp(&a.cols[c].dim);
-            for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int64_t dr = EXT ? *gp(&a.cols[c].default_row) : -1;
+            if (EXT && dr >= 0) {
+                const DevCol col = a.cols[c];
+                for (int d = 0; d < dim / 4; d++) y[d] = row_slice(col, dr, d);
+            } else {
+                for (int d = 0; d < dim / 4; d++) y[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
             if (a.training) *gp(a.bag_n + b) = 0;
+            if (EXT && a.training && a.has_default) default_entry(a, a.cols[c], b, 0);
             zero_bags++;
         }
     }
@@ -710,6 +750,7 @@ static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int
     a.pw_in = pweights;
     a.pw_save = reinterpret_cast<float *>(ws + plan->ws.pw);
     a.posid = reinterpret_cast<uint32_t *>(ws + plan->ws.posid);
+    a.has_default = plan->has_default ? 1 : 0;
     a.Y = out;
     a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
     a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
@@ -726,7 +767,7 @@ static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int
     }
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
-    if (mask || pweights || plan->has_trunc)
+    if (mask || pweights || plan->has_trunc || plan->has_default)
         hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
                            static_cast<hipStream_t>(stream), a);
     else

@@ -52,8 +52,9 @@ struct DevCol {
     int32_t glanes;          // lanes per gradient row (same as lanes)
     int32_t seq_max;         // keep at most this many positions per bag (0: all)
     int32_t seq_keep_last;   // ... the last seq_max (1) or the first (0)
+    int64_t default_row;     // row read by a bag with no valid position, or -1 (zero vector)
 };
-static_assert(sizeof(DevCol) == 104, "DevCol layout");
+static_assert(sizeof(DevCol) == 112, "DevCol layout");
 static_assert(kOffCap % kWave == 0, "window loads are unrolled per lane");
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
@@ -86,6 +87,8 @@ struct emb_plan {
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
     bool has_trunc = false;        // some column truncates its bags
     bool last_weighted = false;    // the last training forward had per-position weights
+    bool has_default = false;      // some column has a default row: the forward adds one
+                                   // sort entry per bag after the N positions
     int64_t last_n = -1;           // positions of the last training forward (read by the backward)
     bool seg_from_keys = false;    // the last dedup skipped the unique list (see emb_backward_dedup)
     emb::DevCol *dcols = nullptr;  // device copy of the column metadata

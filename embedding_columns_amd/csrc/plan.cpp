@@ -77,6 +77,8 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
             if (d.n_boundaries > (int64_t(1) << 30)) return fail(EMB_ERR_UNSUPPORTED, at + "too many boundaries");
         }
         if (d.seq_max < 0) return fail(EMB_ERR_INVALID_ARG, at + "seq_max must be >= 0");
+        if (d.default_row < -1 || d.default_row >= d.rows)
+            return fail(EMB_ERR_INVALID_ARG, at + "default_row must be -1 or in [0, rows)");
         if (d.seq_keep_last != 0 && d.seq_keep_last != 1)
             return fail(EMB_ERR_INVALID_ARG, at + "seq_keep_last must be 0 or 1");
         if (!d.weights) return fail(EMB_ERR_INVALID_ARG, at + "weights is NULL");
@@ -94,8 +96,9 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
 
 void plan_layout(emb_plan &P)
 {
-    const int64_t N = std::max<int64_t>(P.max_ids, 1);
     const int64_t nb = (int64_t)P.n_cols * P.batch;
+    // sort entries: the positions, plus one per bag when a column has a default row
+    const int64_t N = std::max<int64_t>(P.max_ids, 1) + (P.has_default ? nb : 0);
     P.max_tiles = std::max<int64_t>(1, (N + P.tile - 1) / P.tile);
     P.sort_blocks = std::max<int64_t>(1, (N + kSortTile - 1) / kSortTile);
     P.uq_blocks = std::max<int64_t>(1, (N + kUqTile - 1) / kUqTile);
@@ -178,6 +181,7 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         h.glanes = pow2_ceil(d.dim / 4);
         h.seq_max = d.seq_max;
         h.seq_keep_last = d.seq_keep_last;
+        h.default_row = d.default_row;
         row_base += (uint64_t)d.rows;
         off += d.dim;
         maxd = std::max(maxd, d.dim);
@@ -186,6 +190,7 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         P.has_keyed |= d.kind == EMB_COL_KEYED;
         P.any_mean |= d.pool == EMB_POOL_MEAN;
         P.has_trunc |= d.seq_max > 0;
+        P.has_default |= d.default_row >= 0;
     }
     P.total_rows = (uint32_t)row_base;
     P.hrow_base = new (std::nothrow) uint32_t[n_cols + 1];

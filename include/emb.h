@@ -79,7 +79,7 @@ typedef enum {
 #define EMB_STAT_VALID          1  /* positions with a table row                     */
 #define EMB_STAT_DROPPED        2  /* positions dropped (out of range, NaN, key < 1) */
 #define EMB_STAT_DEFAULT        3  /* positions reading the DEFAULT row              */
-#define EMB_STAT_ZERO_BAGS      4  /* bags whose output is the zero default          */
+#define EMB_STAT_ZERO_BAGS      4  /* bags with no valid position (zero or default row) */
 #define EMB_STAT_UNIQUE         5  /* distinct (column, row) pairs in emb_backward   */
 #define EMB_STAT_TABLE_INSERTED 6  /* keys newly placed in a keyed table             */
 #define EMB_STAT_TABLE_ADMITTED 7  /* keys that received a row (admission)           */
@@ -107,6 +107,13 @@ typedef struct emb_column_desc {
     int32_t seq_keep_last;     /* 1: keep a bag's last seq_max positions, 0: its first. */
                                /* KEYED: the table lookup before the forward still sees */
                                /* (and counts) every key; truncation acts on pooling.   */
+    int64_t default_row;       /* -1: a bag with no valid position pools to the zero     */
+                               /* vector.  0 .. rows-1: it reads this row instead, as one */
+                               /* position of weight 1, and the row gets that bag's      */
+                               /* gradient (RECom explainer: a default fills in a missing */
+                               /* feature; RECom merges that empty-row filling into the  */
+                               /* lookup).  Plans with a default row use the global     */
+                               /* radix sort in emb_backward and have no atomic backward. */
 } emb_column_desc;
 
 typedef struct emb_plan_opts {
@@ -185,9 +192,11 @@ emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, const int64_t 
  * touched (column, row) pairs by a radix sort of their keys, sums each pair's
  * contributions w_r * grad_out[s(r), off_c:off_c+dim] and applies opts->opt.
  *   grad_out   fp32 [batch, sum(dim)].
- *   uniq_keys  uint32 [n_ids] or NULL: the distinct keys, ascending, key = row_base_c + row
- *              with row_base_c = sum of rows of the columns before c.
- *   uniq_grads fp32 [n_ids, max(dim)] or NULL (EMIT only): gradient of uniq_keys[u] in row u.
+ *   uniq_keys  uint32 [n_ids + n_def] or NULL: the distinct keys, ascending, key =
+ *              row_base_c + row with row_base_c = sum of rows of the columns before c;
+ *              n_def = the number of columns with a default row (0 without).
+ *   uniq_grads fp32 [n_ids + n_def, max(dim)] or NULL (EMIT only): gradient of
+ *              uniq_keys[u] in row u.
  *   n_uniq     int64 device scalar or NULL: number of distinct keys.
  * SGD / ADAGRAD update the columns' weights (and opt_state) in place; rows that
  * no position touched are left bit-identical.

@@ -204,7 +204,7 @@ def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows
     G = np.ascontiguousarray(G, dtype=np.float32)
     assert G.shape == (B, cols.sum_dim)
     mask, pweights = _mask(mask), _pw(pweights)
-    cap = max(n, 1)
+    cap = max(n + len(cols.cols), 1)          # + one default row per column at most
     ucol = np.zeros(cap, dtype=np.int32)
     urow = np.zeros(cap, dtype=np.int64)
     ug = np.zeros((cap, cols.max_dim), dtype=np.float64)

@@ -158,7 +158,10 @@ def check_rows_adagrad(col, before, st_before, after_gpu, st_gpu, g_ref, gbound,
     dlt = RTOL_F32 * gbound.ravel() + 1e-30
     hi_e, _ = oracle.adagrad_array(e0, a0, g - dlt, lr, eps)
     lo_e, _ = oracle.adagrad_array(e0, a0, g + dlt, lr, eps)
-    slack = 4 * 2.0 ** -24 * (np.abs(e0) + lr)
+    # fp32 evaluation of E - lr g / (sqrt(A) + eps) with the hardware square root and
+    # reciprocal (about 1 ulp each), two rounded products, the rounded eps add and the
+    # final subtraction: at most 4 ulp (2^-23 relative) of |E| + lr
+    slack = 8 * 2.0 ** -24 * (np.abs(e0) + lr)
     lo_e, hi_e = lo_e - slack, hi_e + slack
     got = as_f64(col, after_gpu[touched]).ravel()
     if col.dtype == W.BF16:

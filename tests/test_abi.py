@@ -45,7 +45,7 @@ def test_symbols_are_plain_c(L):
 
 def _col(L, **kw):
     d = dict(kind=L.HASH, pool=L.SUM, dtype=L.F32, dim=16, rows=1000, id_lo=0, id_hi=1 << 40,
-             boundaries=None, n_boundaries=0, weights=4096, opt_state=None)
+             boundaries=None, n_boundaries=0, weights=4096, opt_state=None, default_row=-1)
     d.update(kw)
     return L.ColumnDesc(**d)
 
@@ -61,7 +61,7 @@ def _query(L, cols, batch=8, max_ids=100, opt=0, lr=0.0, eps=0.0, tile=0):
 def test_plan_query_accepts_a_valid_plan(L):
     s, pb, wb, _ = _query(L, [_col(L), _col(L, kind=L.BUCKET, boundaries=8192, n_boundaries=64,
                                           rows=65, dim=4)])
-    assert s == 0 and pb >= 2 * 104 and wb > 0
+    assert s == 0 and pb >= 2 * 112 and wb > 0
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -81,6 +81,8 @@ def test_plan_query_accepts_a_valid_plan(L):
     (dict(kind=3, dtype=1, dim=16), 2, "fp32"),
     (dict(seq_max=-1), 1, "seq_max"),
     (dict(seq_max=4, seq_keep_last=2), 1, "seq_keep_last"),
+    (dict(default_row=1000), 1, "default_row"),
+    (dict(default_row=-2), 1, "default_row"),
 ])
 def test_plan_query_rejects_bad_columns(L, kw, status, msg):
     s, _, _, err = _query(L, [_col(L), _col(L, **kw)])
