@@ -273,6 +273,9 @@ def make_batch(w: Workload, seed: int) -> Batch:
     forced = np.zeros(C * B, dtype=bool)
     for c, col in enumerate(w.cols):
         L = _bag_lengths(w, rng, col)
+        if c in w.extra.get("lens", {}):          # per-column uniform lengths
+            lo, hi = w.extra["lens"][c]
+            L = rng.integers(lo, hi + 1, size=B)
         if w.empty_frac > 0 and col.kind != BUCKET:
             f = rng.random(B) < w.empty_frac
             L = np.where(f, 0, L)
