@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
-    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex",
+    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex", "emb_transform", "emb_forward_rows",
     "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
@@ -73,6 +73,8 @@ _SIGS = {
     "emb_plan_destroy": [_VP],
     "emb_forward": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_forward_ex": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
+    "emb_transform": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP],
+    "emb_forward_rows": [_VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
@@ -167,6 +169,19 @@ def emb_forward_ex(plan, offsets, ids, fvals, keyed_rows, pweights, mask, n_ids,
     _check(lib().emb_forward_ex(plan, _ptr(offsets), _ptr(ids), _ptr(fvals), _ptr(keyed_rows),
                                 _ptr(pweights), _ptr(mask), n_ids, _ptr(out), _ptr(workspace),
                                 1 if training else 0, _ptr(stats), _stream(stream)))
+
+
+def emb_transform(plan, offsets, ids, fvals, keyed_rows, mask, n_ids, rows_out, stats=None,
+                  stream=None):
+    _check(lib().emb_transform(plan, _ptr(offsets), _ptr(ids), _ptr(fvals), _ptr(keyed_rows),
+                               _ptr(mask), n_ids, _ptr(rows_out), _ptr(stats), _stream(stream)))
+
+
+def emb_forward_rows(plan, offsets, rows, pweights, n_ids, out, workspace, training, stats=None,
+                     stream=None):
+    _check(lib().emb_forward_rows(plan, _ptr(offsets), _ptr(rows), _ptr(pweights), n_ids,
+                                  _ptr(out), _ptr(workspace), 1 if training else 0, _ptr(stats),
+                                  _stream(stream)))
 
 
 def emb_backward(plan, grad_out, workspace, uniq_keys=None, uniq_grads=None, n_uniq=None,

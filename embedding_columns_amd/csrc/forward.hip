@@ -43,6 +43,7 @@ struct FwdArgs {
     float *pw_save;          // training with weights: the weights, for the backward
     uint32_t *posid;         // ... and each position's own index (the sort's values)
     int32_t has_default;     // training entries N + bag record the default-row fills
+    int32_t *rows_out;       // transform-only launch: the row code of every position
     float *Y;
     uint32_t *keys;
     int32_t *bags;
@@ -56,6 +57,15 @@ struct FwdArgs {
 };
 
 constexpr int kColCache = 8;
+
+// What one launch of the forward kernel does:
+//   kFused      transform + gather + pool (emb_forward, emb_forward_ex);
+//   kTransform  the transform only: the row code of every position goes to rows_out
+//               (emb_transform; it touches no workspace, so it may run on another
+//               stream while the previous step's backward still uses it);
+//   kFromRows   gather + pool from row codes a transform-only launch made
+//               (emb_forward_rows); truncation and the mask were applied there.
+enum FwdMode { kFused = 0, kTransform = 1, kFromRows = 2 };
 // A bag of at most kShort positions is never cut by a tile boundary: the tile
 // holding its start finishes it (tiles span at most kTileMax + kShort - 1
 // positions).  Only longer bags are split and combined through the workspace.
@@ -435,7 +445,7 @@ __device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L
 }
 
 // EXT: the extended forward (truncation, mask or per-position weights)
-template <bool EXT>
+template <bool EXT, int MODE>
 __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
                                               const TileIn &in, int32_t (&cnt)[5])
@@ -453,7 +463,11 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
         const int p = t.p0 + lane + kWave * i;
         if (p < s0 || p >= s1) continue;
         int r;
-        if (col.kind == EMB_COL_HASH) {
+        if (MODE == kFromRows) {
+            // row codes from a transform-only launch, checked like keyed rows
+            const int kr = in.kr[i];
+            r = kr == -2 ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
+        } else if (col.kind == EMB_COL_HASH) {
             const int64_t id = in.id[i];
             r = (id >= col.id_lo && id < col.id_hi)
                     ? (int)mod_magic(splitmix64((uint64_t)id), rows, col.magic) : -1;
@@ -469,7 +483,7 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
         // removed positions are counted apart from the transform's drops
-        const bool removed = EXT && !position_kept(a, L, t, col, p);
+        const bool removed = EXT && MODE != kFromRows && !position_kept(a, L, t, col, p);
         cnt[2] += (r == -1 && !removed);
         cnt[4] += removed;
         if (removed) r = -1;
@@ -509,9 +523,10 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const 
     return min(t.t1, win ? offw<true>(a, L, t, (c + 1) * a.B) : offat(a, L, t, (c + 1) * a.B));
 }
 
-// EXT: some column truncates, or the call has a mask or per-position weights (a
-// separate instance, so that the plain forward carries none of that code)
-template <bool EXT>
+// EXT: some column truncates or has a default row, or the call has a mask or
+// per-position weights (a separate instance, so that the plain forward carries
+// none of that code).  MODE: FwdMode.
+template <bool EXT, int MODE>
 __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 {
     __shared__ WaveLds lds[kTileWaves];
@@ -531,8 +546,8 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     for (int i = 0; i < kPL; i++) {
         const int p = x0 + lane + kWave * i;
         const bool ok = p < N;
-        in.id[i] = (a.ids && ok) ? *gp(a.ids + p) : 0;
-        in.fv[i] = (a.fvals && ok) ? *gp(a.fvals + p) : 0.f;
+        in.id[i] = (MODE != kFromRows && a.ids && ok) ? *gp(a.ids + p) : 0;
+        in.fv[i] = (MODE != kFromRows && a.fvals && ok) ? *gp(a.fvals + p) : 0.f;
         in.kr[i] = (a.krows && ok) ? *gp(a.krows + p) : 0;
     }
 
@@ -634,10 +649,17 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            if (EXT) fwd_transform<true>(a, L, t, col, s0, s1, in, cnt);
-            else fwd_transform<false>(a, L, t, col, s0, s1, in, cnt);
+            if (EXT) fwd_transform<true, MODE>(a, L, t, col, s0, s1, in, cnt);
+            else fwd_transform<false, MODE>(a, L, t, col, s0, s1, in, cnt);
         }
-        for (int c = c_first; c <= c_last; c++) {
+        if (MODE == kTransform) {
+#pragma unroll
+            for (int i = 0; i < kPL; i++) {
+                const int p = t.p0 + lane + kWave * i;
+                if (p >= t.t0 && p < t.t1) *gp(a.rows_out + p) = L.rows[p - t.t0];
+            }
+        }
+        for (int c = c_first; c <= c_last && MODE != kTransform; c++) {
             const int cu = uniform(c);
             const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
@@ -663,6 +685,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     // offsets are in the LDS window and their columns were cached by the
     // transform: then the loop reads LDS only (a global read in it would wait
     // for every Y store issued so far)
+    if (MODE == kTransform) own_hi = own_lo;   // outputs are the forward's
     const int c_base = t.t0 < t.t1 ? t.bf / a.B : 0;
     const bool zfast = t.t0 < t.t1 && own_lo >= t.wb && own_hi < t.wb + t.wn &&
                        own_lo / a.B >= c_base && (own_hi - 1) / a.B <= t.bl / a.B &&
@@ -698,6 +721,9 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
         }
     }
 
+    // per-position counts come from the launch that transforms (a kFromRows
+    // launch counts only its bags)
+    if (MODE == kFromRows) cnt[0] = cnt[1] = cnt[2] = cnt[3] = cnt[4] = 0;
     if (a.stats) {
         const int64_t s0 = wave_sum_i64(cnt[0]), s1 = wave_sum_i64(cnt[1]);
         const int64_t s2 = wave_sum_i64(cnt[2]), s3 = wave_sum_i64(cnt[3]);
@@ -717,20 +743,40 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 
 using namespace emb;
 
-static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+template <int MODE>
+static void launch_fwd(bool ext, int64_t blocks, const FwdArgs &a, void *stream)
+{
+    if (ext)
+        hipLaunchKernelGGL((fwd_kernel<true, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           static_cast<hipStream_t>(stream), a);
+    else
+        hipLaunchKernelGGL((fwd_kernel<false, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           static_cast<hipStream_t>(stream), a);
+}
+
+static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets, const int64_t *ids,
                                const float *fvals, const int32_t *keyed_rows, const float *pweights,
-                               const uint8_t *mask, int64_t n_ids, float *out, void *workspace,
-                               int32_t training, int64_t *stats, void *stream)
+                               const uint8_t *mask, int32_t *rows_out, int64_t n_ids, float *out,
+                               void *workspace, int32_t training, int64_t *stats, void *stream)
 {
     if (!plan) return fail(EMB_ERR_INVALID_ARG, "plan is NULL");
-    if (!offsets || !out || !workspace) return fail(EMB_ERR_INVALID_ARG, "offsets, out and workspace are required");
+    if (!offsets) return fail(EMB_ERR_INVALID_ARG, "offsets are required");
+    if (mode != kTransform && (!out || !workspace))
+        return fail(EMB_ERR_INVALID_ARG, "out and workspace are required");
     if (n_ids < 0 || n_ids > plan->max_ids)
         return fail(EMB_ERR_WORKSPACE, "n_ids exceeds the plan's max_ids");
-    if (plan->has_hash && n_ids > 0 && !ids) return fail(EMB_ERR_INVALID_ARG, "ids required (hash/identity columns)");
-    if (plan->has_bucket && n_ids > 0 && !fvals) return fail(EMB_ERR_INVALID_ARG, "fvals required (bucket columns)");
-    if (plan->has_keyed && n_ids > 0 && !keyed_rows) return fail(EMB_ERR_INVALID_ARG, "keyed_rows required (keyed columns)");
-    if (!aligned(out, 16)) return fail(EMB_ERR_INVALID_ARG, "out must be 16-byte aligned");
-    if (!aligned(workspace, 256)) return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (mode == kFromRows) {
+        if (n_ids > 0 && !keyed_rows) return fail(EMB_ERR_INVALID_ARG, "rows required");
+    } else {
+        if (plan->has_hash && n_ids > 0 && !ids) return fail(EMB_ERR_INVALID_ARG, "ids required (hash/identity columns)");
+        if (plan->has_bucket && n_ids > 0 && !fvals) return fail(EMB_ERR_INVALID_ARG, "fvals required (bucket columns)");
+        if (plan->has_keyed && n_ids > 0 && !keyed_rows) return fail(EMB_ERR_INVALID_ARG, "keyed_rows required (keyed columns)");
+    }
+    if (mode == kTransform && n_ids > 0 && !rows_out) return fail(EMB_ERR_INVALID_ARG, "rows_out required");
+    if (mode != kTransform && !aligned(out, 16)) return fail(EMB_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (mode != kTransform && !aligned(workspace, 256))
+        return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (mode == kTransform) training = 0;      // writes nothing but rows_out (and stats)
     FwdArgs a{};
     char *ws = static_cast<char *>(workspace);
     a.cols = plan->dcols;
@@ -748,31 +794,36 @@ static emb_status forward_impl(emb_plan *plan, const int32_t *offsets, const int
     a.krows = keyed_rows;
     a.mask = mask;
     a.pw_in = pweights;
-    a.pw_save = reinterpret_cast<float *>(ws + plan->ws.pw);
-    a.posid = reinterpret_cast<uint32_t *>(ws + plan->ws.posid);
     a.has_default = plan->has_default ? 1 : 0;
+    a.rows_out = rows_out;
     a.Y = out;
-    a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
-    a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
-    a.bag_n = reinterpret_cast<int32_t *>(ws + plan->ws.bag_n);
-    a.part = reinterpret_cast<float *>(ws + plan->ws.fpart);
-    a.pcnt = reinterpret_cast<int32_t *>(ws + plan->ws.fcnt);
-    a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
+    if (ws) {
+        a.pw_save = reinterpret_cast<float *>(ws + plan->ws.pw);
+        a.posid = reinterpret_cast<uint32_t *>(ws + plan->ws.posid);
+        a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
+        a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);
+        a.bag_n = reinterpret_cast<int32_t *>(ws + plan->ws.bag_n);
+        a.part = reinterpret_cast<float *>(ws + plan->ws.fpart);
+        a.pcnt = reinterpret_cast<int32_t *>(ws + plan->ws.fcnt);
+        a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
+        a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
+    }
     a.stats = stats;
     a.total_rows = plan->total_rows;
-    a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
     if (training) {
         plan->last_n = n_ids;
         plan->last_weighted = pweights != nullptr;
     }
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
-    if (mask || pweights || plan->has_trunc || plan->has_default)
-        hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           static_cast<hipStream_t>(stream), a);
-    else
-        hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           static_cast<hipStream_t>(stream), a);
+    if (mode == kTransform) {
+        launch_fwd<kTransform>(mask || plan->has_trunc, blocks, a, stream);
+    } else if (mode == kFromRows) {
+        a.mask = nullptr;                      // applied by the transform
+        launch_fwd<kFromRows>(pweights || plan->has_default, blocks, a, stream);
+    } else {
+        launch_fwd<kFused>(mask || pweights || plan->has_trunc || plan->has_default, blocks, a, stream);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));
     return EMB_OK;
@@ -783,8 +834,8 @@ extern "C" emb_status emb_forward(emb_plan *plan, const int32_t *offsets, const 
                                   float *out, void *workspace, int32_t training, int64_t *stats,
                                   void *stream)
 {
-    return forward_impl(plan, offsets, ids, fvals, keyed_rows, nullptr, nullptr, n_ids, out,
-                        workspace, training, stats, stream);
+    return forward_impl(kFused, plan, offsets, ids, fvals, keyed_rows, nullptr, nullptr, nullptr,
+                        n_ids, out, workspace, training, stats, stream);
 }
 
 extern "C" emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
@@ -793,6 +844,24 @@ extern "C" emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, con
                                      float *out, void *workspace, int32_t training, int64_t *stats,
                                      void *stream)
 {
-    return forward_impl(plan, offsets, ids, fvals, keyed_rows, pweights, mask, n_ids, out,
-                        workspace, training, stats, stream);
+    return forward_impl(kFused, plan, offsets, ids, fvals, keyed_rows, pweights, mask, nullptr,
+                        n_ids, out, workspace, training, stats, stream);
+}
+
+extern "C" emb_status emb_transform(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                    const float *fvals, const int32_t *keyed_rows,
+                                    const uint8_t *mask, int64_t n_ids, int32_t *rows_out,
+                                    int64_t *stats, void *stream)
+{
+    return forward_impl(kTransform, plan, offsets, ids, fvals, keyed_rows, nullptr, mask, rows_out,
+                        n_ids, nullptr, nullptr, 0, stats, stream);
+}
+
+extern "C" emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, const int32_t *rows,
+                                       const float *pweights, int64_t n_ids, float *out,
+                                       void *workspace, int32_t training, int64_t *stats,
+                                       void *stream)
+{
+    return forward_impl(kFromRows, plan, offsets, nullptr, nullptr, rows, pweights, nullptr, nullptr,
+                        n_ids, out, workspace, training, stats, stream);
 }

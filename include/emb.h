@@ -188,6 +188,32 @@ emb_status emb_forward_ex(emb_plan *plan, const int32_t *offsets, const int64_t 
                           int32_t training, int64_t *stats, void *stream);
 
 /*
+ * The forward in two launches, so that the transform of the next batch can run
+ * on another stream while this step's backward still uses the workspace (the
+ * pipelined preparation of RecIS Sec. 3.3: feature transformation for iteration
+ * t + 1 overlaps the training work of iteration t, since it neither reads nor
+ * updates parameters).
+ *
+ * emb_transform: the transform and filter of every position (hash + mod, identity,
+ * bucketize, keyed rows; truncation and the mask) and nothing else.
+ *   rows_out  int32 [n_ids], caller-owned device memory: the row of each position,
+ *             EMB_ROW_DROPPED (-1) for a dropped or removed one, EMB_ROW_DEFAULT (-2)
+ *             for a keyed DEFAULT one.
+ *   Touches no workspace; stats (or NULL) gets the per-position counters.  Other
+ *   arguments as emb_forward_ex.
+ * emb_forward_rows: emb_forward_ex from row codes made by emb_transform for the
+ *   same plan and batch (offsets, n_ids): gather, pool, and with training != 0
+ *   the record the backward needs.  Row codes outside [0, rows) other than -2 are
+ *   dropped.  stats gets the bag counter only (the transform counted the rest).
+ */
+emb_status emb_transform(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                         const float *fvals, const int32_t *keyed_rows, const uint8_t *mask,
+                         int64_t n_ids, int32_t *rows_out, int64_t *stats, void *stream);
+emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, const int32_t *rows,
+                            const float *pweights, int64_t n_ids, float *out, void *workspace,
+                            int32_t training, int64_t *stats, void *stream);
+
+/*
  * Backward of the last training forward on this workspace: deduplicates the
  * touched (column, row) pairs by a radix sort of their keys, sums each pair's
  * contributions w_r * grad_out[s(r), off_c:off_c+dim] and applies opts->opt.

@@ -54,9 +54,9 @@ class Step:
         self.kr = keyed_rows
         self.stats = torch.zeros(E.STAT_COUNT, dtype=torch.int64, device=self.dev)
 
-    def forward(self, training=True, mask=None, pweights=None):
+    def forward(self, training=True, mask=None, pweights=None, split=False):
         """mask: uint8 numpy [N], pweights: fp32 numpy [N], or None (with both None
-        the plain entry point runs)."""
+        the plain entry point runs).  split: emb_transform, then emb_forward_rows."""
         kinds = {c.kind for c in self.w.cols}
         n = self.b.n
         ids = self.ids[:n] if n else None
@@ -65,7 +65,17 @@ class Step:
         args = (ids if (kinds & {W.HASH, W.IDENTITY}) and n else None,
                 fv if W.BUCKET in kinds and n else None,
                 self.kr if W.KEYED in kinds and n else None)
-        if mask is None and pweights is None:
+        if split:
+            m = None if mask is None or not n else torch.from_numpy(
+                np.ascontiguousarray(mask, dtype=np.uint8)).to(self.dev)
+            v = None if pweights is None or not n else torch.from_numpy(
+                np.ascontiguousarray(pweights, dtype=np.float32)).to(self.dev)
+            self.rows = torch.full((max(n, 1),), -7, dtype=torch.int32, device=self.dev)
+            E.emb_transform(self.cols.plan, self.off, *args, m, n, self.rows if n else None,
+                            self.stats)
+            E.emb_forward_rows(self.cols.plan, self.off, self.rows if n else None, v, n, Y,
+                               self.cols.workspace, training, self.stats)
+        elif mask is None and pweights is None:
             E.emb_forward(self.cols.plan, self.off, *args, n, Y, self.cols.workspace, training,
                           self.stats)
         else:
@@ -178,19 +188,20 @@ def check_rows_adagrad(col, before, st_before, after_gpu, st_gpu, g_ref, gbound,
 
 
 def run_dense_case(w, seed, tile=0, training=True, device="cuda", check_bwd=True, ask_unique=True,
-                   mask_keep=None, weighted=False):
+                   mask_keep=None, weighted=False, split=False):
     """Full parity of one step for HASH / IDENTITY / BUCKET workloads.  With
     ask_unique=False the backward returns nothing (the benchmark's path) and only
     the updated rows are compared.  mask_keep: run the masked forward with a
     random mask that keeps each position with this probability.  weighted: pass
-    random per-position weights."""
+    random per-position weights.  split: the forward as emb_transform followed by
+    emb_forward_rows, whose row codes must equal the oracle's bit for bit."""
     b = W.make_batch(w, seed=seed)
     mask = None if mask_keep is None else W.make_mask(b.n, seed, mask_keep)
     pw = W.make_position_weights(b.n, seed) if weighted else None
     wts, sts = W.make_tables(w, seed=seed, device="cpu")
     G = W.make_grad(w, seed=seed, device="cpu")
     st = Step(w, b, wts, sts, tile=tile, device=device)
-    Y = st.forward(training=training, mask=mask, pweights=pw)
+    Y = st.forward(training=training, mask=mask, pweights=pw, split=split)
     ws = st.cols.workspace_view(max(b.n, 1)) if training else None
     ws = (ws[0][:b.n], ws[1][:b.n], ws[2]) if ws is not None else None
     host_w = [to_np(t) for t in wts]
@@ -198,6 +209,8 @@ def run_dense_case(w, seed, tile=0, training=True, device="cuda", check_bwd=True
     oc = oracle_columns(w, [x.copy() for x in host_w], [None if s is None else s.copy() for s in host_s])
     ref = oracle.forward(oc, w.batch, b.offsets, b.ids, b.fvals, mask=mask, pweights=pw)
     torch.cuda.synchronize()
+    if split and b.n:
+        assert np.array_equal(to_np(st.rows)[:b.n], ref[3]), "emb_transform row codes differ"
     check_forward(w, b, Y, ws, ref, training)
     out = {"Y": Y, "step": st, "batch": b, "ref": ref, "mask": mask, "pweights": pw}
     if not (training and check_bwd):

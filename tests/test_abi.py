@@ -124,3 +124,5 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_backward_atomic(None, None, None, None) == 1
     assert L.lib().emb_forward_ex(None, None, None, None, None, None, None, 0, None, None, 0, None,
                                   None) == 1
+    assert L.lib().emb_transform(None, None, None, None, None, None, 0, None, None, None) == 1
+    assert L.lib().emb_forward_rows(None, None, None, None, 0, None, None, 0, None, None) == 1
