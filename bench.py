@@ -166,16 +166,55 @@ def run(args):
     tstats = stats if args.stats else None
     kstats = stats if args.stats else None
 
+    # --pipeline: batch i+1's transform (emb_transform) runs on a second stream at
+    # default priority while step i's backward runs; step i's forward gathers from
+    # the row codes (emb_forward_rows).  Row-code buffers alternate between steps.
+    pipe = args.pipeline and not keyed
+    if pipe:
+        main_s = torch.cuda.current_stream(dev)
+        side_s = torch.cuda.Stream(device=dev)
+        prow = [torch.empty(max(max_ids, 1), dtype=torch.int32, device=dev) for _ in range(2)]
+        ready = {}
+        tev = []
+
+    def transform(i, stream):
+        d = dbat[i % len(dbat)]
+        E.emb_transform(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
+                        d["fv"] if 2 in kinds else None, None, None, d["n"], prow[i % 2], tstats,
+                        stream=stream)
+        ready[i] = torch.cuda.Event()
+        ready[i].record(stream)
+
     def step(i, ev=None):
         d = dbat[i % len(dbat)]
         n = d["n"]
         if keyed:
             table.lookup_or_insert(d["ids"], rows_out=krows[i][:n], stats=kstats)
+        if pipe:
+            if i not in ready:
+                transform(i, main_s)
+            main_s.wait_event(ready.pop(i))
         if ev is not None:
             ev[0].record()
-        E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
-                      d["fv"] if 2 in kinds else None, krows[i][:n] if keyed else None, n, Y,
-                      plan.workspace, training, tstats)
+        if pipe:
+            E.emb_forward_rows(plan.plan, d["off"], prow[i % 2], None, n, Y, plan.workspace,
+                               training, tstats)
+            # the next transform may overwrite prow[(i + 1) % 2] once this forward is
+            # queued: that buffer's last reader was the previous step's forward
+            done = torch.cuda.Event()
+            done.record(main_s)
+            side_s.wait_event(done)
+            if ev is not None:
+                t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0e.record(side_s)
+            transform(i + 1, side_s)
+            if ev is not None:
+                t1e.record(side_s)
+                tev.append((t0e, t1e))
+        else:
+            E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
+                          d["fv"] if 2 in kinds else None, krows[i][:n] if keyed else None, n, Y,
+                          plan.workspace, training, tstats)
         if ev is not None:
             ev[1].record()
         if training and args.atomic_backward:
@@ -258,6 +297,9 @@ def run(args):
                           "gbs": round(ub / (apply_avg * 1e-3) / 1e9, 1)}
         if not args.atomic_backward:
             kernels["dedup_sort_unique"] = {"us": round(1000 * float(np.mean(dedup_ms)), 2)}
+    if pipe:
+        kernels["transform_side_stream"] = {
+            "launch_us": round(1000 * float(np.mean([a.elapsed_time(b) for a, b in tev])), 2)}
     dom = "fwd_kernel" if (not training or fwd_avg >= apply_avg) else akern
     dk = kernels[dom]
     achieved = dk["gbs"]
@@ -280,7 +322,8 @@ def run(args):
                    "valid_lookups_per_step": int(lookups / args.steps),
                    "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
                    "backward": ("atomic" if args.atomic_backward else "sorted") if training else "none",
-                   "tile": plan.opts.tile or 256, "fwd_launches_per_step": 1},
+                   "tile": plan.opts.tile or 256, "fwd_launches_per_step": 2 if pipe else 1,
+                   "pipelined_transform": bool(pipe)},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
@@ -347,6 +390,8 @@ def main():
     ap.add_argument("--atomic-backward", action="store_true",
                     help="SGD by atomic scatter (no sort) instead of the sorted segment apply")
     ap.add_argument("--inference", action="store_true", help="forward only (no backward)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="transform the next batch on a second stream during the backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
