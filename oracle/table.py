@@ -13,6 +13,16 @@ Step rule (batch-level, independent of thread order):
   a fresh row (oracle_init_row); every occurrence of an admitted key returns its
   row, the others return DEFAULT (a zero row that counts in a mean).
   Keys < 1 are dropped.  Prepopulated keys are admitted with count 0.
+
+Lifecycle (Monolith Sec. 2.1 also expires IDs that go unseen for long, so the
+table holds only live features):
+  every lookup-or-insert is one table step s = 0, 1, 2, ...; a key present after
+  step s (found or inserted) records last_seen = s; prepopulated / imported keys
+  record the step counter's value at that time;
+  evict(min_seen) removes every key with last_seen < min_seen: its count, its
+  admission and its row values are gone, and a later occurrence starts it anew;
+  a checkpoint is (keys, counts, last_seen, admitted, values, step counter), and
+  a table restored from it behaves exactly like the original.
 """
 from __future__ import annotations
 
@@ -40,6 +50,8 @@ class OracleTable:
             raise ValueError("duplicate prepopulated keys")
         self.count = np.zeros(self.keys.size, dtype=np.int64)
         self.admitted = np.ones(self.keys.size, dtype=bool)
+        self.step_no = 0
+        self.seen = np.zeros(self.keys.size, dtype=np.int64)
         self.prepop_idx = order.astype(np.int64)         # index into the prepop rows
         self._prepop_rows = prepop_rows
         self.vals = {}                                    # key -> row values (new or updated)
@@ -98,17 +110,58 @@ class OracleTable:
             cnt2 = np.concatenate([self.count, m[~hit]])
             adm2 = np.concatenate([self.admitted, np.zeros(new.size, dtype=bool)])
             pidx2 = np.concatenate([self.prepop_idx, np.full(new.size, -1, dtype=np.int64)])
+            seen2 = np.concatenate([self.seen, np.zeros(new.size, dtype=np.int64)])
             order = np.argsort(keys2, kind="stable")
             self.keys, self.count = keys2[order], cnt2[order]
             self.admitted, self.prepop_idx = adm2[order], pidx2[order]
+            self.seen = seen2[order]
         # admit whatever reached the threshold and has no row yet
         idx, hit = self._find(uk)
         assert hit.all()
+        self.seen[idx] = self.step_no
+        self.step_no += 1
         fresh = (~self.admitted[idx]) & (self.count[idx] >= self.threshold)
         for k in uk[fresh].tolist():
             self.vals[k] = init_row(k, self.dim, self.init_std)
         self.admitted[idx[fresh]] = True
         return uk, self.admitted[idx]
+
+    # ------------------------------------------------------------ lifecycle
+    def evict(self, min_seen: int) -> int:
+        """Removes the keys last seen before step min_seen; returns how many."""
+        keep = self.seen >= min_seen
+        for k in self.keys[~keep].tolist():
+            self.vals.pop(int(k), None)
+        n = int((~keep).sum())
+        self.keys, self.count, self.admitted = self.keys[keep], self.count[keep], self.admitted[keep]
+        self.prepop_idx, self.seen = self.prepop_idx[keep], self.seen[keep]
+        return n
+
+    def checkpoint(self):
+        """(keys, counts, last_seen, admitted, values [n, dim], step counter), keys ascending;
+        values are zero for keys without a row."""
+        vals = np.zeros((self.keys.size, self.dim), dtype=np.float32)
+        if self.admitted.any():
+            vals[self.admitted] = self.row_values(self.keys[self.admitted])
+        return (self.keys.copy(), self.count.copy(), self.seen.copy(), self.admitted.copy(), vals,
+                self.step_no)
+
+    @classmethod
+    def restore(cls, capacity, dim, threshold, init_std, ckpt):
+        keys, counts, seen, admitted, vals, step_no = ckpt
+        T = cls(capacity, dim, threshold, init_std)
+        order = np.argsort(np.asarray(keys, dtype=np.int64), kind="stable")
+        T.keys = np.asarray(keys, dtype=np.int64)[order]
+        T.count = np.asarray(counts, dtype=np.int64)[order]
+        T.seen = np.asarray(seen, dtype=np.int64)[order]
+        T.admitted = np.asarray(admitted, dtype=bool)[order]
+        T.prepop_idx = np.full(T.keys.size, -1, dtype=np.int64)
+        vals = np.asarray(vals, dtype=np.float32)[order]
+        for k, a, v in zip(T.keys.tolist(), T.admitted.tolist(), vals):
+            if a:
+                T.vals[int(k)] = v.copy()
+        T.step_no = int(step_no)
+        return T
 
     def resolve(self, keys):
         """Per-position rows into a compact local pool for the oracle's forward:

@@ -588,6 +588,53 @@ def test_table_model_vs_dict():
         OracleTable(2, 4, 2, 0.01).step(np.array([1, 2, 3], np.int64))
 
 
+def test_table_lifecycle_vs_dict():
+    """Last-seen steps, eviction and checkpoint/restore of the table model against a
+    plain dict model: an evicted key loses count, admission and row, and starts
+    anew; a restored model continues exactly like the original."""
+    rng = np.random.default_rng(22)
+    pre = np.array([5, 6], dtype=np.int64)
+    pre_rows = rng.normal(size=(2, 4)).astype(np.float32)
+    T = OracleTable(256, 4, 2, 0.01, pre, pre_rows)
+    d = {5: dict(c=0, seen=0, row=pre_rows[0]), 6: dict(c=0, seen=0, row=pre_rows[1])}
+    for step in range(12):
+        keys = rng.integers(-1, 30, size=25).astype(np.int64)
+        T.step(keys)
+        for k in set(keys.tolist()):
+            if k < 1:
+                continue
+            e = d.setdefault(k, dict(c=0, seen=0, row=None))
+            e["c"] += int((keys == k).sum())
+            e["seen"] = step
+            if e["row"] is None and e["c"] >= 2:
+                e["row"] = oracle.init_row(k, 4, 0.01)
+        if step % 4 == 3:
+            gone = [k for k, e in d.items() if e["seen"] < step - 2]
+            for k in gone:
+                del d[k]
+            assert T.evict(step - 2) == len(gone)
+        ks = np.array(sorted(d), dtype=np.int64)
+        present, cnt, adm = T.state(ks)
+        assert present.all() and cnt.tolist() == [d[k]["c"] for k in ks.tolist()]
+        assert adm.tolist() == [d[k]["row"] is not None for k in ks.tolist()]
+        assert T.keys.size == len(d)
+        assert T.seen.tolist() == [d[k]["seen"] for k in ks.tolist()]
+        for k, a in zip(ks.tolist(), adm.tolist()):
+            if a:
+                assert np.array_equal(T.row_values([k])[0], d[k]["row"])
+    # restore from a checkpoint, then run both on the same steps
+    R = OracleTable.restore(256, 4, 2, 0.01, T.checkpoint())
+    for step in range(3):
+        keys = rng.integers(-1, 40, size=25).astype(np.int64)
+        a, b = T.step(keys), R.step(keys)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert T.evict(T.step_no - 2) == R.evict(R.step_no - 2)
+        ca, cb = T.checkpoint(), R.checkpoint()
+        for x, y in zip(ca[:5], cb[:5]):
+            assert np.array_equal(x, y)
+        assert ca[5] == cb[5]
+
+
 # --------------------------------------------------------------- generators
 
 def test_generator_statistics_training_front_end():
