@@ -20,7 +20,8 @@ __all__ = [
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
     "emb_table_rows", "emb_table_bulk_insert", "emb_table_lookup_or_insert", "emb_table_find",
-    "emb_table_export", "emb_last_error", "EmbeddingColumns", "KeyedTable",
+    "emb_table_export", "emb_table_step", "emb_table_set_step", "emb_table_track_seen", "emb_table_evict",
+    "emb_table_save", "emb_table_load", "emb_last_error", "EmbeddingColumns", "KeyedTable",
     "HASH", "IDENTITY", "BUCKET", "KEYED", "SUM", "MEAN", "F32", "BF16", "OPT_EMIT", "OPT_SGD",
     "OPT_ADAGRAD", "ROW_DROPPED", "ROW_DEFAULT", "STAT_COUNT",
 ]
@@ -32,7 +33,7 @@ OPT_EMIT, OPT_SGD, OPT_ADAGRAD = 0, 1, 2
 ROW_DROPPED, ROW_DEFAULT = -1, -2
 STAT_COUNT = 16
 STAT_NAMES = ["ids", "valid", "dropped", "default", "zero_bags", "unique", "table_inserted",
-              "table_admitted", "table_full", "max_probe", "filtered"]
+              "table_admitted", "table_full", "max_probe", "filtered", "table_evicted"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -87,6 +88,11 @@ _SIGS = {
     "emb_table_lookup_or_insert": [_VP, _VP, _I64, _VP, _VP, _VP],
     "emb_table_find": [_VP, _VP, _I64, _VP, _VP, _VP],
     "emb_table_export": [_VP, _VP, _VP, _VP, _VP, _VP],
+    "emb_table_set_step": [_VP, _I64],
+    "emb_table_track_seen": [_VP, _I32],
+    "emb_table_evict": [_VP, _I64, _VP, _VP, _VP, _VP],
+    "emb_table_save": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "emb_table_load": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP],
 }
 
 
@@ -105,6 +111,8 @@ def lib():
             fn.restype = C.c_int
         L.emb_table_rows.argtypes = [_VP]
         L.emb_table_rows.restype = _VP
+        L.emb_table_step.argtypes = [_VP]
+        L.emb_table_step.restype = C.c_int64
         L.emb_last_error.argtypes = []
         L.emb_last_error.restype = C.c_char_p
         _lib = L
@@ -251,6 +259,33 @@ def emb_table_export(table, keys, counts, rows, n_out, stream=None):
                                   _stream(stream)))
 
 
+def emb_table_step(table) -> int:
+    return int(lib().emb_table_step(table))
+
+
+def emb_table_set_step(table, step):
+    _check(lib().emb_table_set_step(table, step))
+
+
+def emb_table_track_seen(table, on):
+    _check(lib().emb_table_track_seen(table, 1 if on else 0))
+
+
+def emb_table_evict(table, min_seen, opt_state=None, n_live=None, stats=None, stream=None):
+    _check(lib().emb_table_evict(table, min_seen, _ptr(opt_state), _ptr(n_live), _ptr(stats),
+                                 _stream(stream)))
+
+
+def emb_table_save(table, keys, counts, seen, admitted, values, n_out, stream=None):
+    _check(lib().emb_table_save(table, _ptr(keys), _ptr(counts), _ptr(seen), _ptr(admitted),
+                                _ptr(values), _ptr(n_out), _stream(stream)))
+
+
+def emb_table_load(table, keys, counts, seen, admitted, values, n, stats=None, stream=None):
+    _check(lib().emb_table_load(table, _ptr(keys), _ptr(counts), _ptr(seen), _ptr(admitted),
+                                _ptr(values), n, _ptr(stats), _stream(stream)))
+
+
 # ------------------------------------------------------------- convenience
 
 def _u8(nbytes, device, zero=False):
@@ -359,7 +394,8 @@ class EmbeddingColumns:
 class KeyedTable:
     """Collisionless keyed table (device memory owned by this object)."""
 
-    def __init__(self, capacity, row_capacity, dim, threshold=2, init_std=0.01, device="cuda"):
+    def __init__(self, capacity, row_capacity, dim, threshold=2, init_std=0.01, device="cuda",
+                 track_seen=False):
         self.device = torch.device(device)
         self.capacity, self.row_capacity, self.dim = int(capacity), int(row_capacity), int(dim)
         nbytes = emb_table_query(self.capacity, self.row_capacity, self.dim)
@@ -367,6 +403,8 @@ class KeyedTable:
         self.table = emb_table_create(self.capacity, self.row_capacity, self.dim, threshold,
                                       init_std, self.mem)
         self._destroy = lib().emb_table_destroy
+        if track_seen:
+            emb_table_track_seen(self.table, True)
         ptr = emb_table_rows(self.table)
         off = ptr - self.mem.data_ptr()
         self.rows = self.mem[off:off + 4 * self.row_capacity * self.dim].view(torch.float32).view(
@@ -392,6 +430,39 @@ class KeyedTable:
         counts = torch.empty(keys.numel(), dtype=torch.int32, device=self.device)
         emb_table_find(self.table, keys, keys.numel(), rows, counts)
         return rows, counts
+
+    @property
+    def step(self) -> int:
+        """The table step the next lookup_or_insert records."""
+        return emb_table_step(self.table)
+
+    def set_step(self, step):
+        emb_table_set_step(self.table, int(step))
+
+    def evict(self, min_seen, opt_state=None, stats=None):
+        """Removes keys last seen before step min_seen; returns the live-key count
+        (a device tensor)."""
+        n_live = torch.zeros(1, dtype=torch.int64, device=self.device)
+        emb_table_evict(self.table, int(min_seen), opt_state, n_live, stats)
+        return n_live
+
+    def save(self):
+        """A checkpoint: (keys, counts, last_seen, admitted, values, step)."""
+        cap, dev = self.capacity, self.device
+        keys = torch.empty(cap, dtype=torch.int64, device=dev)
+        counts = torch.empty(cap, dtype=torch.int32, device=dev)
+        seen = torch.empty(cap, dtype=torch.int32, device=dev)
+        adm = torch.empty(cap, dtype=torch.uint8, device=dev)
+        vals = torch.empty(cap, self.dim, dtype=torch.float32, device=dev)
+        n = torch.zeros(1, dtype=torch.int64, device=dev)
+        emb_table_save(self.table, keys, counts, seen, adm, vals, n)
+        k = int(n.item())
+        return keys[:k], counts[:k], seen[:k], adm[:k], vals[:k], self.step
+
+    def load(self, ckpt, stats=None):
+        keys, counts, seen, adm, vals, step = ckpt
+        emb_table_load(self.table, keys, counts, seen, adm, vals.contiguous(), keys.numel(), stats)
+        self.set_step(step)
 
     def export(self):
         keys = torch.empty(self.capacity, dtype=torch.int64, device=self.device)

@@ -104,9 +104,16 @@ struct emb_table {
     float init_a = 0.f;            // fp32(init_std * sqrt(3)); 0 = zero rows
     int64_t *slot_keys = nullptr;  // [capacity], 0 = empty
     int32_t *slot_count = nullptr; // [capacity]
+    int32_t *slot_seen = nullptr;  // [capacity], table step that last saw the key
     int32_t *slot_row = nullptr;   // [capacity], -1 = not admitted
     float *pool = nullptr;         // [row_capacity, dim]
-    int32_t *next_row = nullptr;   // device counter of allocated rows
+    int32_t *next_row = nullptr;   // device counters: [0] rows taken from the pool's end,
+                                   // [1] rows on the free list, [2] live keys, [3] evicted
+    int32_t *free_rows = nullptr;  // [row_capacity], rows freed by eviction (a stack)
+    int64_t *tmp_keys = nullptr;   // [capacity] eviction: the live slots, compacted
+    int32_t *tmp_count = nullptr, *tmp_row = nullptr, *tmp_seen = nullptr;
+    int64_t step = 0;              // lookups so far: the step the next lookup records
+    bool track_seen = false;       // lookups record last-seen steps
     size_t bytes = 0;
 };
 

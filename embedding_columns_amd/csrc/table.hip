@@ -14,6 +14,10 @@
 //   ht_admit    a slot whose count reached the threshold and has no row claims
 //               one (CAS on the row field), takes a pool row and initializes it
 //   ht_resolve  every occurrence reads its slot's row, or DEFAULT
+//
+// Lifecycle: each slot also keeps the table step that last saw its key; eviction
+// (ht_evict_scan, ht_clear, ht_reinsert) frees the rows of keys unseen since a
+// given step onto a free list and rebuilds the slot array from the live keys.
 #include <algorithm>
 #include <cmath>
 #include <string>
@@ -26,15 +30,25 @@ constexpr int32_t kSlotNoRow = -1;
 constexpr int32_t kSlotClaim = -3;     // row being allocated by one thread
 constexpr int32_t kPosRefused = -3;    // per-position code between the launches
 
+// device counters (emb_table::next_row)
+constexpr int kCtrBump = 0;    // rows taken from the unused end of the pool
+constexpr int kCtrFree = 1;    // rows on the free list (below zero after failed pops: empty)
+constexpr int kCtrLive = 2;    // eviction: live keys compacted so far
+constexpr int kCtrEvicted = 3; // eviction: keys removed
+
 struct TabArgs {
     unsigned long long *keys;   // slot keys (0 = empty)
     int32_t *count;
     int32_t *row;
+    int32_t *seen;              // last-seen table step (written only when tracking)
     float *pool;
-    int32_t *next_row;
+    int32_t *next_row;          // the counters above
+    int32_t *free_rows;
     int64_t cap, row_cap;
     int32_t dim, threshold;
     float init_a;
+    int32_t step;
+    int32_t track;              // record last-seen steps in lookups (emb_table_track_seen)
 };
 
 static TabArgs tab_args(const emb_table &t)
@@ -42,9 +56,13 @@ static TabArgs tab_args(const emb_table &t)
     TabArgs a;
     a.keys = reinterpret_cast<unsigned long long *>(t.slot_keys);
     a.count = t.slot_count;
+    a.seen = t.slot_seen;
     a.row = t.slot_row;
     a.pool = t.pool;
     a.next_row = t.next_row;
+    a.free_rows = t.free_rows;
+    a.step = (int32_t)t.step;
+    a.track = t.track_seen ? 1 : 0;
     a.cap = t.capacity;
     a.row_cap = t.row_capacity;
     a.dim = t.dim;
@@ -198,6 +216,22 @@ __device__ __forceinline__ void init_row(const TabArgs &a, int64_t r, unsigned l
     }
 }
 
+// A row for a newly admitted key: one from the free list if any, else the next
+// unused one; -1 if the pool is exhausted.  Pops happen only in admission
+// kernels and pushes only in eviction, which never overlap: the first F pops of
+// a launch (F = the list's size) get distinct entries, later ones see an empty
+// list.  The load before the decrement keeps the counter from drifting far
+// below zero; eviction clamps it back to zero before pushing.
+__device__ __forceinline__ int32_t alloc_row(const TabArgs &a)
+{
+    if (__hip_atomic_load(&a.next_row[kCtrFree], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 0) {
+        const int32_t f = atomicSub(&a.next_row[kCtrFree], 1) - 1;
+        if (f >= 0) return __hip_atomic_load(&a.free_rows[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int32_t r = atomicAdd(&a.next_row[kCtrBump], 1);
+    return (int64_t)r < a.row_cap ? r : -1;
+}
+
 __device__ __forceinline__ void stat_add(int64_t *stats, int idx, int64_t v)
 {
     const int64_t s = wave_sum_i64(v);
@@ -268,8 +302,14 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kLdsSlots; i += kCountTile)
-        if (lslot[i] >= 0) atomicAdd(&a.count[lslot[i]], lcnt[i]);
+    // each distinct slot once per block: its count, and (when tracking) this step as
+    // its last-seen step (every block stores the same value)
+    for (int i = threadIdx.x; i < kLdsSlots; i += kCountTile) {
+        if (lslot[i] >= 0) {
+            atomicAdd(&a.count[lslot[i]], lcnt[i]);
+            if (a.track) a.seen[lslot[i]] = a.step;
+        }
+    }
     if (stats && threadIdx.x == 0) {
         if (lstat[0]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_INSERTED], lstat[0]);
         if (lstat[1]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_FULL], lstat[1]);
@@ -288,8 +328,8 @@ __global__ __launch_bounds__(kBlock) void ht_admit(TabArgs a, const int64_t *__r
         if (s >= 0 && __hip_atomic_load(&a.row[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSlotNoRow &&
             a.count[s] >= a.threshold) {
             if (atomicCAS(&a.row[s], kSlotNoRow, kSlotClaim) == kSlotNoRow) {
-                const int32_t r = atomicAdd(a.next_row, 1);
-                if ((int64_t)r < a.row_cap) {
+                const int32_t r = alloc_row(a);
+                if (r >= 0) {
                     init_row(a, r, (unsigned long long)keys[p]);
                     atomicExch(&a.row[s], r);
                     adm = 1;
@@ -333,8 +373,9 @@ __global__ __launch_bounds__(kBlock) void ht_bulk(TabArgs a, const int64_t *__re
                 full = 1;
             } else if (inserted) {
                 ins = 1;
-                const int32_t r = atomicAdd(a.next_row, 1);
-                if ((int64_t)r < a.row_cap) {
+                a.seen[s] = a.step;
+                const int32_t r = alloc_row(a);
+                if (r >= 0) {
                     adm = 1;
                     if (rows) {
                         const float4 *src = reinterpret_cast<const float4 *>(rows + p * a.dim);
@@ -397,13 +438,176 @@ __global__ __launch_bounds__(kBlock) void ht_export(TabArgs a, int64_t *__restri
     }
 }
 
+// ---------------------------------------------------------------- lifecycle
+
+__global__ void ht_evict_prep(TabArgs a)
+{
+    if (threadIdx.x == 0) {
+        a.next_row[kCtrFree] = max(a.next_row[kCtrFree], 0);
+        a.next_row[kCtrLive] = 0;
+        a.next_row[kCtrEvicted] = 0;
+    }
+}
+
+// one slot per thread: an expired key's row goes to the free list, a live key is
+// appended (with its count, row and step) to the compaction buffers
+__global__ __launch_bounds__(kBlock) void ht_evict_scan(TabArgs a, int32_t min_seen,
+                                                       float *__restrict__ opt_state,
+                                                       int64_t *__restrict__ tkeys,
+                                                       int32_t *__restrict__ tcount,
+                                                       int32_t *__restrict__ trow,
+                                                       int32_t *__restrict__ tseen)
+{
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const unsigned long long key = s < a.cap ? a.keys[s] : 0ull;
+    const bool occ = key != 0ull;
+    const bool live = occ && a.seen[s] >= min_seen;
+    if (occ && !live) {
+        const int32_t r = a.row[s];
+        if (r >= 0) {
+            const int32_t i = atomicAdd(&a.next_row[kCtrFree], 1);
+            a.free_rows[i] = r;
+            if (opt_state) {         // the next key to get this row starts from zero state
+                float4 *z = reinterpret_cast<float4 *>(opt_state + (int64_t)r * a.dim);
+                for (int d = 0; d < a.dim / 4; d++) z[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    }
+    const uint64_t m = __ballot(live);
+    const int lane = lane_id();
+    const int64_t ev = wave_sum_i64(occ && !live);
+    if (lane == 0 && ev) atomicAdd(&a.next_row[kCtrEvicted], (int32_t)ev);
+    if (!m) return;
+    const int leader = __ffsll((long long)m) - 1;
+    int32_t base = 0;
+    if (lane == leader) base = atomicAdd(&a.next_row[kCtrLive], __popcll(m));
+    base = __shfl(base, leader, kWave);
+    if (live) {
+        const int32_t i = base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        tkeys[i] = (int64_t)key;
+        tcount[i] = a.count[s];
+        trow[i] = a.row[s];
+        tseen[i] = a.seen[s];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void ht_clear(TabArgs a)
+{
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (s >= a.cap) return;
+    a.keys[s] = 0ull;
+    a.count[s] = 0;
+    a.row[s] = kSlotNoRow;
+    a.seen[s] = 0;
+}
+
+// the live keys back into the cleared slots (all distinct, at most cap of them,
+// so every insert finds a slot)
+__global__ __launch_bounds__(kBlock) void ht_reinsert(TabArgs a, const int64_t *__restrict__ tkeys,
+                                                     const int32_t *__restrict__ tcount,
+                                                     const int32_t *__restrict__ trow,
+                                                     const int32_t *__restrict__ tseen,
+                                                     int64_t *n_live, int64_t *stats)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int32_t live = a.next_row[kCtrLive];
+    if (i == 0) {
+        if (n_live) *n_live = live;
+        if (stats && a.next_row[kCtrEvicted])
+            atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_EVICTED],
+                      (unsigned long long)a.next_row[kCtrEvicted]);
+    }
+    if (i >= live) return;
+    bool inserted;
+    int64_t probes;
+    const int64_t s = probe_insert(a, (unsigned long long)tkeys[i], inserted, probes);
+    if (s < 0) return;                  // cannot happen: live <= cap distinct keys
+    a.count[s] = tcount[i];
+    a.row[s] = trow[i];
+    a.seen[s] = tseen[i];
+}
+
+// checkpoint: every occupied slot with its row values
+__global__ __launch_bounds__(kBlock) void ht_save(TabArgs a, int64_t *__restrict__ keys,
+                                                 int32_t *__restrict__ counts,
+                                                 int32_t *__restrict__ seen,
+                                                 uint8_t *__restrict__ admitted,
+                                                 float *__restrict__ values,
+                                                 unsigned long long *n_out)
+{
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const bool occ = s < a.cap && a.keys[s] != 0ull;
+    const uint64_t m = __ballot(occ);
+    if (!m) return;
+    unsigned long long base = 0;
+    const int lane = lane_id();
+    const int leader = __ffsll((long long)m) - 1;
+    if (lane == leader) base = atomicAdd(n_out, (unsigned long long)__popcll(m));
+    base = __shfl(base, leader, kWave);
+    if (occ) {
+        const uint64_t below = m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+        const int64_t i = (int64_t)base + __popcll(below);
+        const int32_t r = a.row[s];
+        keys[i] = (int64_t)a.keys[s];
+        counts[i] = a.count[s];
+        seen[i] = a.seen[s];
+        admitted[i] = r >= 0;
+        float4 *dst = reinterpret_cast<float4 *>(values + i * a.dim);
+        const float4 *src = reinterpret_cast<const float4 *>(a.pool + (int64_t)max(r, 0) * a.dim);
+        for (int d = 0; d < a.dim / 4; d++) dst[d] = r >= 0 ? src[d] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void ht_load(TabArgs a, const int64_t *__restrict__ keys,
+                                                 const int32_t *__restrict__ counts,
+                                                 const int32_t *__restrict__ seen,
+                                                 const uint8_t *__restrict__ admitted,
+                                                 const float *__restrict__ values, int64_t n,
+                                                 int64_t *stats)
+{
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    int64_t ins = 0, adm = 0, full = 0, probes = 0;
+    if (p < n && keys[p] >= 1) {
+        bool inserted;
+        const int64_t s = probe_insert(a, (unsigned long long)keys[p], inserted, probes);
+        if (s < 0) {
+            full = 1;
+        } else if (inserted) {
+            ins = 1;
+            a.count[s] = counts[p];
+            a.seen[s] = seen[p];
+            if (admitted[p]) {
+                const int32_t r = alloc_row(a);
+                if (r >= 0) {
+                    const float4 *src = reinterpret_cast<const float4 *>(values + p * a.dim);
+                    float4 *dst = reinterpret_cast<float4 *>(a.pool + (int64_t)r * a.dim);
+                    for (int d = 0; d < a.dim / 4; d++) dst[d] = src[d];
+                    a.row[s] = r;
+                    adm = 1;
+                } else {
+                    full = 1;
+                }
+            }
+        }
+    }
+    stat_add(stats, EMB_STAT_TABLE_INSERTED, ins);
+    stat_add(stats, EMB_STAT_TABLE_ADMITTED, adm);
+    stat_add(stats, EMB_STAT_TABLE_FULL, full);
+    stat_max(stats, EMB_STAT_MAX_PROBE, probes);
+}
+
 }  // namespace emb
 
 using namespace emb;
 
 static size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static emb_status table_sizes(int64_t capacity, int64_t row_capacity, int32_t dim, size_t off[5])
+// device memory: slot keys, counts, rows, last-seen steps; the counters; the
+// free list; the eviction's compaction buffers; the row pool
+enum { kOffKeys, kOffCount, kOffSeen, kOffRow, kOffCtr, kOffFree, kOffTmpKeys, kOffTmpCount,
+       kOffTmpRow, kOffTmpSeen, kOffPool, kNumOff };
+
+static emb_status table_sizes(int64_t capacity, int64_t row_capacity, int32_t dim, size_t off[kNumOff])
 {
     if (capacity < 2 || capacity > (int64_t(1) << 30) || (capacity & (capacity - 1)))
         return fail(EMB_ERR_INVALID_ARG, "capacity must be a power of two in [2, 2^30]");
@@ -411,12 +615,19 @@ static emb_status table_sizes(int64_t capacity, int64_t row_capacity, int32_t di
         return fail(EMB_ERR_INVALID_ARG, "row_capacity must be in [1, 2^31-1]");
     if (dim <= 0 || dim % 4 || dim > kMaxDimF32)
         return fail(EMB_ERR_UNSUPPORTED, "table dim must be a multiple of 4 and <= 256");
+    const size_t cap = (size_t)capacity;
     size_t o = 0;
-    off[0] = o; o = a256(o + 8 * (size_t)capacity);     // keys
-    off[1] = o; o = a256(o + 4 * (size_t)capacity);     // counts
-    off[2] = o; o = a256(o + 4 * (size_t)capacity);     // rows
-    off[3] = o; o = a256(o + 256);                      // next_row
-    off[4] = o;                                         // row pool [row_capacity, dim]
+    off[kOffKeys] = o; o = a256(o + 8 * cap);
+    off[kOffCount] = o; o = a256(o + 4 * cap);
+    off[kOffSeen] = o; o = a256(o + 4 * cap);
+    off[kOffRow] = o; o = a256(o + 4 * cap);
+    off[kOffCtr] = o; o = a256(o + 256);
+    off[kOffFree] = o; o = a256(o + 4 * (size_t)row_capacity);
+    off[kOffTmpKeys] = o; o = a256(o + 8 * cap);
+    off[kOffTmpCount] = o; o = a256(o + 4 * cap);
+    off[kOffTmpRow] = o; o = a256(o + 4 * cap);
+    off[kOffTmpSeen] = o; o = a256(o + 4 * cap);
+    off[kOffPool] = o;                                  // row pool [row_capacity, dim]
     return EMB_OK;
 }
 
@@ -425,10 +636,10 @@ extern "C" {
 emb_status emb_table_query(int64_t capacity, int64_t row_capacity, int32_t dim, size_t *table_bytes)
 {
     if (!table_bytes) return fail(EMB_ERR_INVALID_ARG, "table_bytes is NULL");
-    size_t off[5];
+    size_t off[kNumOff];
     emb_status s = table_sizes(capacity, row_capacity, dim, off);
     if (s != EMB_OK) return s;
-    *table_bytes = off[4] + a256(4 * (size_t)row_capacity * (size_t)dim);
+    *table_bytes = off[kOffPool] + a256(4 * (size_t)row_capacity * (size_t)dim);
     return EMB_OK;
 }
 
@@ -437,7 +648,7 @@ emb_status emb_table_create(int64_t capacity, int64_t row_capacity, int32_t dim,
 {
     if (!out) return fail(EMB_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    size_t off[5];
+    size_t off[kNumOff];
     emb_status s = table_sizes(capacity, row_capacity, dim, off);
     if (s != EMB_OK) return s;
     if (!table_mem || !aligned(table_mem, 256)) return fail(EMB_ERR_INVALID_ARG, "table_mem must be 256-byte aligned device memory");
@@ -451,13 +662,19 @@ emb_status emb_table_create(int64_t capacity, int64_t row_capacity, int32_t dim,
     T->dim = dim;
     T->threshold = threshold;
     T->init_a = (float)((double)init_std * std::sqrt(3.0));
-    T->slot_keys = reinterpret_cast<int64_t *>(m + off[0]);
-    T->slot_count = reinterpret_cast<int32_t *>(m + off[1]);
-    T->slot_row = reinterpret_cast<int32_t *>(m + off[2]);
-    T->next_row = reinterpret_cast<int32_t *>(m + off[3]);
-    T->pool = reinterpret_cast<float *>(m + off[4]);
+    T->slot_keys = reinterpret_cast<int64_t *>(m + off[kOffKeys]);
+    T->slot_count = reinterpret_cast<int32_t *>(m + off[kOffCount]);
+    T->slot_seen = reinterpret_cast<int32_t *>(m + off[kOffSeen]);
+    T->slot_row = reinterpret_cast<int32_t *>(m + off[kOffRow]);
+    T->next_row = reinterpret_cast<int32_t *>(m + off[kOffCtr]);
+    T->free_rows = reinterpret_cast<int32_t *>(m + off[kOffFree]);
+    T->tmp_keys = reinterpret_cast<int64_t *>(m + off[kOffTmpKeys]);
+    T->tmp_count = reinterpret_cast<int32_t *>(m + off[kOffTmpCount]);
+    T->tmp_row = reinterpret_cast<int32_t *>(m + off[kOffTmpRow]);
+    T->tmp_seen = reinterpret_cast<int32_t *>(m + off[kOffTmpSeen]);
+    T->pool = reinterpret_cast<float *>(m + off[kOffPool]);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemsetAsync(m, 0, off[2], st);                               // keys, counts
+    hipError_t e = hipMemsetAsync(m, 0, off[kOffRow], st);                 // keys, counts, steps
     if (e == hipSuccess) e = hipMemsetAsync(T->slot_row, 0xFF, 4 * (size_t)capacity, st);   // rows = -1
     if (e == hipSuccess) e = hipMemsetAsync(T->next_row, 0, 256, st);
     if (e != hipSuccess) {
@@ -509,6 +726,7 @@ emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int
     hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_admit, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_resolve, dim3(grid_of(n)), dim3(kBlock), 0, st, a, n, rows_out);
+    table->step++;
     return launched("lookup_or_insert");
 }
 
@@ -532,6 +750,67 @@ emb_status emb_table_export(emb_table *table, int64_t *keys, int32_t *counts, in
     hipLaunchKernelGGL(ht_export, dim3(grid_of(table->capacity)), dim3(kBlock), 0, st, tab_args(*table),
                        keys, counts, rows, reinterpret_cast<unsigned long long *>(n_out));
     return launched("ht_export");
+}
+
+int64_t emb_table_step(const emb_table *table) { return table ? table->step : -1; }
+
+emb_status emb_table_track_seen(emb_table *table, int32_t on)
+{
+    if (!table) return fail(EMB_ERR_INVALID_ARG, "table is NULL");
+    table->track_seen = on != 0;
+    return EMB_OK;
+}
+
+emb_status emb_table_set_step(emb_table *table, int64_t step)
+{
+    if (!table || step < 0 || step > INT32_MAX) return fail(EMB_ERR_INVALID_ARG, "bad table step");
+    table->step = step;
+    return EMB_OK;
+}
+
+emb_status emb_table_evict(emb_table *table, int64_t min_seen, float *opt_state, int64_t *n_live,
+                           int64_t *stats, void *stream)
+{
+    if (!table) return fail(EMB_ERR_INVALID_ARG, "table is NULL");
+    if (opt_state && !aligned(opt_state, 16)) return fail(EMB_ERR_INVALID_ARG, "opt_state must be 16-byte aligned");
+    const int32_t ms = (int32_t)std::min<int64_t>(std::max<int64_t>(min_seen, INT32_MIN), INT32_MAX);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const TabArgs a = tab_args(*table);
+    const unsigned g = grid_of(table->capacity);
+    hipLaunchKernelGGL(ht_evict_prep, dim3(1), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL(ht_evict_scan, dim3(g), dim3(kBlock), 0, st, a, ms, opt_state, table->tmp_keys,
+                       table->tmp_count, table->tmp_row, table->tmp_seen);
+    hipLaunchKernelGGL(ht_clear, dim3(g), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(ht_reinsert, dim3(g), dim3(kBlock), 0, st, a, table->tmp_keys,
+                       table->tmp_count, table->tmp_row, table->tmp_seen, n_live, stats);
+    return launched("emb_table_evict");
+}
+
+emb_status emb_table_save(emb_table *table, int64_t *keys, int32_t *counts, int32_t *seen,
+                          uint8_t *admitted, float *values, int64_t *n_out, void *stream)
+{
+    if (!table || !keys || !counts || !seen || !admitted || !values || !n_out)
+        return fail(EMB_ERR_INVALID_ARG, "bad save arguments");
+    if (!aligned(values, 16)) return fail(EMB_ERR_INVALID_ARG, "values must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemsetAsync(n_out, 0, sizeof(int64_t), st);
+    if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("save clear: ") + hipGetErrorString(e));
+    hipLaunchKernelGGL(ht_save, dim3(grid_of(table->capacity)), dim3(kBlock), 0, st, tab_args(*table),
+                       keys, counts, seen, admitted, values, reinterpret_cast<unsigned long long *>(n_out));
+    return launched("ht_save");
+}
+
+emb_status emb_table_load(emb_table *table, const int64_t *keys, const int32_t *counts,
+                          const int32_t *seen, const uint8_t *admitted, const float *values,
+                          int64_t n, int64_t *stats, void *stream)
+{
+    if (!table || n < 0 || (n > 0 && (!keys || !counts || !seen || !admitted || !values)))
+        return fail(EMB_ERR_INVALID_ARG, "bad load arguments");
+    if (values && !aligned(values, 16)) return fail(EMB_ERR_INVALID_ARG, "values must be 16-byte aligned");
+    if (n == 0) return EMB_OK;
+    hipLaunchKernelGGL(ht_load, dim3(grid_of(n)), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       tab_args(*table), keys, counts, seen, admitted, values, n, stats);
+    return launched("ht_load");
 }
 
 }  // extern "C"

@@ -86,6 +86,7 @@ typedef enum {
 #define EMB_STAT_TABLE_FULL     8  /* key occurrences refused: no free slot or row   */
 #define EMB_STAT_MAX_PROBE      9  /* longest probe sequence seen (max, not sum)     */
 #define EMB_STAT_FILTERED      10  /* positions removed by sequence truncation or the mask */
+#define EMB_STAT_TABLE_EVICTED 11  /* keys removed by emb_table_evict                  */
 #define EMB_STAT_COUNT         16
 
 /* One embedding column (host struct), in output order.  Row-major tables. */
@@ -320,6 +321,52 @@ emb_status emb_table_find(emb_table *table, const int64_t *keys, int64_t n, int3
  * rows int32 (-1 if not admitted), each [capacity]; n_out int64 device scalar. */
 emb_status emb_table_export(emb_table *table, int64_t *keys, int32_t *counts, int32_t *rows,
                             int64_t *n_out, void *stream);
+
+/*
+ * Table lifecycle (Monolith Sec. 2.1 expires IDs that stay inactive, so that the
+ * table holds the live features only).  Every emb_table_lookup_or_insert is one
+ * table step: step k (k = 0, 1, ...) records k as the last-seen step of each key
+ * it finds or inserts, once tracking is on (emb_table_track_seen; off by
+ * default: the record costs one scattered store per distinct key per 1024
+ * occurrences, about 7 % of the keyed training step, and keys inserted while it
+ * is off keep last-seen 0); emb_table_bulk_insert and emb_table_load always
+ * record the current step.  Rows freed by eviction go to a free list that admission takes
+ * from before the unused end of the pool.  None of these calls may overlap
+ * another call on the same table.
+ *
+ * emb_table_step: the step the next lookup-or-insert will record (host value).
+ * emb_table_set_step: sets it (restoring a checkpoint).
+ *
+ * emb_table_evict: removes every key whose last-seen step is < min_seen: its slot,
+ *   count and admission are dropped and its row goes to the free list (a later
+ *   occurrence starts the key anew).  The slot array is rebuilt from the live keys
+ *   (compaction), so probe sequences stay short.  Row indices of live keys do not
+ *   change.  opt_state: fp32 [row_capacity, dim] optimizer state of the column
+ *   using the table, or NULL: the freed rows' state is zeroed.  n_live: int64
+ *   device scalar or NULL (live keys after the call); stats gets
+ *   EMB_STAT_TABLE_EVICTED.  Callers evict by age (min_seen = step - max_age)
+ *   or when their count of keys reaches a load limit.
+ *
+ * emb_table_save: a checkpoint of every key, in unspecified order: keys int64,
+ *   counts int32, last-seen steps int32, admitted uint8 (1 = has a row), values
+ *   fp32 [capacity, dim] (the row, or zeros), each with room for `capacity`
+ *   entries; n_out int64 device scalar.  Together with emb_table_step it is the
+ *   table's whole state.
+ * emb_table_load: inserts n checkpoint entries in that layout into a table:
+ *   absent keys get their count and last-seen step, and admitted ones a row with
+ *   the saved values (row pool full: not admitted, counted in
+ *   EMB_STAT_TABLE_FULL); keys already present are left as they are.
+ */
+int64_t emb_table_step(const emb_table *table);
+emb_status emb_table_track_seen(emb_table *table, int32_t on);
+emb_status emb_table_set_step(emb_table *table, int64_t step);
+emb_status emb_table_evict(emb_table *table, int64_t min_seen, float *opt_state, int64_t *n_live,
+                           int64_t *stats, void *stream);
+emb_status emb_table_save(emb_table *table, int64_t *keys, int32_t *counts, int32_t *seen,
+                          uint8_t *admitted, float *values, int64_t *n_out, void *stream);
+emb_status emb_table_load(emb_table *table, const int64_t *keys, const int32_t *counts,
+                          const int32_t *seen, const uint8_t *admitted, const float *values,
+                          int64_t n, int64_t *stats, void *stream);
 
 /* Message for the last non-OK status on this host thread. */
 const char *emb_last_error(void);

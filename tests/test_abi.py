@@ -125,4 +125,9 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_forward_ex(None, None, None, None, None, None, None, 0, None, None, 0, None,
                                   None) == 1
     assert L.lib().emb_transform(None, None, None, None, None, None, 0, None, None, None) == 1
+    assert L.lib().emb_table_evict(None, 0, None, None, None, None) == 1
+    assert L.lib().emb_table_save(None, None, None, None, None, None, None, None) == 1
+    assert L.lib().emb_table_load(None, None, None, None, None, None, 0, None, None) == 1
+    assert L.lib().emb_table_set_step(None, 0) == 1 and L.lib().emb_table_step(None) == -1
+    assert L.lib().emb_table_track_seen(None, 1) == 1
     assert L.lib().emb_forward_rows(None, None, None, None, 0, None, None, 0, None, None) == 1
