@@ -23,12 +23,32 @@ table holds only live features):
   admission and its row values are gone, and a later occurrence starts it anew;
   a checkpoint is (keys, counts, last_seen, admitted, values, step counter), and
   a table restored from it behaves exactly like the original.
+
+Count-min admission (optional; Monolith Sec. 2.1 filters IDs by frequency, and a
+probabilistic filter avoids holding a slot for every rare ID): keys not in the
+table are counted in a d x w sketch instead of slots.  Cell j of key k is
+h_j(k) = x_j mod w, where x_0, x_1, ... are the outputs of a SplitMix64 generator
+seeded with k (x_j = splitmix64(k + j * gamma), gamma = 0x9E3779B97F4A7C15).  A
+step adds m_k to the d cells of every absent key, then each absent key whose
+estimate min_j C[j, h_j(k)] reaches the threshold enters the table with
+count = its estimate and a fresh row; the others read DEFAULT.  Keys in the
+table count exactly, as above.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import ROW_DEFAULT, ROW_DROPPED, init_row
+from . import ROW_DEFAULT, ROW_DROPPED, init_row, splitmix64
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+
+
+def count_min_cells(keys, depth: int, width: int) -> np.ndarray:
+    """[depth, n] sketch cells of the keys: SplitMix64 output j of seed k, mod width."""
+    k = np.asarray(keys, dtype=np.int64).astype(np.uint64)
+    with np.errstate(over="ignore"):
+        return np.stack([splitmix64(k + np.uint64(j) * GAMMA) % np.uint64(width)
+                         for j in range(depth)]).astype(np.int64)
 
 
 class TableFull(RuntimeError):
@@ -52,11 +72,15 @@ class OracleTable:
         self.admitted = np.ones(self.keys.size, dtype=bool)
         self.step_no = 0
         self.seen = np.zeros(self.keys.size, dtype=np.int64)
+        self.sketch = None                                # count-min: int64 [depth, width]
         self.prepop_idx = order.astype(np.int64)         # index into the prepop rows
         self._prepop_rows = prepop_rows
         self.vals = {}                                    # key -> row values (new or updated)
         if self.keys.size > capacity:
             raise TableFull("prepopulation exceeds capacity")
+
+    def use_count_min(self, depth: int, width: int):
+        self.sketch = np.zeros((depth, width), dtype=np.int64)
 
     # ------------------------------------------------------------- queries
     def _find(self, k: np.ndarray):
@@ -98,6 +122,22 @@ class OracleTable:
         valid = keys >= 1
         uk, m = np.unique(keys[valid], return_counts=True)
         idx, hit = self._find(uk)
+        new_cnt = m[~hit]
+        if self.sketch is not None:
+            # absent keys: add the step's occurrences to the sketch, then admit
+            # those whose estimate reached the threshold
+            absent, ma = uk[~hit], m[~hit]
+            cells = count_min_cells(absent, *self.sketch.shape)
+            for j in range(self.sketch.shape[0]):
+                np.add.at(self.sketch[j], cells[j], ma)
+            est = (np.min(np.stack([self.sketch[j][cells[j]] for j in range(self.sketch.shape[0])]),
+                          axis=0) if absent.size else np.zeros(0, np.int64))
+            enter = est >= self.threshold
+            hit = hit.copy()
+            keep = np.ones(uk.size, dtype=bool)
+            keep[np.nonzero(~hit)[0][~enter]] = False       # stay in the sketch only
+            new_cnt = est[enter]
+            uk, m, idx, hit = uk[keep], m[keep], idx[keep], hit[keep]
         new = uk[~hit]
         if self.keys.size + new.size > self.capacity:
             raise TableFull(f"{new.size} new keys, {self.capacity - self.keys.size} free slots")
@@ -107,7 +147,7 @@ class OracleTable:
         # insert the absent keys with their counts
         if new.size:
             keys2 = np.concatenate([self.keys, new])
-            cnt2 = np.concatenate([self.count, m[~hit]])
+            cnt2 = np.concatenate([self.count, new_cnt])
             adm2 = np.concatenate([self.admitted, np.zeros(new.size, dtype=bool)])
             pidx2 = np.concatenate([self.prepop_idx, np.full(new.size, -1, dtype=np.int64)])
             seen2 = np.concatenate([self.seen, np.zeros(new.size, dtype=np.int64)])

@@ -635,6 +635,69 @@ def test_table_lifecycle_vs_dict():
         assert ca[5] == cb[5]
 
 
+def test_count_min_cells_are_splitmix64_outputs():
+    """Cell j of key k is output j of a SplitMix64 generator seeded with k (the
+    published vectors), reduced mod the width."""
+    from oracle.table import count_min_cells
+    with open(os.path.join(GOLDEN, "splitmix64_vectors.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    by_seed = {}
+    for seed, i, out in rows:
+        by_seed.setdefault(int(seed), {})[int(i)] = int(out)
+    for seed, outs in by_seed.items():
+        if seed >= 1 << 63:
+            continue
+        depth = max(outs) + 1
+        for width in (1 << 62, 1000):
+            cells = count_min_cells(np.array([seed], np.int64), depth, width)[:, 0]
+            for j, out in outs.items():
+                assert int(cells[j]) == out % width
+
+
+def test_count_min_admission_vs_brute_force_and_exact():
+    """The count-min model against a per-occurrence brute force with a narrow
+    sketch (many collisions), and against exact counting with a wide one."""
+    from oracle.table import count_min_cells
+    rng = np.random.default_rng(23)
+    steps = [rng.integers(-1, 400, size=120).astype(np.int64) for _ in range(8)]
+    for width, depth in ((16, 3), (1 << 24, 3)):
+        T = OracleTable(1024, 4, 3, 0.01)
+        T.use_count_min(depth, width)
+        E = OracleTable(1024, 4, 3, 0.01)                # exact counting in slots
+        C = np.zeros((depth, width), dtype=np.int64)
+        table = {}                                       # key -> count (keys in the table)
+        for keys in steps:
+            m = {}
+            for k in keys.tolist():
+                if k >= 1:
+                    m[k] = m.get(k, 0) + 1
+            absent = [k for k in m if k not in table]
+            for k in absent:
+                cells = count_min_cells(np.array([k], np.int64), depth, width)[:, 0]
+                for j in range(depth):
+                    C[j, cells[j]] += m[k]
+            for k in m:
+                if k in table:
+                    table[k] += m[k]
+            for k in absent:
+                cells = count_min_cells(np.array([k], np.int64), depth, width)[:, 0]
+                est = min(C[j, cells[j]] for j in range(depth))
+                if est >= 3:
+                    table[k] = int(est)
+            T.step(keys)
+            E.step(keys)
+            assert T.keys.tolist() == sorted(table)
+            assert T.count.tolist() == [table[k] for k in sorted(table)]
+            assert T.admitted.all()                      # enter with count >= threshold
+            rows, _, _ = T.resolve(keys)
+            for k, r in zip(keys.tolist(), rows.tolist()):
+                assert (r >= 0) == (k in table) and (r == oracle.ROW_DROPPED) == (k < 1)
+            if width > 1 << 20:                          # no collisions: the exact outcome
+                assert np.array_equal(rows, E.resolve(keys)[0])
+                _, ec, ea = E.state(T.keys)
+                assert np.array_equal(ec, T.count) and ea.all()
+
+
 # --------------------------------------------------------------- generators
 
 def test_generator_statistics_training_front_end():
