@@ -20,7 +20,8 @@ __all__ = [
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
     "emb_table_rows", "emb_table_bulk_insert", "emb_table_lookup_or_insert", "emb_table_find",
-    "emb_table_export", "emb_table_step", "emb_table_set_step", "emb_table_track_seen", "emb_table_evict",
+    "emb_table_export", "emb_table_step", "emb_table_set_step", "emb_table_track_seen", "emb_table_use_count_min",
+    "emb_table_evict",
     "emb_table_save", "emb_table_load", "emb_last_error", "EmbeddingColumns", "KeyedTable",
     "HASH", "IDENTITY", "BUCKET", "KEYED", "SUM", "MEAN", "F32", "BF16", "OPT_EMIT", "OPT_SGD",
     "OPT_ADAGRAD", "ROW_DROPPED", "ROW_DEFAULT", "STAT_COUNT",
@@ -90,6 +91,7 @@ _SIGS = {
     "emb_table_export": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_table_set_step": [_VP, _I64],
     "emb_table_track_seen": [_VP, _I32],
+    "emb_table_use_count_min": [_VP, _I32, _I64, _VP],
     "emb_table_evict": [_VP, _I64, _VP, _VP, _VP, _VP],
     "emb_table_save": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_table_load": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP],
@@ -267,6 +269,10 @@ def emb_table_set_step(table, step):
     _check(lib().emb_table_set_step(table, step))
 
 
+def emb_table_use_count_min(table, depth, width, sketch):
+    _check(lib().emb_table_use_count_min(table, depth, width, _ptr(sketch)))
+
+
 def emb_table_track_seen(table, on):
     _check(lib().emb_table_track_seen(table, 1 if on else 0))
 
@@ -430,6 +436,11 @@ class KeyedTable:
         counts = torch.empty(keys.numel(), dtype=torch.int32, device=self.device)
         emb_table_find(self.table, keys, keys.numel(), rows, counts)
         return rows, counts
+
+    def use_count_min(self, depth, width):
+        """Count-min admission with a fresh depth x width sketch (owned by this object)."""
+        self.sketch = torch.zeros(depth, width, dtype=torch.int32, device=self.device)
+        emb_table_use_count_min(self.table, depth, width, self.sketch)
 
     @property
     def step(self) -> int:

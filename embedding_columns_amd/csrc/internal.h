@@ -114,6 +114,9 @@ struct emb_table {
     int32_t *tmp_count = nullptr, *tmp_row = nullptr, *tmp_seen = nullptr;
     int64_t step = 0;              // lookups so far: the step the next lookup records
     bool track_seen = false;       // lookups record last-seen steps
+    int32_t *sketch = nullptr;     // count-min admission counters [cm_depth][cm_width], or NULL
+    int32_t cm_depth = 0;
+    int64_t cm_width = 0;
     size_t bytes = 0;
 };
 

@@ -29,6 +29,14 @@ namespace emb {
 constexpr int32_t kSlotNoRow = -1;
 constexpr int32_t kSlotClaim = -3;     // row being allocated by one thread
 constexpr int32_t kPosRefused = -3;    // per-position code between the launches
+constexpr int32_t kPosPending = -4;    // count-min: absent key, counted in the sketch
+
+// Count-min cell of sketch row j for a key: output j of a SplitMix64 generator
+// seeded with the key (splitmix64(key + j * gamma)), modulo the power-of-two width.
+__device__ __forceinline__ uint64_t cm_cell(uint64_t key, int j, uint64_t wmask)
+{
+    return splitmix64(key + (uint64_t)j * 0x9E3779B97F4A7C15ull) & wmask;
+}
 
 // device counters (emb_table::next_row)
 constexpr int kCtrBump = 0;    // rows taken from the unused end of the pool
@@ -49,6 +57,9 @@ struct TabArgs {
     float init_a;
     int32_t step;
     int32_t track;              // record last-seen steps in lookups (emb_table_track_seen)
+    int32_t *sketch;            // count-min admission: [depth][width] counters, or NULL
+    int32_t depth;
+    uint64_t wmask;             // width - 1 (width a power of two)
 };
 
 static TabArgs tab_args(const emb_table &t)
@@ -63,6 +74,9 @@ static TabArgs tab_args(const emb_table &t)
     a.free_rows = t.free_rows;
     a.step = (int32_t)t.step;
     a.track = t.track_seen ? 1 : 0;
+    a.sketch = t.sketch;
+    a.depth = t.cm_depth;
+    a.wmask = (uint64_t)t.cm_width - 1;
     a.cap = t.capacity;
     a.row_cap = t.row_capacity;
     a.dim = t.dim;
@@ -271,12 +285,26 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
     const int64_t key = p < n ? *gp(keys + p) : 0;
     if (p < n && key < 1) *gp(pos + p) = EMB_ROW_DROPPED;
     if (key >= 1) {
-        bool inserted;
-        const int64_t s = probe_insert(a, (unsigned long long)key, inserted, probes);
-        if (s < 0) {
-            *gp(pos + p) = kPosRefused;
-            full = 1;
+        bool inserted = false;
+        int64_t s;
+        if (a.sketch) {
+            // count-min admission: a key in the table counts in its slot; an absent
+            // one adds to its sketch cells and waits for cm_enter
+            s = probe_find(a, (unsigned long long)key);
+            if (s < 0) {
+                *gp(pos + p) = kPosPending;
+                for (int j = 0; j < a.depth; j++)
+                    atomicAdd(&a.sketch[(int64_t)j * (int64_t)(a.wmask + 1) +
+                                        (int64_t)cm_cell((uint64_t)key, j, a.wmask)], 1);
+            }
         } else {
+            s = probe_insert(a, (unsigned long long)key, inserted, probes);
+            if (s < 0) {
+                *gp(pos + p) = kPosRefused;
+                full = 1;
+            }
+        }
+        if (s >= 0) {
             *gp(pos + p) = (int32_t)s;
             ins = inserted;
             // count this occurrence in the block's LDS hash
@@ -315,6 +343,41 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
         if (lstat[1]) atomicAdd((unsigned long long *)&stats[EMB_STAT_TABLE_FULL], lstat[1]);
         if (lstat[2]) atomicMax((unsigned long long *)&stats[EMB_STAT_MAX_PROBE], lstat[2]);
     }
+}
+
+// count-min admission, after every occurrence of the step reached the sketch: an
+// absent key whose estimate (the least of its cells) reached the threshold enters
+// the table with that count; ht_admit then gives it a row.  All occurrences of a
+// key compute the same estimate; the one whose insert lands sets the count.
+__global__ __launch_bounds__(kBlock) void cm_enter(TabArgs a, const int64_t *__restrict__ keys,
+                                                  int64_t n, int32_t *__restrict__ pos,
+                                                  int64_t *stats)
+{
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    int64_t ins = 0, full = 0, probes = 0;
+    if (p < n && pos[p] == kPosPending) {
+        const uint64_t key = (uint64_t)keys[p];
+        int32_t est = INT32_MAX;
+        for (int j = 0; j < a.depth; j++)
+            est = min(est, a.sketch[(int64_t)j * (int64_t)(a.wmask + 1) + (int64_t)cm_cell(key, j, a.wmask)]);
+        if (est >= a.threshold) {
+            bool inserted;
+            const int64_t s = probe_insert(a, (unsigned long long)key, inserted, probes);
+            if (s < 0) {
+                full = 1;                      // stays pending: reads DEFAULT
+            } else {
+                if (inserted) {
+                    a.count[s] = est;
+                    if (a.track) a.seen[s] = a.step;
+                    ins = 1;
+                }
+                pos[p] = (int32_t)s;
+            }
+        }
+    }
+    stat_add(stats, EMB_STAT_TABLE_INSERTED, ins);
+    stat_add(stats, EMB_STAT_TABLE_FULL, full);
+    stat_max(stats, EMB_STAT_MAX_PROBE, probes);
 }
 
 __global__ __launch_bounds__(kBlock) void ht_admit(TabArgs a, const int64_t *__restrict__ keys,
@@ -724,6 +787,8 @@ emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int
     const TabArgs a = tab_args(*table);
     const unsigned cgrid = (unsigned)std::max<int64_t>(1, (n + kCountTile - 1) / kCountTile);
     hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
+    if (a.sketch)
+        hipLaunchKernelGGL(cm_enter, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_admit, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_resolve, dim3(grid_of(n)), dim3(kBlock), 0, st, a, n, rows_out);
     table->step++;
@@ -753,6 +818,23 @@ emb_status emb_table_export(emb_table *table, int64_t *keys, int32_t *counts, in
 }
 
 int64_t emb_table_step(const emb_table *table) { return table ? table->step : -1; }
+
+emb_status emb_table_use_count_min(emb_table *table, int32_t depth, int64_t width, int32_t *sketch)
+{
+    if (!table) return fail(EMB_ERR_INVALID_ARG, "table is NULL");
+    if (!sketch) {
+        table->sketch = nullptr;
+        return EMB_OK;
+    }
+    if (depth < 1 || depth > 8) return fail(EMB_ERR_INVALID_ARG, "count-min depth must be in [1, 8]");
+    if (width < 2 || width > (int64_t(1) << 30) || (width & (width - 1)))
+        return fail(EMB_ERR_INVALID_ARG, "count-min width must be a power of two in [2, 2^30]");
+    if (!aligned(sketch, 4)) return fail(EMB_ERR_INVALID_ARG, "sketch must be 4-byte aligned");
+    table->sketch = sketch;
+    table->cm_depth = depth;
+    table->cm_width = width;
+    return EMB_OK;
+}
 
 emb_status emb_table_track_seen(emb_table *table, int32_t on)
 {

@@ -357,6 +357,22 @@ emb_status emb_table_export(emb_table *table, int64_t *keys, int32_t *counts, in
  *   the saved values (row pool full: not admitted, counted in
  *   EMB_STAT_TABLE_FULL); keys already present are left as they are.
  */
+/*
+ * Count-min admission (a probabilistic frequency filter; Monolith Sec. 2.1 admits
+ * an ID once its frequency reaches a threshold): with a sketch set, a key that
+ * is not in the table takes no slot; its occurrences add to `depth` counters,
+ * counter j in row j at x_j mod width, where x_0, x_1, ... are the outputs of a
+ * SplitMix64 generator seeded with the key.  After all occurrences of a step are
+ * added, an absent key whose estimate (the least of its counters) reaches the
+ * threshold enters the table with that count and gets a row; the others read
+ * DEFAULT.  Keys in the table count exactly in their slots.
+ *   sketch  int32 [depth, width] device memory, caller-owned, zero-filled before
+ *           first use; NULL switches the filter off (exact counting in slots).
+ *   depth in [1, 8]; width a power of two in [2, 2^30].
+ * The sketch is not part of emb_table_save; its owner keeps it.
+ */
+emb_status emb_table_use_count_min(emb_table *table, int32_t depth, int64_t width, int32_t *sketch);
+
 int64_t emb_table_step(const emb_table *table);
 emb_status emb_table_track_seen(emb_table *table, int32_t on);
 emb_status emb_table_set_step(emb_table *table, int64_t step);

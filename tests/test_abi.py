@@ -130,4 +130,5 @@ def test_calls_fail_loudly_on_null_plan(L):
     assert L.lib().emb_table_load(None, None, None, None, None, None, 0, None, None) == 1
     assert L.lib().emb_table_set_step(None, 0) == 1 and L.lib().emb_table_step(None) == -1
     assert L.lib().emb_table_track_seen(None, 1) == 1
+    assert L.lib().emb_table_use_count_min(None, 2, 16, None) == 1
     assert L.lib().emb_forward_rows(None, None, None, None, 0, None, None, 0, None, None) == 1

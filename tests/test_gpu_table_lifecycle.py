@@ -139,3 +139,32 @@ def test_evict_zeroes_freed_optimizer_state():
     # the freed rows serve the next admissions
     again = to_np(T.lookup_or_insert(torch.arange(100, 130, dtype=torch.int64, device=DEV)))
     assert set(again.tolist()) == set(old[:30].tolist())
+
+
+@pytest.mark.parametrize("depth,width", [(2, 64), (3, 1 << 20)])
+def test_count_min_admission_vs_model(depth, width):
+    """Count-min admission: absent keys live only in the sketch until their
+    estimate reaches the threshold (a narrow sketch admits early through
+    collisions, a wide one like exact counting); per step the key set, counts,
+    admission, outcomes and row values match the model."""
+    steps = _batches(8, 91 + depth, universe=2000, size=600)
+    T = E.KeyedTable(1 << 12, 1 << 12, DIM, threshold=3, init_std=0.01, device=DEV,
+                     track_seen=True)
+    T.use_count_min(depth, width)
+    O = OracleTable(1 << 12, DIM, 3, 0.01)
+    O.use_count_min(depth, width)
+    for s, k in enumerate(steps):
+        rows = to_np(T.lookup_or_insert(torch.from_numpy(k).to(DEV)))
+        O.step(k)
+        krows, pool_keys, pool = O.resolve(k)
+        assert np.array_equal(rows == E.ROW_DEFAULT, krows == oracle.ROW_DEFAULT)
+        assert np.array_equal(rows == E.ROW_DROPPED, krows == oracle.ROW_DROPPED)
+        adm = rows >= 0
+        got = to_np(T.rows[torch.from_numpy(rows[adm]).long().to(DEV)])
+        assert np.array_equal(got, pool[krows[adm]])
+        _check_against_model(T, O)
+        assert np.array_equal(to_np(T.sketch).astype(np.int64), O.sketch), "sketch counters differ"
+        if s == 4:
+            T.evict(3)
+            O.evict(3)
+            _check_against_model(T, O)
