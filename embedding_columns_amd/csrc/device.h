@@ -127,6 +127,29 @@ __device__ __forceinline__ int64_t wave_upper_bound(const T *a, int64_t n, T x)
     return lo;
 }
 
+// wave_upper_bound started from a guess: one round of 64 probes 64 apart around
+// `guess` brackets the answer when it lies within 2048 entries of the guess (one
+// more round then finds it); otherwise the full search runs.  Same result.
+template <typename T>
+__device__ __forceinline__ int64_t wave_upper_bound_near(const T *a, int64_t n, T x, int64_t guess)
+{
+    const int l = lane_id();
+    const int64_t lo = min(max(guess - 2048, (int64_t)0), max(n - 4096, (int64_t)0));
+    const int64_t i = lo + (int64_t)l * 64;
+    const bool le = (i < n) ? (a[i] <= x) : false;
+    const int cnt = __popcll(__ballot(le));
+    if (cnt == 0) {
+        if (lo == 0) return 0;                       // a[0] > x
+        return wave_upper_bound(a, n, x);
+    }
+    const int64_t i0 = lo + (int64_t)(cnt - 1) * 64;  // a[i0] <= x
+    if (cnt == 64 && i0 + 64 < n) return wave_upper_bound(a, n, x);
+    // the answer is in (i0, min(i0 + 64, n)]
+    const int64_t j = i0 + 1 + l;
+    const bool le2 = (l < 63 && j < n) ? (a[j] <= x) : false;
+    return i0 + 1 + __popcll(__ballot(le2));
+}
+
 // First index i in [0, n) with a[i] >= x, n if none.
 template <typename T>
 __device__ __forceinline__ int64_t wave_lower_bound(const T *a, int64_t n, T x)

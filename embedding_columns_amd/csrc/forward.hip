@@ -556,7 +556,10 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     int own_lo, own_hi;
     int b0 = nbag;
     if (x0 < x1) {
-        b0 = (int)wave_upper_bound(a.off, (int64_t)nbag + 1, x0) - 1;   // bag holding x0
+        // bag holding x0; the search starts at the bag a uniform spread of the
+        // positions would put there
+        b0 = (int)wave_upper_bound_near(a.off, (int64_t)nbag + 1, x0,
+                                        (int64_t)x0 * nbag / max(N, 1)) - 1;
         t.wb = max(0, b0 - kMargin);
     } else {
         t.wb = 0;
