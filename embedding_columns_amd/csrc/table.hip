@@ -267,6 +267,9 @@ constexpr int kLdsSlots = 2 * kCountTile;      // load factor <= 1/2: every inse
 constexpr int kLdsSlotBits = 11;
 static_assert((1 << kLdsSlotBits) == kLdsSlots, "LDS hash size");
 
+// CM: count-min admission (absent keys go to the sketch), a separate instance so
+// that exact counting carries none of its code
+template <bool CM>
 __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t *__restrict__ keys,
                                                       int64_t n, int32_t *__restrict__ pos,
                                                       int64_t *stats)
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
     if (key >= 1) {
         bool inserted = false;
         int64_t s;
-        if (a.sketch) {
+        if (CM) {
             // count-min admission: a key in the table counts in its slot; an absent
             // one adds to its sketch cells and waits for cm_enter
             s = probe_find(a, (unsigned long long)key);
@@ -786,9 +789,12 @@ emb_status emb_table_lookup_or_insert(emb_table *table, const int64_t *keys, int
     hipStream_t st = static_cast<hipStream_t>(stream);
     const TabArgs a = tab_args(*table);
     const unsigned cgrid = (unsigned)std::max<int64_t>(1, (n + kCountTile - 1) / kCountTile);
-    hipLaunchKernelGGL(ht_count, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
-    if (a.sketch)
+    if (a.sketch) {
+        hipLaunchKernelGGL(ht_count<true>, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
         hipLaunchKernelGGL(cm_enter, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
+    } else {
+        hipLaunchKernelGGL(ht_count<false>, dim3(cgrid), dim3(kCountTile), 0, st, a, keys, n, rows_out, stats);
+    }
     hipLaunchKernelGGL(ht_admit, dim3(grid_of(n)), dim3(kBlock), 0, st, a, keys, n, rows_out, stats);
     hipLaunchKernelGGL(ht_resolve, dim3(grid_of(n)), dim3(kBlock), 0, st, a, n, rows_out);
     table->step++;
