@@ -130,9 +130,11 @@ def run(args):
     log(f"[bench] {w.name}: {n_pool} batches generated in {time.time() - t0:.1f}s, "
         f"positions/batch {np.mean([b.n for b in batches]):.0f}")
     dbat = []
-    for b in batches:
+    for j, b in enumerate(batches):
         dbat.append(dict(off=torch.from_numpy(b.offsets).to(dev), ids=torch.from_numpy(b.ids).to(dev),
-                         fv=torch.from_numpy(b.fvals).to(dev), n=b.n))
+                         fv=torch.from_numpy(b.fvals).to(dev), n=b.n,
+                         pw=(torch.from_numpy(W.make_position_weights(b.n, 1000 * cfg + j)).to(dev)
+                             if args.weights else None)))
     max_ids = max(b.n for b in batches)
 
     table = None
@@ -211,6 +213,10 @@ def run(args):
             if ev is not None:
                 t1e.record(side_s)
                 tev.append((t0e, t1e))
+        elif args.weights:
+            E.emb_forward_ex(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
+                             d["fv"] if 2 in kinds else None, krows[i][:n] if keyed else None,
+                             d["pw"], None, n, Y, plan.workspace, training, tstats)
         else:
             E.emb_forward(plan.plan, d["off"], d["ids"] if kinds & {0, 1} else None,
                           d["fv"] if 2 in kinds else None, krows[i][:n] if keyed else None, n, Y,
@@ -323,7 +329,8 @@ def run(args):
                    "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
                    "backward": ("atomic" if args.atomic_backward else "sorted") if training else "none",
                    "tile": plan.opts.tile or 256, "fwd_launches_per_step": 2 if pipe else 1,
-                   "pipelined_transform": bool(pipe)},
+                   "pipelined_transform": bool(pipe),
+                   "position_weights": bool(args.weights)},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
@@ -398,6 +405,8 @@ def main():
     ap.add_argument("--atomic-backward", action="store_true",
                     help="SGD by atomic scatter (no sort) instead of the sorted segment apply")
     ap.add_argument("--inference", action="store_true", help="forward only (no backward)")
+    ap.add_argument("--weights", action="store_true",
+                    help="per-position weights (the extended forward, emb_forward_ex)")
     ap.add_argument("--pipeline", action="store_true",
                     help="transform the next batch on a second stream during the backward")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -66,6 +66,8 @@ constexpr int kColCache = 8;
 //   kFromRows   gather + pool from row codes a transform-only launch made
 //               (emb_forward_rows); truncation and the mask were applied there.
 enum FwdMode { kFused = 0, kTransform = 1, kFromRows = 2 };
+constexpr int kFeatFilter = 1;    // truncation or a mask: positions are removed
+constexpr int kFeatWeights = 2;   // per-position weights or default rows
 // A bag of at most kShort positions is never cut by a tile boundary: the tile
 // holding its start finishes it (tiles span at most kTileMax + kShort - 1
 // positions).  Only longer bags are split and combined through the workspace.
@@ -286,13 +288,11 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             // every load is issued (dropped / default / past-the-run positions read
             // row 0), so that the single wait below covers exactly these loads
             int r[U];
-            float vw[U];
             RowRaw<BF> h[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int x = L.rows[min(p + u, ge - 1) - t.t0];   // unconditional LDS reads
                 r[u] = (p + u < ge) ? x : -1;
-                vw[u] = EXT ? L.wt[min(p + u, ge - 1) - t.t0] : 1.0f;
             }
 #pragma unroll
             for (int u = 0; u < U; u++)
@@ -324,10 +324,13 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                 const float4 w = row_f32(h[u]);
                 const bool use = pp < ge && r[u] >= 0;
                 if (EXT) {
-                    acc[0] += use ? vw[u] * w.x : 0.f;
-                    acc[1] += use ? vw[u] * w.y : 0.f;
-                    acc[2] += use ? vw[u] * w.z : 0.f;
-                    acc[3] += use ? vw[u] * w.w : 0.f;
+                    // the weight is read here, not with the batch: registers are
+                    // short in this loop
+                    const float vw = L.wt[min(pp, ge - 1) - t.t0];
+                    acc[0] += use ? vw * w.x : 0.f;
+                    acc[1] += use ? vw * w.y : 0.f;
+                    acc[2] += use ? vw * w.z : 0.f;
+                    acc[3] += use ? vw * w.w : 0.f;
                 } else {
                     acc[0] += use ? w.x : 0.f;
                     acc[1] += use ? w.y : 0.f;
@@ -444,8 +447,9 @@ __device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L
     return keep;
 }
 
-// EXT: the extended forward (truncation, mask or per-position weights)
-template <bool EXT, int MODE>
+// FEAT: the extended forward's parts this launch needs, kFeatFilter (truncation
+// or the mask) and kFeatWeights (per-position weights or default rows)
+template <int FEAT, int MODE>
 __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
                                               const TileIn &in, int32_t (&cnt)[5])
@@ -483,12 +487,12 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
             r = kr == EMB_ROW_DEFAULT ? -2 : ((kr >= 0 && (uint64_t)kr < rows) ? kr : -1);
         }
         // removed positions are counted apart from the transform's drops
-        const bool removed = EXT && MODE != kFromRows && !position_kept(a, L, t, col, p);
+        const bool removed = (FEAT & kFeatFilter) && MODE != kFromRows && !position_kept(a, L, t, col, p);
         cnt[2] += (r == -1 && !removed);
         cnt[4] += removed;
         if (removed) r = -1;
         L.rows[p - t.t0] = r;
-        if (EXT) {
+        if (FEAT & kFeatWeights) {
             const float v = a.pw_in ? *gp(a.pw_in + p) : 1.0f;
             L.wt[p - t.t0] = v;
             if (a.training && a.pw_in) {
@@ -523,12 +527,14 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const 
     return min(t.t1, win ? offw<true>(a, L, t, (c + 1) * a.B) : offat(a, L, t, (c + 1) * a.B));
 }
 
-// EXT: some column truncates or has a default row, or the call has a mask or
-// per-position weights (a separate instance, so that the plain forward carries
-// none of that code).  MODE: FwdMode.
-template <bool EXT, int MODE>
+// FEAT: the parts of the extended forward this launch needs (kFeatFilter: a
+// column truncates or the call has a mask; kFeatWeights: per-position weights or
+// a column with a default row), each a separate instance so that the plain
+// forward carries none of that code.  MODE: FwdMode.
+template <int FEAT, int MODE>
 __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 {
+    constexpr bool EXT = (FEAT & kFeatWeights) != 0;
     __shared__ WaveLds lds[kTileWaves];
     const int w = threadIdx.x / kWave, lane = lane_id();
     WaveLds &L = lds[w];
@@ -652,8 +658,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             const int s0 = col_lo(a, L, t, cu, c_first, win), s1 = col_hi(a, L, t, cu, c_last, win);
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
-            if (EXT) fwd_transform<true, MODE>(a, L, t, col, s0, s1, in, cnt);
-            else fwd_transform<false, MODE>(a, L, t, col, s0, s1, in, cnt);
+            fwd_transform<FEAT, MODE>(a, L, t, col, s0, s1, in, cnt);
         }
         if (MODE == kTransform) {
 #pragma unroll
@@ -746,15 +751,11 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 
 using namespace emb;
 
-template <int MODE>
-static void launch_fwd(bool ext, int64_t blocks, const FwdArgs &a, void *stream)
+template <int FEAT, int MODE>
+static void launch_one(int64_t blocks, const FwdArgs &a, void *stream)
 {
-    if (ext)
-        hipLaunchKernelGGL((fwd_kernel<true, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           static_cast<hipStream_t>(stream), a);
-    else
-        hipLaunchKernelGGL((fwd_kernel<false, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL((fwd_kernel<FEAT, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
 }
 
 static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets, const int64_t *ids,
@@ -819,13 +820,22 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
     }
     // contiguous tile ranges per XCD: each L2 caches the rows of fewer columns
     const int64_t blocks = xcd_grid((a.ntiles + kTileWaves - 1) / kTileWaves, 0);
+    const bool filt = mask || plan->has_trunc, wts = pweights || plan->has_default;
     if (mode == kTransform) {
-        launch_fwd<kTransform>(mask || plan->has_trunc, blocks, a, stream);
+        if (filt) launch_one<kFeatFilter, kTransform>(blocks, a, stream);
+        else launch_one<0, kTransform>(blocks, a, stream);
     } else if (mode == kFromRows) {
         a.mask = nullptr;                      // applied by the transform
-        launch_fwd<kFromRows>(pweights || plan->has_default, blocks, a, stream);
+        if (wts) launch_one<kFeatWeights, kFromRows>(blocks, a, stream);
+        else launch_one<0, kFromRows>(blocks, a, stream);
+    } else if (filt && wts) {
+        launch_one<kFeatFilter | kFeatWeights, kFused>(blocks, a, stream);
+    } else if (filt) {
+        launch_one<kFeatFilter, kFused>(blocks, a, stream);
+    } else if (wts) {
+        launch_one<kFeatWeights, kFused>(blocks, a, stream);
     } else {
-        launch_fwd<kFused>(mask || pweights || plan->has_trunc || plan->has_default, blocks, a, stream);
+        launch_one<0, kFused>(blocks, a, stream);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));
