@@ -463,13 +463,17 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
         return;
     }
 
-    // local key: the row, or rows / rows + 1 for dropped / DEFAULT
+    // local key: the row, or rows / rows + 1 for dropped / DEFAULT.  The values
+    // are read now too, with the keys, and wait in registers: at the end they go
+    // through the free LDS key buffer instead of a second round of global reads.
+    uint32_t vv[kCSItems];
     {
         uint32_t kv[kCSItems];
 #pragma unroll
         for (int j = 0; j < kCSItems; j++) {
             const int i = j * kCSBlock + t;
             kv[j] = i < cnt ? *gp(kin + P0 + i) : 0u;
+            vv[j] = i < cnt ? *gp(vin + P0 + i) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < kCSItems; j++) {
@@ -528,8 +532,15 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
         __syncthreads();
     }
 
-    // back to global keys; the bags are gathered before any is written (in place)
+    // back to global keys; each value is gathered from the other key buffer
+    // (free now), where the values were put in position order
     const int fin = passes & 1;
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = j * kCSBlock + t;
+        if (i < cnt) S.key[fin ^ 1][i] = vv[j];
+    }
+    __syncthreads();
     uint32_t ko[kCSItems], vo[kCSItems];
 #pragma unroll
     for (int j = 0; j < kCSItems; j++) {
@@ -537,10 +548,9 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
         if (i < cnt) {
             const uint32_t k = S.key[fin][i];
             ko[j] = k < rows ? k + rb : total_rows + (k - rows);
-            vo[j] = *gp(vin + P0 + S.idx[fin][i]);
+            vo[j] = S.key[fin ^ 1][S.idx[fin][i]];
         }
     }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kCSItems; j++) {
         const int i = j * kCSBlock + t;
