@@ -683,8 +683,7 @@ struct BwdArgs {
     int64_t ntiles;
     const float *G;
     const uint32_t *sval;       // sorted bags (PW: sorted positions)
-    const int32_t *pbags;       // PW: bag of each position
-    const float *pw;            // PW: weight of each position
+    const uint2 *bw;            // PW: (bag, weight bits) of each position
     const int32_t *bag_n;
     const uint32_t *seg;        // [U + 1]
     const uint32_t *ukeys;      // [U]
@@ -695,6 +694,7 @@ struct BwdArgs {
     int32_t *pcnt;
     uint32_t *tick;
     int32_t any_mean;           // some column pools by mean
+    int32_t all_mean;           // every column pools by mean
     int32_t zero;               // 0, unknown to the compiler: keeps repeated row loads distinct
     uint32_t total_rows;        // keys >= this are dropped / DEFAULT contributors: no row
     int32_t xcd_chunk;          // tile order over the XCDs (0: contiguous ranges)
@@ -1211,13 +1211,15 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         // bagr holds positions here (< N: the sorted entries are positions)
 #pragma unroll
         for (int i = 0; i < kPL; i++) {
-            vw[i] = *gp(a.pw + bagr[i]);
-            bagr[i] = *gp(a.pbags + bagr[i]);
+            const uint2 r = *gp(a.bw + bagr[i]);
+            bagr[i] = (int)r.x;
+            vw[i] = __uint_as_float(r.y);
         }
-        // the mean weight is folded in here, per contributor's column
+        // the mean weight is folded in here, per contributor's column (a lookup
+        // of its pooling only when the plan mixes sum and mean columns)
 #pragma unroll
         for (int i = 0; i < kPL; i++) {
-            const bool mean = *gp(&a.cols[bagr[i] / a.B].pool) == EMB_POOL_MEAN;
+            const bool mean = a.all_mean ? true : (a.any_mean ? *gp(&a.cols[bagr[i] / a.B].pool) == EMB_POOL_MEAN : false);
             nr[i] = mean ? max(*gp(a.bag_n + bagr[i]), 1) : 1;
         }
     } else if (a.any_mean) {
@@ -1323,7 +1325,7 @@ struct AtomArgs {
     const int32_t *bags;        // forward: bag per position
     const int32_t *bag_n;
     const uint32_t *cstart;     // forward: first position of each column [C + 1]
-    const float *pw;            // forward: weight of each position, or NULL (all 1)
+    const uint2 *bw;            // forward: (bag, weight bits) of each position, or NULL
     uint32_t total_rows;
 };
 
@@ -1362,7 +1364,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void atomic_apply(AtomArgs a)
                 const int pp = min(b0 + j * G + g, cend - 1);
                 key[j] = b0 + j * G + g < cend ? *gp(a.keys + pp) : a.total_rows;
                 bag[j] = *gp(a.bags + pp);
-                vw[j] = a.pw ? *gp(a.pw + pp) : 1.0f;
+                vw[j] = a.bw ? __uint_as_float((*gp(a.bw + pp)).y) : 1.0f;
             }
 #pragma unroll
             for (int j = 0; j < U; j++) {
@@ -1538,8 +1540,7 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     // the sorted bags sit in the buffer the last radix pass wrote
     a.sval = reinterpret_cast<const uint32_t *>(
         ws + (sort_passes(plan) % 2 ? W.vals2 : (plan->last_weighted ? W.posid : W.bags)));
-    a.pbags = reinterpret_cast<const int32_t *>(ws + W.bags);
-    a.pw = reinterpret_cast<const float *>(ws + W.pw);
+    a.bw = reinterpret_cast<const uint2 *>(ws + W.bw);
     a.skeys = reinterpret_cast<const uint32_t *>(ws + (sort_passes(plan) % 2 ? W.keys2 : W.keys));
     a.bag_n = reinterpret_cast<const int32_t *>(ws + W.bag_n);
     a.seg = reinterpret_cast<const uint32_t *>(ws + W.seg);
@@ -1550,6 +1551,7 @@ extern "C" emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, 
     a.pcnt = reinterpret_cast<int32_t *>(ws + W.bcnt);
     a.tick = reinterpret_cast<uint32_t *>(ws + W.btick);
     a.any_mean = plan->any_mean ? 1 : 0;
+    a.all_mean = plan->all_mean ? 1 : 0;
     a.zero = 0;
     a.total_rows = plan->total_rows;
     // Sorted segments of a few long columns change cost along the tile range
@@ -1609,7 +1611,7 @@ extern "C" emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out,
     a.bags = reinterpret_cast<const int32_t *>(ws + plan->ws.bags);
     a.bag_n = reinterpret_cast<const int32_t *>(ws + plan->ws.bag_n);
     a.cstart = reinterpret_cast<const uint32_t *>(ws + plan->ws.cstart);
-    a.pw = plan->last_weighted ? reinterpret_cast<const float *>(ws + plan->ws.pw) : nullptr;
+    a.bw = plan->last_weighted ? reinterpret_cast<const uint2 *>(ws + plan->ws.bw) : nullptr;
     a.total_rows = plan->total_rows;
     hipLaunchKernelGGL(atomic_apply, dim3((unsigned)a.ntiles), dim3(kTileBlock), 0,
                        static_cast<hipStream_t>(stream), a);

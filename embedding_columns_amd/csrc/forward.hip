@@ -40,7 +40,7 @@ struct FwdArgs {
     const int32_t *krows;
     const uint8_t *mask;     // per-position keep byte, or NULL
     const float *pw_in;      // per-position weight, or NULL (all 1)
-    float *pw_save;          // training with weights: the weights, for the backward
+    uint2 *bw;               // training with weights: (bag, weight bits) of each position
     uint32_t *posid;         // ... and each position's own index (the sort's values)
     int32_t has_default;     // training entries N + bag record the default-row fills
     int32_t *rows_out;       // transform-only launch: the row code of every position
@@ -143,7 +143,7 @@ __device__ __forceinline__ void default_entry(const FwdArgs &a, const DevCol &co
                                                        : a.total_rows;
     *gp(a.bags + x) = bag;
     if (a.pw_in) {
-        *gp(a.pw_save + x) = 1.0f;
+        *gp(a.bw + x) = make_uint2((uint32_t)bag, __float_as_uint(1.0f));
         *gp(a.posid + x) = (uint32_t)x;
     }
 }
@@ -495,10 +495,7 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
         if (FEAT & kFeatWeights) {
             const float v = a.pw_in ? *gp(a.pw_in + p) : 1.0f;
             L.wt[p - t.t0] = v;
-            if (a.training && a.pw_in) {
-                *gp(a.pw_save + p) = v;
-                *gp(a.posid + p) = (uint32_t)p;
-            }
+            if (a.training && a.pw_in) *gp(a.posid + p) = (uint32_t)p;
         }
         cnt[0] += 1;
         cnt[1] += (r >= 0);
@@ -684,7 +681,12 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
 #pragma unroll
             for (int i = 0; i < kPL; i++) {
                 const int p = t.p0 + lane + kWave * i;
-                if (p >= t.t0 && p < t.t1) *gp(a.bags + p) = L.pbag[p - t.t0];
+                if (p >= t.t0 && p < t.t1) {
+                    *gp(a.bags + p) = L.pbag[p - t.t0];
+                    // the weighted backward reads bag and weight in one load
+                    if (EXT && a.pw_in)
+                        *gp(a.bw + p) = make_uint2((uint32_t)L.pbag[p - t.t0], __float_as_uint(L.wt[p - t.t0]));
+                }
             }
         }
     }
@@ -802,7 +804,7 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
     a.rows_out = rows_out;
     a.Y = out;
     if (ws) {
-        a.pw_save = reinterpret_cast<float *>(ws + plan->ws.pw);
+        a.bw = reinterpret_cast<uint2 *>(ws + plan->ws.bw);
         a.posid = reinterpret_cast<uint32_t *>(ws + plan->ws.posid);
         a.keys = reinterpret_cast<uint32_t *>(ws + plan->ws.keys);
         a.bags = reinterpret_cast<int32_t *>(ws + plan->ws.bags);

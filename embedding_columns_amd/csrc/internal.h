@@ -66,7 +66,7 @@ struct WsLayout {
     size_t seg, ukeys, ucnt, uscan, misc;     // unique rows: segment starts, keys, block counts
     size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
     size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
-    size_t pw, posid;                         // weighted forward -> backward: weight and index per position
+    size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
     size_t total;
 };
 
@@ -85,6 +85,7 @@ struct emb_plan {
     int64_t sort_blocks = 0;       // radix blocks of the largest batch
     int64_t uq_blocks = 0;         // unique-row blocks of the largest batch
     bool has_hash = false, has_bucket = false, has_keyed = false, any_mean = false;
+    bool all_mean = true;          // every column pools by mean
     bool has_trunc = false;        // some column truncates its bags
     bool last_weighted = false;    // the last training forward had per-position weights
     bool has_default = false;      // some column has a default row: the forward adds one

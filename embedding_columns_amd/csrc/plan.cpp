@@ -124,7 +124,7 @@ void plan_layout(emb_plan &P)
     L.bcnt = take(4 * 2 * P.max_tiles);
     L.btick = take(4 * P.max_tiles);
     L.cstart = take(4 * ((size_t)P.n_cols + 1));
-    L.pw = take(4 * N);
+    L.bw = take(8 * N);
     L.posid = take(4 * N);
     L.total = o;
 }
@@ -189,6 +189,7 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         P.has_bucket |= d.kind == EMB_COL_BUCKET;
         P.has_keyed |= d.kind == EMB_COL_KEYED;
         P.any_mean |= d.pool == EMB_POOL_MEAN;
+        P.all_mean &= d.pool == EMB_POOL_MEAN;
         P.has_trunc |= d.seq_max > 0;
         P.has_default |= d.default_row >= 0;
     }
