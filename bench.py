@@ -413,7 +413,7 @@ def main():
                     help="also run a 1 GiB device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(column-wise sharding with one all-to-all is designed, not built).", file=sys.stderr)
         sys.exit(2)
     run(args)

@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
     EMB_OK = 0,
     EMB_ERR_INVALID_ARG = 1,   /* bad descriptor, pointer, size or alignment */
-    EMB_ERR_UNSUPPORTED = 2,   /* a valid request this build does not handle (e.g. dim) */
+    EMB_ERR_UNSUPPORTED = 2,   /* a valid request the library does not handle (e.g. dim) */
     EMB_ERR_WORKSPACE = 3,     /* a caller buffer is smaller than the query returned */
     EMB_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } emb_status;
