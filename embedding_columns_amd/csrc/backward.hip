@@ -712,10 +712,14 @@ static_assert(kKeyWin % kWave == 0, "key window loads are unrolled per lane");
 struct BwdLds {
     int32_t bag[kSegSpan];      // bag of each contributor of the tile
     float wt[kSegSpan];         // pooling weight of each contributor
-    uint32_t kw[kKeyWin];       // sorted keys x0 - 64 .. x0 + 383 (sentinels outside [0, nv))
+    union {                     // the keys are read only before the walk, the pieces
+                                // only during it: sharing keeps a wave under 8 KB of
+                                // LDS, five waves per SIMD
+        uint32_t kw[kKeyWin];   // sorted keys x0 - 64 .. x0 + 383 (sentinels outside [0, nv))
+        float part[kWave][4];
+    };
     uint32_t seg[kOffCap];      // window of segment starts
     uint32_t ukey[kOffCap];     // unique keys of the same segments
-    float part[kWave][4];
     int32_t hseg[kWave], hpass[kWave];
     int32_t njob;                  // segments whose last piece arrived here: summed by the
     int32_t job_u[4], job_c[4];    //   whole wavefront once the walk is done
