@@ -9,8 +9,9 @@ one batch already resident in HBM; steps cycle a pool of pre-generated batches.
 
 Prints one JSON line: lookups/s (valid (column, sample, ID) positions per
 second), the roofline of the dominant kernel (algorithmic bytes / its average
-launch time, timed with HIP events on the launch stream), and the CPU oracle
-timed on one batch on the host.
+launch time, timed with HIP events on the launch stream), the HBM traffic of
+that kernel from the committed counter summary, and the CPU oracle timed on the
+host over at least 10 s of the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
