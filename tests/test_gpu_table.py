@@ -174,3 +174,43 @@ def test_table_high_load_probing():
     assert np.all(to_np(ar) == E.ROW_DROPPED)
     gk, gc, gr = (to_np(x) for x in T.export())
     assert set(gk.tolist()) == set(keys.tolist())
+
+
+def test_keyed_column_with_transform_variants():
+    """A KEYED column with truncation, a mask, per-position weights and a default
+    row: the rows come from the table, the rest as for hashed columns."""
+    w = _keyed_workload(1 << 14, 500, 64, 3000)
+    w.empty_frac = 0.3                       # empty bags read the default row
+    w.cols[0].seq_max, w.cols[0].seq_keep_last = 40, 1
+    w.cols[0].default_row = 5
+    T, O, _ = _setup(w, seed=56)
+    b = W.make_batch(w, seed=5600)
+    mask = W.make_mask(b.n, 5600, 0.8)
+    pw = W.make_position_weights(b.n, 5600)
+    G = W.make_grad(w, seed=5600, device="cpu")
+    rows = T.lookup_or_insert(torch.from_numpy(b.ids).to(DEV))
+    torch.cuda.synchronize()
+    before = to_np(T.rows).copy()
+    cols = E.EmbeddingColumns(w.cols, [T.rows], batch=w.batch, max_ids=b.n, opt=W.OPT_SGD,
+                              lr=w.lr, device=DEV)
+    off = torch.from_numpy(b.offsets).to(DEV)
+    Y = cols.forward(off, keyed_rows=rows, training=True,
+                     weights=torch.from_numpy(pw).to(DEV), mask=torch.from_numpy(mask).to(DEV))
+    cols.backward(G.to(DEV), want_count=False)
+    torch.cuda.synchronize()
+    # oracle on the GPU's own row indices (the table's placement is its choice)
+    oc = oracle.Columns(w.cols, [before.copy()])
+    g_rows = to_np(rows)
+    Yr, Yb, _, _ = oracle.forward(oc, w.batch, b.offsets, keyed_rows=g_rows, mask=mask, pweights=pw)
+    err = np.abs(to_np(Y).astype(np.float64) - Yr)
+    assert np.all(err <= RTOL_F32 * Yb + 1e-12), "pooled outputs differ"
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), keyed_rows=g_rows,
+                                         opt=W.OPT_SGD, lr=w.lr, mask=mask, pweights=pw)
+    after = to_np(T.rows)
+    d = np.abs(after[urow].astype(np.float64) - oc.weights[0][urow])
+    tol = w.lr * RTOL_F32 * ub[:, :32] + 2.0 ** -22 * (np.abs(before[urow]) + np.abs(after[urow])) + 1e-30
+    assert np.all(d <= tol), "updated rows differ"
+    untouched = np.setdiff1d(np.arange(before.shape[0]), urow)
+    # bitwise: pool rows no key owns are uninitialized memory (any bit pattern)
+    assert np.array_equal(after[untouched].view(np.uint32), before[untouched].view(np.uint32))
+    assert 5 in set(urow.tolist())           # the default row took the empty bags' gradient
