@@ -442,13 +442,185 @@ __device__ void col_sort_big(ColSortLds &S, uint32_t *kA, uint32_t *vA, uint32_t
     }
 }
 
+// Columns whose local keys fit 20 bits (tables below 2^20 - 2 rows) sort in at
+// most two passes of 10-bit digits.  Pass 1 ranks the keys straight from
+// registers and writes (key >> 10, position) packed in 24 bits; pass 2 ranks
+// those by their high digit.  Per-wave counts are 16-bit halves of 32-bit
+// words (a count or offset never exceeds kColCap), which keeps 1024 digits per
+// wave inside the LDS the 7-bit sort uses.  At the end the keys and values go
+// into the two buffers by position and are gathered in sorted order.
+constexpr int kC2Bits = 10;
+constexpr int kC2Radix = 1 << kC2Bits;
+constexpr int kC2PosBits = 14;
+static_assert(kColCap <= (1 << kC2PosBits), "positions fit the packed item");
+static_assert(kCSBlock == kC2Radix, "one thread per digit in the digit scan");
+
+struct ColSort2Lds {
+    uint32_t b1[kColCap];                  // pass 1 output: (key >> 10) << 14 | position
+    uint32_t b2[kColCap];                  // pass 2 output, same packing
+    uint32_t run[kCSWaves][kC2Radix / 2];  // per-wave counts, then offsets: digit d in half d & 1 of word d / 2
+    uint32_t wsum[kCSWaves];
+};
+
+union ColSortShared {
+    ColSortLds s7;
+    ColSort2Lds s10;
+};
+
+// One stable ranking pass over the items of a column in wave-contiguous order
+// (wave w holds items w*per .. w*per+per-1, lane-fastest): item j of this lane
+// has value item[j] and digit (PASS 1) key[j] & 1023 of its local key, or
+// (PASS 2) item[j] >> 14; the values land in `out` in digit order.
+template <int PASS>
+__device__ __forceinline__ uint32_t c2_digit(uint32_t key, uint32_t item)
+{
+    return PASS == 1 ? (key & (kC2Radix - 1)) : (item >> kC2PosBits);
+}
+
+template <int PASS>
+__device__ __forceinline__ void c2_pass(ColSort2Lds &S, const uint32_t (&key)[kCSItems],
+                                        const uint32_t (&item)[kCSItems], int per, int cnt,
+                                        uint32_t *out)
+{
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int k = lane; k < kC2Radix / 2; k += kWave) S.run[w][k] = 0u;
+    wave_sync();
+    // rank within this wave's earlier items of the digit: lower lanes now, plus
+    // the count before this round, which the group's lowest lane gets back from
+    // its LDS add (taken at once: registers are short here)
+    uint32_t rk[kCSItems];
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        const bool in = j * kWave < per && i < cnt;
+        const uint32_t d = in ? c2_digit<PASS>(key[j], item[j]) : 0u;
+        const uint64_t peers = match_digit<kC2Bits>(d, in);
+        const int lead = in ? __ffsll((unsigned long long)peers) - 1 : lane;
+        uint32_t prev = 0u;
+        if (in && lead == lane) {
+            const uint32_t sh = (d & 1u) * 16u;
+            prev = (atomicAdd(&S.run[w][d >> 1], (uint32_t)__popcll(peers) << sh) >> sh) & 0xFFFFu;
+        }
+        rk[j] = (uint32_t)__popcll(peers & lt_mask) + (uint32_t)__shfl((int)prev, lead, kWave);
+    }
+    __syncthreads();
+    // offsets: thread t < 512 takes digits 2t and 2t+1; an exclusive scan of the
+    // pair totals over those threads gives the digit starts, then each wave's
+    // offset within a digit adds the counts of the waves before it
+    uint32_t tlo = 0, thi = 0, incl = 0;
+    if (t < kC2Radix / 2) {
+#pragma unroll
+        for (int k = 0; k < kCSWaves; k++) {
+            const uint32_t v = S.run[k][t];
+            tlo += v & 0xFFFFu;
+            thi += v >> 16;
+        }
+        incl = tlo + thi;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += y;
+        }
+        if (lane == kWave - 1) S.wsum[w] = incl;
+    }
+    __syncthreads();
+    if (t < kC2Radix / 2) {
+        uint32_t carry = 0;
+        for (int k = 0; k < w; k++) carry += S.wsum[k];
+        uint32_t blo = carry + incl - (tlo + thi), bhi = blo + tlo;
+#pragma unroll
+        for (int k = 0; k < kCSWaves; k++) {
+            const uint32_t v = S.run[k][t];
+            S.run[k][t] = blo | (bhi << 16);
+            blo += v & 0xFFFFu;
+            bhi += v >> 16;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        if (j * kWave < per && i < cnt) {
+            const uint32_t d = c2_digit<PASS>(key[j], item[j]);
+            const uint32_t o = ((S.run[w][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu) + rk[j];
+            out[o] = item[j];
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void col_sort_2pass(ColSort2Lds &S, const uint32_t *kin, const uint32_t *vin,
+                                               uint32_t *kout, uint32_t *vout, int P0, int cnt,
+                                               uint32_t rb, uint32_t rows, uint32_t total_rows,
+                                               int bits)
+{
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const int per = ((cnt + kCSBlock - 1) / kCSBlock) * kWave;
+    // keys and values of this thread's items, wave-contiguous, all loads at once
+    uint32_t kv[kCSItems], vv[kCSItems], item[kCSItems];
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        const bool in = j * kWave < per && i < cnt;
+        kv[j] = in ? *gp(kin + P0 + i) : 0u;
+        vv[j] = in ? *gp(vin + P0 + i) : 0u;
+    }
+    // pass 1: the low digit of the local key (the row, or rows / rows + 1 for
+    // dropped / DEFAULT); kv holds local keys until the end
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        kv[j] = kv[j] < total_rows ? kv[j] - rb : rows + (kv[j] - total_rows);
+        item[j] = ((kv[j] >> kC2Bits) << kC2PosBits) | (uint32_t)i;
+    }
+    c2_pass<1>(S, kv, item, per, cnt, S.b1);
+    uint32_t *res = S.b1;
+    if (bits > kC2Bits) {
+        // pass 2: the high digit, in the pass 1 order
+#pragma unroll
+        for (int j = 0; j < kCSItems; j++) {
+            const int i = w * per + j * kWave + lane;
+            item[j] = (j * kWave < per && i < cnt) ? S.b1[i] : 0u;
+        }
+        c2_pass<2>(S, kv, item, per, cnt, S.b2);
+        res = S.b2;
+    }
+    // sorted order -> positions; then keys and values by position into the two
+    // buffers, gathered in sorted order
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        item[j] = (j * kWave < per && i < cnt) ? (res[i] & ((1u << kC2PosBits) - 1u)) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        if (j * kWave < per && i < cnt) {
+            S.b1[i] = kv[j] < rows ? kv[j] + rb : total_rows + (kv[j] - rows);
+            S.b2[i] = vv[j];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCSItems; j++) {
+        const int i = w * per + j * kWave + lane;
+        if (j * kWave < per && i < cnt) {
+            *gp(kout + P0 + i) = S.b1[item[j]];
+            *gp(vout + P0 + i) = S.b2[item[j]];
+        }
+    }
+}
+
 __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vin, uint32_t *kspare,
                                                     uint32_t *vspare, uint32_t *kout, uint32_t *vout,
                                                     int64_t n, const uint32_t *__restrict__ cstart,
                                                     const uint32_t *__restrict__ row_base,
                                                     uint32_t total_rows, uint32_t *misc)
 {
-    __shared__ ColSortLds S;
+    __shared__ ColSortShared SU;
+    ColSortLds &S = SU.s7;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int c = blockIdx.x;
     if (c == 0 && t == 0) *gp(misc) = (uint32_t)n;   // every position is a contributor slot
@@ -460,6 +632,10 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
     const int passes = (bits + kCSBits - 1) / kCSBits;
     if (cnt > kColCap) {
         col_sort_big(S, kin, vin, kspare, vspare, kout, vout, P0, cnt, rb, rows, total_rows, passes);
+        return;
+    }
+    if (bits <= 2 * kC2Bits) {
+        col_sort_2pass(SU.s10, kin, vin, kout, vout, P0, cnt, rb, rows, total_rows, bits);
         return;
     }
 
