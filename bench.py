@@ -264,6 +264,7 @@ def run(args):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps in {wall * 1e3:.1f} ms")
     st = stats.cpu().numpy()
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bwd_ms = np.array([e[1].elapsed_time(e[3]) for e in evs])
@@ -396,8 +397,10 @@ def cpu_baseline(w, batches, plan, G, weights, states, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 100; 20 for the keyed workload, whose steps each "
+                         "need a batch of their own)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; 5 keyed)")
     ap.add_argument("--workload", default="front-end", choices=sorted(WORKLOADS))
     ap.add_argument("--batches", type=int, default=4)
     ap.add_argument("--tile", type=int, default=0)
@@ -413,6 +416,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
+    keyed = WORKLOADS[args.workload] == 5
+    if args.steps is None:
+        args.steps = 20 if keyed else 100
+    if args.warmup is None:
+        args.warmup = 5 if keyed else 10
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(column-wise sharding with one all-to-all is designed, not built).", file=sys.stderr)
