@@ -4,8 +4,8 @@ Default workload: the training sparse front end -- 200 hashed columns, batch
 4096, tables of 1e4..1e6 rows (log-uniform) and dims 8..64 in fp32, Poisson(3)
 bags with 5 % forced-empty bags and 2 % out-of-range IDs, Zipf(1.1) raw IDs over
 2^40, alternating sum/mean pooling, one SGD step (lr 0.01).  A step is one
-forward launch plus the backward (sort, unique rows, segment-sum + SGD) over
-one batch already resident in HBM; steps cycle a pool of pre-generated batches.
+forward launch plus the backward (per-column sort by row, then a segment-sum and
+the SGD update of each distinct row) over one batch already resident in HBM; steps cycle a pool of pre-generated batches.
 
 Prints one JSON line: lookups/s (valid (column, sample, ID) positions per
 second), the roofline of the dominant kernel (algorithmic bytes / its average
@@ -13,7 +13,9 @@ launch time, timed with HIP events on the launch stream), the HBM traffic of
 that kernel from the committed counter summary, and the CPU oracle timed on the
 host over at least 10 s of the same workload.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+  python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME]
+
+(the keyed-table workload defaults to 20 steps after 5)
 """
 from __future__ import annotations
 
