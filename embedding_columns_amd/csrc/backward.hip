@@ -613,13 +613,13 @@ __device__ __forceinline__ void col_sort_2pass(ColSort2Lds &S, const uint32_t *k
     }
 }
 
-__global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vin, uint32_t *kspare,
-                                                    uint32_t *vspare, uint32_t *kout, uint32_t *vout,
-                                                    int64_t n, const uint32_t *__restrict__ cstart,
-                                                    const uint32_t *__restrict__ row_base,
-                                                    uint32_t total_rows, uint32_t *misc)
+__device__ __forceinline__ void col_sort_column(ColSortShared &SU, uint32_t *kin, uint32_t *vin,
+                                                uint32_t *kspare, uint32_t *vspare, uint32_t *kout,
+                                                uint32_t *vout, int64_t n,
+                                                const uint32_t *__restrict__ cstart,
+                                                const uint32_t *__restrict__ row_base,
+                                                uint32_t total_rows, uint32_t *misc)
 {
-    __shared__ ColSortShared SU;
     ColSortLds &S = SU.s7;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int c = blockIdx.x;
@@ -735,6 +735,77 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
             *gp(vout + P0 + i) = vo[j];
         }
     }
+}
+
+// Valid keys (below total_rows) of column blockIdx.x, counted in its sorted keys:
+// the dropped ones sort after the column's rows.
+__device__ __forceinline__ void col_valid_count(const uint32_t *kout, const uint32_t *cstart,
+                                                uint32_t total_rows, uint32_t *vcnt)
+{
+    __syncthreads();   // every wave's sorted keys are written
+    if (threadIdx.x >= kWave) return;
+    const int c = blockIdx.x;
+    const int64_t P0 = cstart[c], cnt = (int64_t)cstart[c + 1] - P0;
+    const int64_t nv = (cnt > 0 && total_rows > 0) ? wave_upper_bound(kout + P0, cnt, total_rows - 1u) : 0;
+    if (lane_id() == 0) vcnt[c] = (uint32_t)nv;
+}
+
+// One workgroup per column.  With vcnt, it also records the column's number of
+// valid keys, for the compaction that turns the column runs into one sorted run.
+__global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vin, uint32_t *kspare,
+                                                    uint32_t *vspare, uint32_t *kout, uint32_t *vout,
+                                                    int64_t n, const uint32_t *__restrict__ cstart,
+                                                    const uint32_t *__restrict__ row_base,
+                                                    uint32_t total_rows, uint32_t *misc, uint32_t *vcnt)
+{
+    __shared__ ColSortShared SU;
+    col_sort_column(SU, kin, vin, kspare, vspare, kout, vout, n, cstart, row_base, total_rows, misc);
+    if (vcnt) col_valid_count(kout, cstart, total_rows, vcnt);
+}
+
+// exclusive prefix of the columns' valid counts: vbase[c]; vbase[C] = all valid keys
+__global__ __launch_bounds__(kBlock) void cs_vscan(const uint32_t *__restrict__ vcnt, int C,
+                                                  uint32_t *__restrict__ vbase)
+{
+    __shared__ uint32_t tmp[kWavesPerBlock];
+    uint32_t carry = 0;
+    for (int s = 0; s < C; s += kBlock) {
+        const int i = s + threadIdx.x;
+        const uint32_t v = i < C ? vcnt[i] : 0u;
+        uint32_t ex;
+        const uint32_t tot = block_exclusive_scan(v, tmp, ex);
+        if (i < C) vbase[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) vbase[C] = carry;
+}
+
+// The column-sorted keys and values, moved so that the valid keys of all columns
+// come first, column after column (one ascending run: columns own disjoint,
+// increasing key ranges), then every column's dropped keys: the layout one
+// global sort gives, which the unique-row kernels read.
+__global__ __launch_bounds__(kBlock) void cs_compact(const uint32_t *__restrict__ kin,
+                                                    const uint32_t *__restrict__ vin,
+                                                    uint32_t *__restrict__ kout,
+                                                    uint32_t *__restrict__ vout, int64_t n,
+                                                    const uint32_t *__restrict__ cstart, int C,
+                                                    const uint32_t *__restrict__ vcnt,
+                                                    const uint32_t *__restrict__ vbase)
+{
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (p >= n) return;
+    // the column holding p: cstart[lo] <= p < cstart[lo + 1] (an empty column
+    // shares its start with the next one, so the last such lo is not empty)
+    int lo = 0, hi = C;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)cstart[mid] <= p) lo = mid; else hi = mid;
+    }
+    const uint32_t c0 = cstart[lo], i = (uint32_t)p - c0, v = vcnt[lo], vb = vbase[lo];
+    // dropped keys: after all valid ones, behind the c0 - vb dropped keys of earlier columns
+    const uint32_t d = i < v ? vb + i : vbase[C] + (c0 - vb) + (i - v);
+    kout[d] = kin[p];
+    vout[d] = vin[p];
 }
 
 // -------------------------------------------------------------- unique rows
@@ -1654,38 +1725,51 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
     const bool from_keys = plan->opt != EMB_OPT_EMIT && !uniq_keys && !n_uniq && !stats;
     plan->seg_from_keys = from_keys;
     const int passes = sort_passes(plan);
-    // Segments found from the keys come from the column sort when the average
-    // column fits its LDS (n <= C * kColCap; a larger column is sorted by its
-    // workgroup through global memory); the sort leaves dropped / DEFAULT keys
-    // inside each column.  Otherwise the global radix passes sort everything;
-    // they also take the default-row entries, which sit after the N positions.
-    if (from_keys && !plan->has_default && n <= (int64_t)plan->n_cols * kColCap) {
-        uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
+    // the sorted keys and values end in the buffers the apply reads them from
+    uint32_t *kf = (passes % 2) ? k1 : k0, *vf = (passes % 2) ? v1 : v0;
+    // The column sort runs when the average column fits its LDS (n <= C * kColCap;
+    // a larger column is sorted by its workgroup through global memory); it
+    // leaves dropped keys inside each column.  Segments found from the keys take
+    // that as it is.  The unique list needs one sorted run of valid keys: the
+    // columns are then sorted into the other buffers and compacted into kf / vf.
+    // Otherwise the global radix passes sort everything; they also take the
+    // default-row entries, which sit after the N positions.
+    if (!plan->has_default && n <= (int64_t)plan->n_cols * kColCap) {
+        const uint32_t *cst = reinterpret_cast<const uint32_t *>(ws + W.cstart);
+        uint32_t *kc = from_keys ? kf : (kf == k0 ? k1 : k0);
+        uint32_t *vc = from_keys ? vf : (vf == v0 ? v1 : v0);
+        uint32_t *vcnt = reinterpret_cast<uint32_t *>(ws + W.ccnt), *vbase = vcnt + plan->n_cols + 1;
         hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, k1, v1,
-                           kf, vf, n, reinterpret_cast<const uint32_t *>(ws + W.cstart), plan->drow_base,
-                           plan->total_rows, misc);
+                           kc, vc, n, cst, plan->drow_base, plan->total_rows, misc,
+                           from_keys ? nullptr : vcnt);
+        if (!from_keys) {
+            hipLaunchKernelGGL(cs_vscan, dim3(1), dim3(kBlock), 0, st, vcnt, plan->n_cols, vbase);
+            hipLaunchKernelGGL(cs_compact, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                               kc, vc, kf, vf, n, cst, plan->n_cols, vcnt, vbase);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("col_sort launch: ") + hipGetErrorString(e));
-        return EMB_OK;
+        if (from_keys) return EMB_OK;
+    } else {
+        for (int p = 0; p < passes; p++) {
+            const int shift = p * kRadixBits;
+            hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
+            hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
+            hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
+                               shift, hist, dtot, nblk, plan->total_rows,
+                               (from_keys && p == passes - 1) ? misc : nullptr);
+            std::swap(k0, k1);
+            std::swap(v0, v1);
+        }
+        if (from_keys) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
+            return EMB_OK;
+        }
     }
-    for (int p = 0; p < passes; p++) {
-        const int shift = p * kRadixBits;
-        hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
-        hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
-        hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
-                           shift, hist, dtot, nblk, plan->total_rows,
-                           (from_keys && p == passes - 1) ? misc : nullptr);
-        std::swap(k0, k1);
-        std::swap(v0, v1);
-    }
-    if (from_keys) {
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
-        return EMB_OK;
-    }
-    hipLaunchKernelGGL(uq_count, dim3((unsigned)ublk), dim3(kBlock), 0, st, k0, n, plan->total_rows, ucnt, misc);
+    hipLaunchKernelGGL(uq_count, dim3((unsigned)ublk), dim3(kBlock), 0, st, kf, n, plan->total_rows, ucnt, misc);
     hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, ublk, uscan, misc, n_uniq, stats);
-    hipLaunchKernelGGL(uq_write, dim3((unsigned)ublk), dim3(kBlock), 0, st, k0, n, plan->total_rows,
+    hipLaunchKernelGGL(uq_write, dim3((unsigned)ublk), dim3(kBlock), 0, st, kf, n, plan->total_rows,
                        uscan, misc, seg, ukeys, uniq_keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));

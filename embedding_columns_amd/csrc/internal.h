@@ -67,6 +67,7 @@ struct WsLayout {
     size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
     size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
     size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
+    size_t ccnt;                              // column sort -> compaction: valid keys per column, their prefix [2 (C + 1)]
     size_t total;
 };
 

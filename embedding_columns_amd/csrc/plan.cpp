@@ -126,6 +126,7 @@ void plan_layout(emb_plan &P)
     L.cstart = take(4 * ((size_t)P.n_cols + 1));
     L.bw = take(8 * N);
     L.posid = take(4 * N);
+    L.ccnt = take(4 * 2 * ((size_t)P.n_cols + 1));
     L.total = o;
 }
 
