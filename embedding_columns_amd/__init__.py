@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
     "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex", "emb_transform", "emb_forward_rows",
+    "emb_stream_copy",
     "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
@@ -23,6 +24,7 @@ __all__ = [
     "emb_table_export", "emb_table_step", "emb_table_set_step", "emb_table_track_seen", "emb_table_use_count_min",
     "emb_table_evict",
     "emb_table_save", "emb_table_load", "emb_last_error", "EmbeddingColumns", "KeyedTable",
+    "EmbeddingStage",
     "HASH", "IDENTITY", "BUCKET", "KEYED", "SUM", "MEAN", "F32", "BF16", "OPT_EMIT", "OPT_SGD",
     "OPT_ADAGRAD", "ROW_DROPPED", "ROW_DEFAULT", "STAT_COUNT",
 ]
@@ -77,6 +79,7 @@ _SIGS = {
     "emb_forward_ex": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_transform": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP],
     "emb_forward_rows": [_VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
+    "emb_stream_copy": [_VP, _VP, _I64, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_apply": [_VP, _VP, _VP, _VP, _VP],
@@ -212,6 +215,10 @@ def emb_backward_apply(plan, grad_out, workspace, uniq_grads=None, stream=None):
 
 def emb_backward_atomic(plan, grad_out, workspace, stream=None):
     _check(lib().emb_backward_atomic(plan, _ptr(grad_out), _ptr(workspace), _stream(stream)))
+
+
+def emb_stream_copy(dst, src, nbytes, stream=None):
+    _check(lib().emb_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
 
 
 def emb_plan_workspace_view(plan, workspace):
@@ -382,6 +389,36 @@ class EmbeddingColumns:
         emb_backward(self.plan, grad_out.contiguous(), self.workspace, keys, grads, nu, stats)
         return keys, grads, nu
 
+    def __call__(self, offsets, ids=None, fvals=None, keyed_rows=None, weights=None, mask=None):
+        """The pooled output [batch, sum(dim)]; under autograd (grad mode on) it is
+        an EmbeddingStage node whose backward runs emb_backward."""
+        if not torch.is_grad_enabled():
+            return self.forward(offsets, ids, fvals, keyed_rows, training=False, weights=weights,
+                                mask=mask)
+        if getattr(self, "_anchor", None) is None:
+            self._anchor = torch.zeros((), device=self.device, requires_grad=True)
+        return EmbeddingStage.apply(self, self._anchor, offsets, ids, fvals, keyed_rows, weights,
+                                    mask, *self.weights)
+
+    def sparse_table_grads(self, keys, grads, n_uniq, want):
+        """EMIT results as one sparse COO gradient [rows, dim] per table (None where
+        want[c] is false): the distinct keys row_base_c + row are split by column."""
+        n = int(n_uniq.item())
+        k = keys[:n].to(torch.int64) & 0xFFFFFFFF
+        base = torch.tensor(self.row_base, dtype=torch.int64, device=self.device)
+        col = torch.searchsorted(base, k, right=True) - 1
+        out = []
+        for c, spec in enumerate(self.cols):
+            if not want[c]:
+                out.append(None)
+                continue
+            sel = col == c
+            rows = (k[sel] - self.row_base[c]).unsqueeze(0)
+            vals = grads[:n][sel][:, :spec.dim].to(self.weights[c].dtype)
+            out.append(torch.sparse_coo_tensor(rows, vals, (spec.rows, spec.dim),
+                                               is_coalesced=True))
+        return out
+
     def backward_atomic(self, grad_out):
         """SGD by atomic scatter of every contribution (no sort; not bit-reproducible)."""
         emb_backward_atomic(self.plan, grad_out.contiguous(), self.workspace)
@@ -395,6 +432,41 @@ class EmbeddingColumns:
             off = ptr - base
             return self.workspace[off:off + 4 * count].view(torch.int32)
         return view(v.keys, n_ids), view(v.bags, n_ids), view(v.bag_n, nb)
+
+
+class EmbeddingStage(torch.autograd.Function):
+    """The fused stage as an autograd node: the forward is emb_forward (training),
+    the backward emb_backward with the plan's optimizer.  Table lookup and update
+    are framework operations, as Monolith Sec. 2.1 treats its hash-table lookups
+    and updates like Variables.
+
+    apply(cols, anchor, offsets, ids, fvals, keyed_rows, pweights, mask, *tables):
+    `anchor` is a scalar that requires grad, so that autograd reaches this node even
+    when no table does; `tables` are the plan's weight tensors.  With SGD or Adagrad
+    the backward updates the touched rows in place and returns no table gradient.
+    With EMIT it keeps the distinct touched keys, their gradients and their count
+    on `cols.emitted`, and gives every table that requires grad a sparse COO
+    gradient over its touched rows."""
+
+    @staticmethod
+    def forward(ctx, cols, anchor, offsets, ids, fvals, keyed_rows, pweights, mask, *tables):
+        ctx.cols = cols
+        ctx.want = [t is not None and t.requires_grad for t in tables]
+        return cols.forward(offsets, ids, fvals, keyed_rows, training=True, weights=pweights,
+                            mask=mask)
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        cols = ctx.cols
+        g = grad_y.contiguous()
+        if g.dtype != torch.float32:
+            raise TypeError("the pooled output's gradient must be fp32")
+        if cols.opts.opt != OPT_EMIT:
+            cols.backward(g, want_count=False)
+            return (None,) * (8 + len(ctx.want))
+        keys, grads, nu = cols.backward(g, want_keys=True, want_grads=True)
+        cols.emitted = (keys, grads, nu)
+        return (None,) * 8 + tuple(cols.sparse_table_grads(keys, grads, nu, ctx.want))
 
 
 class KeyedTable:

@@ -256,6 +256,13 @@ emb_status emb_backward_apply(emb_plan *plan, const float *grad_out, void *works
  * the sorted path. */
 emb_status emb_backward_atomic(emb_plan *plan, const float *grad_out, void *workspace, void *stream);
 
+/* A plain streaming copy of `bytes` (a multiple of 16, both buffers 16-byte
+ * aligned device memory): dst[i] = src[i].  Not part of the stage; it measures
+ * the bandwidth a purely contiguous read + write kernel reaches on this GPU, the
+ * practical ceiling next to the specified peak that the stage's kernels are
+ * reported against.  EMB_ERR_INVALID_ARG for bad sizes or alignment. */
+emb_status emb_stream_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
 /* Device views into a workspace after a training forward (parity checks):
  * keys uint32 [n_ids] (row_base_c + row; sum(rows) for a dropped position,
  * sum(rows)+1 for a DEFAULT one), bags int32 [n_ids] (bag index c*B+s),

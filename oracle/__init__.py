@@ -35,6 +35,22 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+_SRC_OMP = os.path.join(_HERE, "oracle_omp.c")
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
+
+
+def build_omp(force: bool = False) -> str:
+    """Compile the timing mode (oracle_omp.c: the same oracle, columns over
+    OpenMP threads)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_OMP))
+    if force or not os.path.exists(_LIB_OMP) or os.path.getmtime(_LIB_OMP) < newest:
+        tmp = _LIB_OMP + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-std=c11", "-fopenmp", "-Wall",
+                               "-shared", "-fPIC", _SRC_OMP, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_OMP)
+    return _LIB_OMP
+
+
 class _Col(C.Structure):
     _fields_ = [("kind", C.c_int32), ("pool", C.c_int32), ("dtype", C.c_int32),
                 ("dim", C.c_int32), ("rows", C.c_int64), ("id_lo", C.c_int64),
@@ -215,3 +231,34 @@ def backward(cols: Columns, B: int, offsets, G, ids=None, fvals=None, keyed_rows
                               _p(ub), cap)
     assert U >= 0
     return ucol[:U], urow[:U], ug[:U], ub[:U]
+
+
+class ColumnSteps:
+    """The timing mode: one forward (+ backward and update) of every column, the
+    columns spread over `threads` OpenMP threads (oracle_omp.c).  G is split into
+    per-column [B, dim] slices once, here; outputs go to per-column arrays."""
+
+    def __init__(self, cols: Columns, B: int, G=None):
+        L = C.CDLL(build_omp())
+        L.oracle_step_columns.restype = C.c_int32
+        L.oracle_step_columns.argtypes = ([C.POINTER(_Col), C.c_int32, C.c_int32] + [C.c_void_p] * 5
+                                          + [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_int32])
+        self.lib, self.cols, self.B = L, cols, B
+        dims = [c.dim for c in cols.cols]
+        offs = np.concatenate([[0], np.cumsum(dims)])
+        self.Y = [np.zeros((B, d), dtype=np.float32) for d in dims]
+        self.G = ([np.ascontiguousarray(G[:, offs[c]:offs[c + 1]], dtype=np.float32)
+                   for c in range(len(dims))] if G is not None else None)
+        self._yp = (C.c_void_p * len(dims))(*[y.ctypes.data for y in self.Y])
+        self._gp = (C.c_void_p * len(dims))(*([g.ctypes.data for g in self.G] if self.G is not None
+                                              else [None] * len(dims)))
+
+    def run(self, offsets, ids=None, fvals=None, training=False, opt=0, lr=0.0, eps=0.0,
+            threads=1) -> int:
+        offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+        ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int64)
+        fvals = None if fvals is None else np.ascontiguousarray(fvals, dtype=np.float32)
+        return int(self.lib.oracle_step_columns(
+            self.cols.arr, len(self.cols.cols), self.B, _p(offsets), _p(ids), _p(fvals),
+            C.cast(self._yp, C.c_void_p), C.cast(self._gp, C.c_void_p), 1 if training else 0,
+            opt, lr, eps, threads))
