@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
     "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex", "emb_transform", "emb_forward_rows",
-    "emb_stream_copy",
+    "emb_forward_noalloc", "emb_stream_copy",
     "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
     "emb_plan_workspace_view", "emb_table_query", "emb_table_create", "emb_table_destroy",
@@ -79,6 +79,7 @@ _SIGS = {
     "emb_forward_ex": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_transform": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP],
     "emb_forward_rows": [_VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
+    "emb_forward_noalloc": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP],
     "emb_stream_copy": [_VP, _VP, _I64, _VP],
     "emb_backward": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "emb_backward_dedup": [_VP, _VP, _VP, _VP, _VP, _VP],
@@ -195,6 +196,13 @@ def emb_forward_rows(plan, offsets, rows, pweights, n_ids, out, workspace, train
     _check(lib().emb_forward_rows(plan, _ptr(offsets), _ptr(rows), _ptr(pweights), n_ids,
                                   _ptr(out), _ptr(workspace), 1 if training else 0, _ptr(stats),
                                   _stream(stream)))
+
+
+def emb_forward_noalloc(plan, offsets, ids, fvals, keyed_rows, n_ids, out, stats=None,
+                        stream=None):
+    _check(lib().emb_forward_noalloc(plan, _ptr(offsets), _ptr(ids), _ptr(fvals),
+                                     _ptr(keyed_rows), n_ids, _ptr(out), _ptr(stats),
+                                     _stream(stream)))
 
 
 def emb_backward(plan, grad_out, workspace, uniq_keys=None, uniq_grads=None, n_uniq=None,

@@ -9,6 +9,6 @@ hipcc --offload-arch=gfx950 -O3 -std=c++17 -fPIC -shared \
     -Xclang -target-feature -Xclang -packed-fp32-ops \
     -Wall -Wno-unused-function \
     -I"$root/include" -I"$here" \
-    "$here/plan.cpp" "$here/forward.hip" "$here/backward.hip" "$here/table.hip" "$here/copy.hip" \
+    "$here/plan.cpp" "$here/forward.hip" "$here/backward.hip" "$here/table.hip" "$here/noalloc.hip" "$here/copy.hip" \
     -o "$tmp"
 mv -f "$tmp" "$out"

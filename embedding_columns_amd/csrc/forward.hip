@@ -760,14 +760,19 @@ static void launch_one(int64_t blocks, const FwdArgs &a, void *stream)
                        static_cast<hipStream_t>(stream), a);
 }
 
+// sc: the split-bag partials and tickets of an inference call come from there
+// instead of a workspace (emb_forward_noalloc); workspace is then NULL
 static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets, const int64_t *ids,
                                const float *fvals, const int32_t *keyed_rows, const float *pweights,
                                const uint8_t *mask, int32_t *rows_out, int64_t n_ids, float *out,
-                               void *workspace, int32_t training, int64_t *stats, void *stream)
+                               void *workspace, int32_t training, int64_t *stats, void *stream,
+                               const FwdScratch *sc = nullptr)
 {
     if (!plan) return fail(EMB_ERR_INVALID_ARG, "plan is NULL");
     if (!offsets) return fail(EMB_ERR_INVALID_ARG, "offsets are required");
-    if (mode != kTransform && (!out || !workspace))
+    if (sc && (mode != kFused || training || workspace))
+        return fail(EMB_ERR_INVALID_ARG, "the fixed scratch serves the inference forward only");
+    if (mode != kTransform && (!out || (!workspace && !sc)))
         return fail(EMB_ERR_INVALID_ARG, "out and workspace are required");
     if (n_ids < 0 || n_ids > plan->max_ids)
         return fail(EMB_ERR_WORKSPACE, "n_ids exceeds the plan's max_ids");
@@ -780,7 +785,7 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
     }
     if (mode == kTransform && n_ids > 0 && !rows_out) return fail(EMB_ERR_INVALID_ARG, "rows_out required");
     if (mode != kTransform && !aligned(out, 16)) return fail(EMB_ERR_INVALID_ARG, "out must be 16-byte aligned");
-    if (mode != kTransform && !aligned(workspace, 256))
+    if (mode != kTransform && !sc && !aligned(workspace, 256))
         return fail(EMB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     if (mode == kTransform) training = 0;      // writes nothing but rows_out (and stats)
     FwdArgs a{};
@@ -813,6 +818,11 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
         a.pcnt = reinterpret_cast<int32_t *>(ws + plan->ws.fcnt);
         a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
         a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
+    }
+    if (sc) {
+        a.part = sc->part;
+        a.pcnt = sc->pcnt;
+        a.tick = sc->tick;
     }
     a.stats = stats;
     a.total_rows = plan->total_rows;
@@ -880,3 +890,30 @@ extern "C" emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, c
     return forward_impl(kFromRows, plan, offsets, nullptr, nullptr, rows, pweights, nullptr, nullptr,
                         n_ids, out, workspace, training, stats, stream);
 }
+
+namespace emb {
+size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout, void *base)
+{
+    const int64_t tiles = std::max<int64_t>(1, (n_ids + plan->tile - 1) / plan->tile);
+    auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t part = a256(sizeof(float) * 2 * (size_t)tiles * (size_t)plan->max_dim);
+    const size_t pcnt = a256(sizeof(int32_t) * 2 * (size_t)tiles);
+    const size_t tick = a256(sizeof(uint32_t) * (size_t)tiles);
+    if (layout) {
+        char *b = static_cast<char *>(base);
+        layout->part = reinterpret_cast<float *>(b);
+        layout->pcnt = reinterpret_cast<int32_t *>(b + part);
+        layout->tick = reinterpret_cast<uint32_t *>(b + part + pcnt);
+        layout->tiles = tiles;
+    }
+    return part + pcnt + tick;
+}
+
+emb_status forward_with_scratch(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
+                                float *out, int64_t *stats, void *stream, const FwdScratch &sc)
+{
+    return forward_impl(kFused, plan, offsets, ids, fvals, keyed_rows, nullptr, nullptr, nullptr,
+                        n_ids, out, nullptr, 0, stats, stream, &sc);
+}
+}  // namespace emb

@@ -123,6 +123,19 @@ struct emb_table {
 };
 
 namespace emb {
+// Split-bag partials and tickets of an inference forward held outside a workspace
+struct FwdScratch {
+    float *part;
+    int32_t *pcnt;
+    uint32_t *tick;
+    int64_t tiles;
+};
+// bytes an inference forward of n_ids positions needs for them; with layout, the
+// regions placed from base (forward.hip)
+size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout, void *base);
+emb_status forward_with_scratch(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                                const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
+                                float *out, int64_t *stats, void *stream, const FwdScratch &sc);
 // host helpers (plan.cpp)
 emb_status fail(emb_status s, const std::string &msg);
 emb_status ok();

@@ -215,6 +215,22 @@ emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, const int32_
                             int32_t training, int64_t *stats, void *stream);
 
 /*
+ * emb_forward (inference, training = 0) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: the split-bag partials and tickets
+ * live in a fixed 32 MiB array inside the library, one per GPU, held until the
+ * process exits; the call allocates nothing.  A batch whose scratch would exceed
+ * the array (about 8 * tiles * max(dim) bytes, tiles = ceil(n_ids / tile))
+ * returns EMB_ERR_WORKSPACE before anything is enqueued.  Each call first clears
+ * the tickets it uses with a fill kernel on `stream`.  All calls on one GPU share
+ * its array: calls that overlap on one GPU (unordered streams) race; order them.
+ * Other arguments, layout and errors as emb_forward.
+ */
+emb_status emb_forward_noalloc(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
+                               const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
+                               float *out, int64_t *stats, void *stream);
+
+/*
  * Backward of the last training forward on this workspace: deduplicates the
  * touched (column, row) pairs by a radix sort of their keys, sums each pair's
  * contributions w_r * grad_out[s(r), off_c:off_c+dim] and applies opts->opt.
