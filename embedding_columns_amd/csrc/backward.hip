@@ -957,8 +957,8 @@ constexpr int kKeyWin = kSegShort + kTileMax + 2 * kSegShort;   // keys [x0 - 64
 static_assert(kKeyWin % kWave == 0, "key window loads are unrolled per lane");
 
 struct BwdLds {
-    int32_t bag[kSegSpan];      // bag of each contributor of the tile
-    float wt[kSegSpan];         // pooling weight of each contributor
+    int32_t bag[kSegSpan];      // bag of each contributor of the tile, then of each entry
+    float wt[kSegSpan];         // pooling weight of each contributor, then each entry's sum
     union {                     // the keys are read only before the walk, the pieces
                                 // only during it: sharing keeps a wave under 8 KB of
                                 // LDS, five waves per SIMD
@@ -967,6 +967,7 @@ struct BwdLds {
     };
     uint32_t seg[kOffCap];      // window of segment starts
     uint32_t ukey[kOffCap];     // unique keys of the same segments
+    int16_t eseg[kOffCap];      // first entry of each of the tile's segments (see compact_entries)
     int32_t hseg[kWave], hpass[kWave];
     int32_t njob;                  // segments whose last piece arrived here: summed by the
     int32_t job_u[4], job_c[4];    //   whole wavefront once the walk is done
@@ -994,12 +995,19 @@ __device__ __forceinline__ uint32_t ukeyat(const BwdArgs &, const BwdLds &L, con
     return L.ukey[u - t.wb];
 }
 
-__device__ __forceinline__ int seg_of(const BwdArgs &a, const BwdLds &L, const BTile &t, int p)
+// The walk runs over entries (compact_entries): segment u's first entry in the
+// tile, and the segment holding entry e.
+__device__ __forceinline__ int esegat(const BwdLds &L, const BTile &t, int u)
+{
+    return (int)L.eseg[u - t.uf];
+}
+
+__device__ __forceinline__ int eseg_of(const BwdLds &L, const BTile &t, int e)
 {
     int lo = t.uf, hi = t.ul + 1;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (segat(a, L, t, mid) <= p) lo = mid; else hi = mid;
+        if (esegat(L, t, mid) <= e) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -1176,8 +1184,12 @@ __device__ __forceinline__ void bwd_job(const BwdArgs &a, const BwdLds &L, const
     if (lane == 0) st_agent(&a.tick[k0], 0u);  // ready for the next call
 }
 
-// one column run [s0, s1) of sorted contributors; P lanes per gradient row
-template <int OPT, bool BF>
+// one column run [s0, s1) of the tile's entries; P lanes per gradient row.
+// DENSE (most entries start a segment): the rows of the entries' segments are
+// loaded with the gradient slices.  Otherwise (long segments, the hot rows of a
+// skewed column) the walk loads gradient slices only, and a segment that ends
+// inside the run loads its row when it ends (a wait, but a rare one).
+template <int OPT, bool BF, bool DENSE>
 __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const BTile &t,
                                             const DevCol &col, int c, int s0, int s1)
 {
@@ -1194,17 +1206,17 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     int hseg = -1, tseg = -1;
     bool hpass = false;
     if (ga < ge) {
-        int u = seg_of(a, L, t, ga);
-        int uend = segat(a, L, t, u + 1);
-        bool before = segat(a, L, t, u) < ga;
-        // Row loads are issued for every contributor, unconditionally: the row of
-        // the segment holding it (lanes past the row's end read lane 0's slice),
-        // used only where a segment starts.  Loads that are always issued keep the
+        int u = eseg_of(L, t, ga);
+        int uend = esegat(L, t, u + 1);
+        bool before = esegat(L, t, u) < ga;
+        // Row loads are issued for every entry, unconditionally: the row of the
+        // segment holding it (lanes past the row's end read lane 0's slice), used
+        // only where a segment starts.  Loads that are always issued keep the
         // compiler's wait counts exact; conditional ones made it wait for every
         // earlier load before issuing the next.  Repeats of a row hit in cache.
         const int qq = qa ? q : 0;
         RowPre cur;
-        row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u, qq), cur);
+        if (DENSE) row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u, qq), cur);
         int64_t e = row_elem(a, L, t, col, u, qq);
         const float *gq = a.G + col.out_off + qq * 4;
         for (int p = ga; p < ge; p += U) {
@@ -1220,21 +1232,24 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 st[j] = p + j < ge && p + j == ue;
                 if (st[j]) {
                     ns++;
-                    ue = segat(a, L, t, u + ns + 1);   // end of segment u + ns
+                    ue = esegat(L, t, u + ns + 1);   // end of segment u + ns
                 }
                 // a.zero stops the compiler from merging repeats of one row into
                 // register copies, which would wait for the load
-                row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u + ns, qq) + (int64_t)j * a.zero, pre[j]);
+                if (DENSE)
+                    row_load<OPT, BF>(a, col, row_elem(a, L, t, col, u + ns, qq) + (int64_t)j * a.zero, pre[j]);
             }
 #pragma unroll
             for (int j = 0; j < U; j++) {
-                const int pl = min(p + j, ge - 1) - t.t0;
+                const int pl = min(p + j, ge - 1);
                 wt[j] = p + j < ge ? L.wt[pl] : 0.f;
                 x[j] = *gp(reinterpret_cast<const float4 *>(gq + (int64_t)(L.bag[pl] - cB) * a.sumD));
             }
             // every load of the batch lands before the row stores below
+            if (DENSE) {
 #pragma unroll
-            for (int j = 0; j < U; j++) row_landed<OPT, BF>(pre[j]);
+                for (int j = 0; j < U; j++) row_landed<OPT, BF>(pre[j]);
+            }
 #pragma unroll
             for (int j = 0; j < U; j++) landed(x[j]);
 #pragma unroll
@@ -1246,13 +1261,14 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                             for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                             hseg = u; hpass = false;
                         } else if (qa && seg_live(a, L, t, u)) {
-                            row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
+                            if (DENSE) row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
+                            else seg_out<OPT, BF>(a, L, t, col, u, acc, q, qa);
                         }
 #pragma unroll
                         for (int v = 0; v < 4; v++) acc[v] = 0.f;
                         u++;
                         before = false;
-                        cur = pre[j];
+                        if (DENSE) cur = pre[j];
                         e = row_elem(a, L, t, col, u, qq);
                     }
                     acc[0] += wt[j] * x[j].x;
@@ -1269,7 +1285,8 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
                 for (int v = 0; v < 4; v++) hacc[v] = acc[v];
                 hseg = u; hpass = false;
             } else if (qa && seg_live(a, L, t, u)) {
-                row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
+                if (DENSE) row_apply<OPT, BF>(a, col, u, e, acc, cur, q);
+                else seg_out<OPT, BF>(a, L, t, col, u, acc, q, qa);
             }
         } else if (before) {
 #pragma unroll
@@ -1396,6 +1413,87 @@ __device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L
     t.ul = nseg - 1;
 }
 
+// Entries: the tile's contributors [t0, t1) merged into maximal runs of one
+// segment (one row) and one bag.  The stable sort keeps such runs together,
+// and every contribution in one carries the same gradient slice G[bag], so the
+// walk reads that slice once, times the run's summed weight (w times the run
+// length when the weight is the bag's pooling weight; the sum of the
+// per-position weights otherwise, added in contributor order).  In a long
+// sequence a hot row repeats inside a bag many times over.  L.bag / L.wt are
+// rewritten in place with the entries, and L.eseg[s] gets the first entry of the
+// tile's s-th segment (t.uf + s): -1 when that segment began before the tile,
+// and at s = nseg the entry count E, or E + 1 when the last segment goes on past
+// the tile (so the walk does not take it as finished).  Returns E.
+template <bool PW>
+__device__ __forceinline__ int compact_entries(BwdLds &L, const BTile &t, int x0)
+{
+    constexpr int kPL = kSegSpan / kWave;
+    const int lane = lane_id();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int kb = x0 - kSegShort;                 // position of L.kw[0]
+    const int len = t.t1 - t.t0;                   // 1 .. kSegSpan
+    int bg[kPL];
+    float ws[kPL];
+    uint64_t hm[kPL], sm[kPL];
+    // heads of entries (hm) and of segments (sm), by ballot
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int idx = lane + kWave * i;
+        const bool in = idx < len;
+        const int j = min(idx, len - 1);
+        const int p = t.t0 + j;
+        bg[i] = L.bag[j];
+        const bool sf = in && (idx == 0 || L.kw[p - kb] != L.kw[p - 1 - kb]);
+        const bool hd = in && (sf || bg[i] != L.bag[max(j - 1, 0)]);
+        hm[i] = __ballot(hd);
+        sm[i] = __ballot(sf);
+    }
+    // each head's summed weight, up to the next head (the masks are uniform)
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int idx = lane + kWave * i;
+        ws[i] = 0.f;
+        if ((hm[i] >> lane) & 1ull) {
+            const uint64_t rest = lane < kWave - 1 ? hm[i] >> (lane + 1) : 0ull;
+            int nxt = len;
+            if (rest) {
+                nxt = idx + __ffsll((unsigned long long)rest);
+            } else {
+#pragma unroll
+                for (int k = kPL - 1; k > i; k--)
+                    if (hm[k]) nxt = kWave * k + __ffsll((unsigned long long)hm[k]) - 1;
+            }
+            if (PW) {
+                float w = 0.f;
+                for (int k = idx; k < nxt; k++) w += L.wt[k];
+                ws[i] = w;
+            } else {
+                ws[i] = L.wt[idx] * (float)(nxt - idx);
+            }
+        }
+    }
+    wave_sync();                                   // every read above precedes the writes
+    int E = 0, S = 0;
+#pragma unroll
+    for (int i = 0; i < kPL; i++) {
+        const int e = E + __popcll(hm[i] & lt_mask), sl = S + __popcll(sm[i] & lt_mask);
+        if ((hm[i] >> lane) & 1ull) {
+            L.bag[e] = bg[i];
+            L.wt[e] = ws[i];
+        }
+        if ((sm[i] >> lane) & 1ull) L.eseg[sl] = (int16_t)e;
+        E += __popcll(hm[i]);
+        S += __popcll(sm[i]);
+    }
+    wave_sync();
+    if (lane == 0) {
+        if ((int)L.seg[t.uf - t.wb] < t.t0) L.eseg[0] = -1;
+        L.eseg[S] = (int16_t)((int)L.seg[t.ul + 1 - t.wb] == t.t1 ? E : E + 1);
+    }
+    wave_sync();
+    return E;
+}
+
 // Where a tile boundary lands: the nominal boundary x, or the end of the short
 // segment (run of equal sorted keys) that x cuts.  The run is measured inside
 // the staged keys x - 64 .. x + 63; a run reaching either edge counts as long.
@@ -1474,10 +1572,16 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
             nr[i] = mean ? max(*gp(a.bag_n + bagr[i]), 1) : 1;
         }
     } else if (a.any_mean) {
+        // the mean weight of each contributor's bag; a plan that mixes sum and
+        // mean columns looks up the pooling of the contributor's column (both
+        // loads depend only on the bag, so they go out together).  A bag with no
+        // valid position reaches here only through its default row's entry,
+        // whose weight is 1.
 #pragma unroll
-        // (a bag with no valid position reaches here only through its default
-        // row's entry, whose weight is 1)
-        for (int i = 0; i < kPL; i++) nr[i] = max(*gp(a.bag_n + bagr[i]), 1);
+        for (int i = 0; i < kPL; i++) {
+            const bool mean = a.all_mean ? true : *gp(&a.cols[bagr[i] / a.B].pool) == EMB_POOL_MEAN;
+            nr[i] = mean ? max(*gp(a.bag_n + bagr[i]), 1) : 1;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < kPL; i++) nr[i] = 1;
@@ -1523,31 +1627,36 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         const int p = x0 + lane + kWave * i;
         if (p >= t.t0 && p < t.t1) {
             L.bag[p - t.t0] = bagr[i];
-            // mean weight; sum columns use 1 (PW: times the contributor's weight)
+            // pooling weight: 1 / n for a mean bag, 1 for a sum bag (PW: times the
+            // contributor's own weight)
             L.wt[p - t.t0] = PW ? vw[i] * __builtin_amdgcn_rcpf((float)nr[i])
                                 : __builtin_amdgcn_rcpf((float)nr[i]);
         }
     }
     if (lane == 0) L.njob = 0;
     wave_sync();
-    // column runs: contributors are sorted by (column, row), and bag / B is the column
-    int p = t.t0;
-    while (p < t.t1) {
-        const int c = uniform(L.bag[p - t.t0] / a.B);
+    const int ne = compact_entries<PW>(L, t, x0);
+    // column runs: entries are sorted by (column, row), and bag / B is the column
+    int p = 0;
+    while (p < ne) {
+        const int c = uniform(L.bag[p] / a.B);
         const int lim = (c + 1) * a.B;
-        int lo = p, hi = t.t1;          // first contributor of a later column
+        int lo = p, hi = ne;            // first entry of a later column
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (L.bag[mid - t.t0] < lim) lo = mid + 1; else hi = mid;
+            if (L.bag[mid] < lim) lo = mid + 1; else hi = mid;
         }
         const int s1 = uniform(lo);
         const DevCol col = a.cols[c];
-        if (!PW && col.pool != EMB_POOL_MEAN) {
-            for (int q = p + lane; q < s1; q += kWave) L.wt[q - t.t0] = 1.0f;
-            wave_sync();
+        // the dense walk where segments average fewer than 4 entries
+        const bool dense = s1 - p < 4 * (eseg_of(L, t, s1 - 1) - eseg_of(L, t, p) + 1);
+        if (col.dtype == EMB_BF16) {
+            if (dense) bwd_segment<OPT, true, true>(a, L, t, col, c, p, s1);
+            else bwd_segment<OPT, true, false>(a, L, t, col, c, p, s1);
+        } else {
+            if (dense) bwd_segment<OPT, false, true>(a, L, t, col, c, p, s1);
+            else bwd_segment<OPT, false, false>(a, L, t, col, c, p, s1);
         }
-        if (col.dtype == EMB_BF16) bwd_segment<OPT, true>(a, L, t, col, c, p, s1);
-        else bwd_segment<OPT, false>(a, L, t, col, c, p, s1);
         p = s1;
     }
     wave_sync();
