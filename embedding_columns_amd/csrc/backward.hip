@@ -1648,8 +1648,10 @@ __global__ __launch_bounds__(kTileBlock, 4) void seg_apply(BwdArgs a)
         }
         const int s1 = uniform(lo);
         const DevCol col = a.cols[c];
-        // the dense walk where segments average fewer than 4 entries
-        const bool dense = s1 - p < 4 * (eseg_of(L, t, s1 - 1) - eseg_of(L, t, p) + 1);
+        // the dense walk where segments average fewer than 8 entries (measured:
+        // with 4, short-segment runs of the training front end lost 6 % to the
+        // waits of the gradient-only walk; always dense, long sequences lost 6 %)
+        const bool dense = s1 - p < 8 * (eseg_of(L, t, s1 - 1) - eseg_of(L, t, p) + 1);
         if (col.dtype == EMB_BF16) {
             if (dense) bwd_segment<OPT, true, true>(a, L, t, col, c, p, s1);
             else bwd_segment<OPT, true, false>(a, L, t, col, c, p, s1);

@@ -175,12 +175,21 @@ __device__ __forceinline__ int64_t wave_lower_bound(const T *a, int64_t n, T x)
     return lo;
 }
 
-// Sum over the wavefront with DPP row shifts / swizzles (via shfl_xor).
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t v)
+// Sum over the 64 lanes of a wavefront with DPP moves (gfx9 controls): swaps
+// inside quads, the half-row and row mirrors, then the row broadcasts of lanes 15
+// and 31 into the odd rows and the upper half; the total ends in lane 63 and is
+// read out as a uniform value.  Every lane of the wavefront must be active.  The
+// per-lane values are counts small enough that the total fits 32 bits.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
 }
 
 // Wait here for loaded values (an empty asm that reads them and orders memory).

@@ -52,11 +52,14 @@ struct FwdArgs {
     int32_t *pcnt;
     uint32_t *tick;
     int64_t *stats;
+    int32_t *fstat;          // with stats: each tile's counters [ntiles][kFStat], summed
+                             // by fwd_stats afterwards (NULL: atomics on stats)
     uint32_t total_rows;
     uint32_t *cstart;        // training: first position of each column, [C + 1]
 };
 
 constexpr int kColCache = 8;
+constexpr int kFStat = 8;          // counters per tile record (6 used)
 
 // What one launch of the forward kernel does:
 //   kFused      transform + gather + pool (emb_forward, emb_forward_ex);
@@ -735,10 +738,18 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     // launch counts only its bags)
     if (MODE == kFromRows) cnt[0] = cnt[1] = cnt[2] = cnt[3] = cnt[4] = 0;
     if (a.stats) {
-        const int64_t s0 = wave_sum_i64(cnt[0]), s1 = wave_sum_i64(cnt[1]);
-        const int64_t s2 = wave_sum_i64(cnt[2]), s3 = wave_sum_i64(cnt[3]);
-        const int64_t s4 = wave_sum_i64(zero_bags), s5 = wave_sum_i64(cnt[4]);
-        if (lane == 0) {
+        const uint32_t s0 = wave_sum_u32(cnt[0]), s1 = wave_sum_u32(cnt[1]);
+        const uint32_t s2 = wave_sum_u32(cnt[2]), s3 = wave_sum_u32(cnt[3]);
+        const uint32_t s4 = wave_sum_u32(zero_bags), s5 = wave_sum_u32(cnt[4]);
+        if (a.fstat) {
+            // this tile's record; fwd_stats adds all of them afterwards (same-address
+            // atomics from every tile serialized the forward)
+            if (lane == 0) {
+                uint4 *r = reinterpret_cast<uint4 *>(a.fstat + t.k * kFStat);
+                r[0] = make_uint4(s0, s1, s2, s3);
+                r[1] = make_uint4(s4, s5, 0u, 0u);
+            }
+        } else if (lane == 0) {
             if (s0) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_IDS], (unsigned long long)s0);
             if (s1) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_VALID], (unsigned long long)s1);
             if (s2) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_DROPPED], (unsigned long long)s2);
@@ -746,6 +757,33 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             if (s4) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_ZERO_BAGS], (unsigned long long)s4);
             if (s5) atomicAdd((unsigned long long *)&a.stats[EMB_STAT_FILTERED], (unsigned long long)s5);
         }
+    }
+}
+
+// The forward's counters: the sum of every tile's record, added to stats.
+__global__ __launch_bounds__(kBlock) void fwd_stats(const int32_t *__restrict__ fstat, int64_t ntiles,
+                                                   int64_t *__restrict__ stats)
+{
+    __shared__ uint32_t part[kWavesPerBlock][6];
+    uint32_t acc[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < ntiles; k += (int64_t)gridDim.x * kBlock) {
+        const uint4 r0 = *gp(reinterpret_cast<const uint4 *>(fstat + k * kFStat));
+        const uint4 r1 = *gp(reinterpret_cast<const uint4 *>(fstat + k * kFStat + 4));
+        acc[0] += r0.x; acc[1] += r0.y; acc[2] += r0.z; acc[3] += r0.w; acc[4] += r1.x; acc[5] += r1.y;
+    }
+    const int w = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < 6; i++) {
+        const uint32_t s = wave_sum_u32(acc[i]);
+        if (lane_id() == 0) part[w][i] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < 6) {
+        unsigned long long s = 0;
+        for (int k = 0; k < kWavesPerBlock; k++) s += part[k][threadIdx.x];
+        const int idx[6] = {EMB_STAT_IDS, EMB_STAT_VALID, EMB_STAT_DROPPED, EMB_STAT_DEFAULT,
+                            EMB_STAT_ZERO_BAGS, EMB_STAT_FILTERED};
+        if (s) atomicAdd((unsigned long long *)&stats[idx[threadIdx.x]], s);
     }
 }
 
@@ -819,10 +857,12 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
         a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
         a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
     }
+    if (ws) a.fstat = reinterpret_cast<int32_t *>(ws + plan->ws.fstat);
     if (sc) {
         a.part = sc->part;
         a.pcnt = sc->pcnt;
         a.tick = sc->tick;
+        a.fstat = sc->fstat;
     }
     a.stats = stats;
     a.total_rows = plan->total_rows;
@@ -851,6 +891,13 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_kernel launch: ") + hipGetErrorString(e));
+    if (stats && a.fstat) {
+        const int64_t sb = std::min<int64_t>(64, (a.ntiles + kBlock - 1) / kBlock);
+        hipLaunchKernelGGL(fwd_stats, dim3((unsigned)sb), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                           a.fstat, a.ntiles, stats);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("fwd_stats launch: ") + hipGetErrorString(e));
+    }
     return EMB_OK;
 }
 
@@ -899,14 +946,16 @@ size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout
     const size_t part = a256(sizeof(float) * 2 * (size_t)tiles * (size_t)plan->max_dim);
     const size_t pcnt = a256(sizeof(int32_t) * 2 * (size_t)tiles);
     const size_t tick = a256(sizeof(uint32_t) * (size_t)tiles);
+    const size_t fst = a256(sizeof(int32_t) * kFStat * (size_t)tiles);
     if (layout) {
         char *b = static_cast<char *>(base);
         layout->part = reinterpret_cast<float *>(b);
         layout->pcnt = reinterpret_cast<int32_t *>(b + part);
         layout->tick = reinterpret_cast<uint32_t *>(b + part + pcnt);
+        layout->fstat = reinterpret_cast<int32_t *>(b + part + pcnt + tick);
         layout->tiles = tiles;
     }
-    return part + pcnt + tick;
+    return part + pcnt + tick + fst;
 }
 
 emb_status forward_with_scratch(emb_plan *plan, const int32_t *offsets, const int64_t *ids,

@@ -68,6 +68,7 @@ struct WsLayout {
     size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
     size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
     size_t ccnt;                              // column sort -> compaction: valid keys per column, their prefix [2 (C + 1)]
+    size_t fstat;                             // forward counters, one 8-word record per tile
     size_t total;
 };
 
@@ -128,6 +129,7 @@ struct FwdScratch {
     float *part;
     int32_t *pcnt;
     uint32_t *tick;
+    int32_t *fstat;
     int64_t tiles;
 };
 // bytes an inference forward of n_ids positions needs for them; with layout, the

@@ -127,6 +127,7 @@ void plan_layout(emb_plan &P)
     L.bw = take(8 * N);
     L.posid = take(4 * N);
     L.ccnt = take(4 * 2 * ((size_t)P.n_cols + 1));
+    L.fstat = take(4 * 8 * P.max_tiles);
     L.total = o;
 }
 

@@ -248,7 +248,7 @@ __device__ __forceinline__ int32_t alloc_row(const TabArgs &a)
 
 __device__ __forceinline__ void stat_add(int64_t *stats, int idx, int64_t v)
 {
-    const int64_t s = wave_sum_i64(v);
+    const uint32_t s = wave_sum_u32((uint32_t)v);     // v is a 0 / 1 flag
     if (stats && lane_id() == 0 && s) atomicAdd((unsigned long long *)&stats[idx], (unsigned long long)s);
 }
 
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kCountTile) void ht_count(TabArgs a, const int64_t 
     }
     if (stats) {
         // one LDS update per wavefront
-        const int64_t si = wave_sum_i64(ins), sf = wave_sum_i64(full);
+        const uint32_t si = wave_sum_u32((uint32_t)ins), sf = wave_sum_u32((uint32_t)full);
         int64_t mp = probes;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mp = max(mp, (int64_t)__shfl_xor(mp, o, 64));
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void ht_evict_scan(TabArgs a, int32_t min_s
     }
     const uint64_t m = __ballot(live);
     const int lane = lane_id();
-    const int64_t ev = wave_sum_i64(occ && !live);
+    const uint32_t ev = wave_sum_u32(occ && !live ? 1u : 0u);
     if (lane == 0 && ev) atomicAdd(&a.next_row[kCtrEvicted], (int32_t)ev);
     if (!m) return;
     const int leader = __ffsll((long long)m) - 1;
