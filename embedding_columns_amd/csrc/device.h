@@ -201,6 +201,10 @@ __device__ __forceinline__ void landed(const float4 &v)
 {
     asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w) : "memory");
 }
+__device__ __forceinline__ void landed(const uint4 &v)
+{
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w) : "memory");
+}
 __device__ __forceinline__ void landed(const uint2 &v)
 {
     asm volatile("" ::"v"(v.x), "v"(v.y) : "memory");

@@ -83,7 +83,7 @@ struct WaveLds {
     float wt[kSpan];                 // weight of each tile position (extended forward)
     int32_t off[kOffCap];            // window of CSR offsets
     union {
-        float part[kWave][4];        // per-lane partial sum of each run's first bag
+        float part[kWave][8];        // per-lane partial sum of each run's first bag
         float bnd[kBndCap];          // bucket boundaries of the current column
     } x;
     int32_t hbag[kWave], hcnt[kWave], hpass[kWave];
@@ -162,12 +162,13 @@ __device__ __forceinline__ float4 row_slice(const DevCol &col, int64_t r, int q)
     return *gp(reinterpret_cast<const float4 *>(static_cast<const float *>(col.weights) + r * col.dim + q * 4));
 }
 
+// V: elements per lane (4, or 8 for bf16 rows whose dim is a multiple of 8)
 template <int V, bool EXT>
 __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int c, int bag,
                                         const float (&acc)[V], int n, int q, bool qa,
                                         int32_t &zero_bags)
 {
-    static_assert(V == 4, "one 4-element slice per lane");
+    static_assert(V == 4 || V == 8, "one or two 4-element slices per lane");
     const int s = bag - c * a.B;
     if (qa) {
         float o[V];
@@ -175,8 +176,11 @@ __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int
 #pragma unroll
         for (int v = 0; v < V; v++) o[v] = acc[v] * sc;
         if (EXT && n == 0 && col.default_row >= 0) {
-            const float4 d = row_slice(col, col.default_row, q);
-            o[0] = d.x; o[1] = d.y; o[2] = d.z; o[3] = d.w;
+#pragma unroll
+            for (int v = 0; v < V; v += 4) {
+                const float4 d = row_slice(col, col.default_row, q * (V / 4) + v / 4);
+                o[v] = d.x; o[v + 1] = d.y; o[v + 2] = d.z; o[v + 3] = d.w;
+            }
         }
         EMB_GLOBAL float4 *y = gp(reinterpret_cast<float4 *>(a.Y + (int64_t)s * a.sumD + col.out_off + q * V));
 #pragma unroll
@@ -244,27 +248,37 @@ __device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, c
     }
 }
 
-// 4 row elements of one lane as loaded: fp32, or bf16 pairs
-template <bool BF> struct RowRawT { using type = float4; };
-template <> struct RowRawT<true> { using type = uint2; };
-template <bool BF> using RowRaw = typename RowRawT<BF>::type;
+// the V row elements of one lane as loaded: fp32 (V = 4), or bf16 pairs (V = 4 or 8)
+template <bool BF, int V> struct RowRawT { using type = float4; };
+template <> struct RowRawT<true, 4> { using type = uint2; };
+template <> struct RowRawT<true, 8> { using type = uint4; };
+template <bool BF, int V> using RowRaw = typename RowRawT<BF, V>::type;
 
-__device__ __forceinline__ float4 row_f32(const float4 &v) { return v; }
-__device__ __forceinline__ float4 row_f32(const uint2 &v)
+__device__ __forceinline__ void row_f32(const float4 &v, float (&w)[4])
 {
-    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+}
+__device__ __forceinline__ void row_f32(const uint2 &v, float (&w)[4])
+{
+    w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+}
+__device__ __forceinline__ void row_f32(const uint4 &v, float (&w)[8])
+{
+    w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+    w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
 }
 
 // one column segment [s0, s1) of the tile.  A row is read by P lanes (a power
-// of two), 4 elements per lane: 16-byte loads for fp32 rows (BF false), 8-byte
-// for bf16.
-template <bool BF, bool W, bool EXT>
+// of two), V elements per lane: 16-byte loads for fp32 rows (BF false, V = 4),
+// 8-byte (V = 4) or 16-byte (V = 8) loads for bf16.  With 8 elements a lane
+// group pays its per-position work (row address, bag checks, counts) for twice
+// the elements; it keeps 4 loads in flight instead of 8, the same bytes.
+template <bool BF, bool W, bool EXT, int V>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
                                             int32_t &zero_bags)
 {
-    constexpr int V = 4;
-    constexpr int U = 8;                       // row loads in flight per lane
+    constexpr int U = V == 8 ? 4 : 8;          // row loads in flight per lane
     constexpr int esz = BF ? 2 : 4;
     const int P = col.lanes, lp = __ffs(P) - 1;
     const int G = kWave >> lp;
@@ -291,7 +305,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             // every load is issued (dropped / default / past-the-run positions read
             // row 0), so that the single wait below covers exactly these loads
             int r[U];
-            RowRaw<BF> h[U];
+            RowRaw<BF, V> h[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int x = L.rows[min(p + u, ge - 1) - t.t0];   // unconditional LDS reads
@@ -299,7 +313,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
             }
 #pragma unroll
             for (int u = 0; u < U; u++)
-                h[u] = *gp(reinterpret_cast<const RowRaw<BF> *>(
+                h[u] = *gp(reinterpret_cast<const RowRaw<BF, V> *>(
                     wbase + (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
 #pragma unroll
             for (int u = 0; u < U; u++) landed(h[u]);   // before the bag-end stores below
@@ -324,21 +338,18 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                 // every loaded row is consumed here, outside any branch: a load
                 // whose result is never read would make the next batch wait for
                 // every outstanding load and store before reusing its registers
-                const float4 w = row_f32(h[u]);
+                float w[V];
+                row_f32(h[u], w);
                 const bool use = pp < ge && r[u] >= 0;
                 if (EXT) {
                     // the weight is read here, not with the batch: registers are
                     // short in this loop
                     const float vw = L.wt[min(pp, ge - 1) - t.t0];
-                    acc[0] += use ? vw * w.x : 0.f;
-                    acc[1] += use ? vw * w.y : 0.f;
-                    acc[2] += use ? vw * w.z : 0.f;
-                    acc[3] += use ? vw * w.w : 0.f;
+#pragma unroll
+                    for (int v = 0; v < V; v++) acc[v] += use ? vw * w[v] : 0.f;
                 } else {
-                    acc[0] += use ? w.x : 0.f;
-                    acc[1] += use ? w.y : 0.f;
-                    acc[2] += use ? w.z : 0.f;
-                    acc[3] += use ? w.w : 0.f;
+#pragma unroll
+                    for (int v = 0; v < V; v++) acc[v] += use ? w[v] : 0.f;
                 }
                 if (pp < ge) {
                     cnt += (r[u] != -1);
@@ -673,11 +684,13 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
             if (s0 >= s1) continue;
             const DevCol col = a.cols[cu];
             if (win) {
-                if (col.dtype == EMB_BF16) fwd_segment<true, true, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
-                else fwd_segment<false, true, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
+                if (col.dtype == EMB_BF16 && col.vec == 8) fwd_segment<true, true, EXT, 8>(a, L, t, col, cu, s0, s1, zero_bags);
+                else if (col.dtype == EMB_BF16) fwd_segment<true, true, EXT, 4>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, true, EXT, 4>(a, L, t, col, cu, s0, s1, zero_bags);
             } else {
-                if (col.dtype == EMB_BF16) fwd_segment<true, false, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
-                else fwd_segment<false, false, EXT>(a, L, t, col, cu, s0, s1, zero_bags);
+                if (col.dtype == EMB_BF16 && col.vec == 8) fwd_segment<true, false, EXT, 8>(a, L, t, col, cu, s0, s1, zero_bags);
+                else if (col.dtype == EMB_BF16) fwd_segment<true, false, EXT, 4>(a, L, t, col, cu, s0, s1, zero_bags);
+                else fwd_segment<false, false, EXT, 4>(a, L, t, col, cu, s0, s1, zero_bags);
             }
         }
         if (a.training) {

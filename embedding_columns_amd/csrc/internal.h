@@ -47,8 +47,8 @@ struct DevCol {
     int32_t n_bnd;
     int32_t out_off;         // first output column of this embedding column
     uint32_t row_base;       // sum of rows of the columns before this one
-    int32_t lanes;           // lanes per row, 4 elements each: pow2 >= dim / 4
-    int32_t vec;             // elements per lane (4)
+    int32_t lanes;           // forward lanes per row, vec elements each: pow2 >= dim / vec
+    int32_t vec;             // forward elements per lane: 8 for bf16 rows with dim % 8 == 0, else 4
     int32_t glanes;          // lanes per gradient row (same as lanes)
     int32_t seq_max;         // keep at most this many positions per bag (0: all)
     int32_t seq_keep_last;   // ... the last seq_max (1) or the first (0)

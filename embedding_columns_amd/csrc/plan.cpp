@@ -178,8 +178,9 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
         h.n_bnd = (int32_t)d.n_boundaries;
         h.out_off = off;
         h.row_base = (uint32_t)row_base;
-        h.vec = 4;
-        h.lanes = pow2_ceil(d.dim / 4);
+        // forward: 8 bf16 elements per lane (16-byte loads) where the dim allows
+        h.vec = (d.dtype == EMB_BF16 && d.dim % 8 == 0) ? 8 : 4;
+        h.lanes = pow2_ceil(d.dim / h.vec);
         h.glanes = pow2_ceil(d.dim / 4);
         h.seq_max = d.seq_max;
         h.seq_keep_last = d.seq_keep_last;

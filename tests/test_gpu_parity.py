@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_harness import run_dense_case, Step, to_np, check_forward, check_rows_sgd, oracle_columns
+from gpu_harness import (run_dense_case, Step, to_np, check_forward, check_rows_sgd, oracle_columns,
+                         check_unique, check_emit)
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -291,6 +292,44 @@ def test_segments_from_keys_column_sort_capacity(big):
     oc = oracle_columns(w, [x.copy() for x in host_w])
     ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
                                          opt=w.opt, lr=w.lr)
+    for c, col in enumerate(cols):
+        sel = ucol == c
+        check_rows_sgd(col, host_w[c], to_np(st.gw[c]), oc.weights[c], urow[sel], ub[sel][:, :col.dim], w.lr)
+
+
+@pytest.mark.parametrize("mode", ["sgd_unique", "emit"])
+@pytest.mark.parametrize("mid_rows", [5000, 20000])
+@pytest.mark.parametrize("big", [12289, 20000])
+def test_column_sort_oversized_column_with_unique_list(big, mid_rows, mode):
+    # one column above the LDS capacity while the average column still fits: the
+    # oversized column is sorted through global memory in 7-bit passes (2 for
+    # 5000 rows, 3 for 20000: the result then ends in the other buffer), the
+    # valid keys of every column are counted and compacted into one sorted run,
+    # and the unique-row list is built from it
+    cols = [W.Column(W.HASH, W.SUM, W.F32, 300, 16, 0, 1 << 40),
+            W.Column(W.IDENTITY, W.MEAN, W.F32, mid_rows, 8),
+            W.Column(W.HASH, W.MEAN, W.F32, 40, 32, 0, 1 << 40)]
+    B = 8
+    lens = [5] * B + [0] * (B - 1) + [big] + [3, 0, 1, 700, 2, 2, 9, 4]
+    n = sum(lens)
+    rng = np.random.default_rng(big + mid_rows)
+    ids = rng.integers(-3, mid_rows + 200, size=n, dtype=np.int64)
+    opt = W.OPT_EMIT if mode == "emit" else W.OPT_SGD
+    w, b = _custom(cols, lens, ids=ids, B=B, opt=opt, lr=0.01)
+    wts, sts = W.make_tables(w, seed=14, device="cpu")
+    G = W.make_grad(w, seed=14, device="cpu")
+    st = Step(w, b, wts, sts, tile=256)
+    st.forward(training=True)
+    ukeys, ugrads, nu = st.backward(G, ask_unique=True)
+    torch.cuda.synchronize()
+    host_w = [to_np(x) for x in wts]
+    oc = oracle_columns(w, [x.copy() for x in host_w])
+    ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, G.numpy(), b.ids, b.fvals,
+                                         opt=w.opt, lr=w.lr)
+    check_unique(w, ukeys, nu, ucol, urow)
+    if opt == W.OPT_EMIT:
+        check_emit(w, ugrads, int(nu.item()), ucol, ug, ub)
+        return
     for c, col in enumerate(cols):
         sel = ucol == c
         check_rows_sgd(col, host_w[c], to_np(st.gw[c]), oc.weights[c], urow[sel], ub[sel][:, :col.dim], w.lr)
