@@ -93,8 +93,12 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDi
 }
 
 // digit histogram of one tile of kSortTile keys; equal digits within a
-// wavefront are added once
-__device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys, int64_t n, int shift,
+// wavefront are added once.  PI: the keys are the first words of (key, value)
+// pairs (the passes between the first and the last keep the pairs together, so
+// that a scattered digit run is one contiguous write instead of two)
+template <bool PI>
+__device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
+                                          const uint2 *__restrict__ pin, int64_t n, int shift,
                                           uint32_t *__restrict__ hist, int64_t nblk,
                                           uint32_t *__restrict__ misc, int64_t tile, uint32_t *h)
 {
@@ -109,7 +113,7 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys, int
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
         const int64_t idx = base + (int64_t)i * kBlock + t;
-        k[i] = idx < n ? *gp(keys + idx) : 0u;
+        k[i] = idx < n ? (PI ? (*gp(pin + idx)).x : *gp(keys + idx)) : 0u;
     }
     // plain LDS atomics; a wavefront whose lanes all carry one digit (hot rows in
     // the high passes) adds once
@@ -130,12 +134,14 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys, int
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys, int64_t n,
+template <bool PI>
+__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys,
+                                                 const uint2 *__restrict__ pin, int64_t n,
                                                  int shift, uint32_t *__restrict__ hist,
                                                  int64_t nblk, uint32_t *__restrict__ misc)
 {
     __shared__ uint32_t h[kRadix];
-    hist_tile(keys, n, shift, hist, nblk, misc, blockIdx.x, h);
+    hist_tile<PI>(keys, pin, n, shift, hist, nblk, misc, blockIdx.x, h);
 }
 
 // exclusive scan of one digit's block counts hist[d][0..nblk) in place, total -> dtot[d]
@@ -172,9 +178,12 @@ struct SortLds {
     uint32_t tmp[kWavesPerBlock];
 };
 
+// PI / PO: the input / output is (key, value) pairs instead of two arrays
+template <bool PI, bool PO>
 __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
                                              const uint32_t *__restrict__ vin,
                                              uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                             const uint2 *__restrict__ pin, uint2 *__restrict__ pout,
                                              int64_t n, int shift, const uint32_t *__restrict__ hist,
                                              const uint32_t *__restrict__ dtot, int64_t nblk,
                                              uint32_t sentinel, uint32_t *__restrict__ misc,
@@ -194,8 +203,14 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
     for (int j = 0; j < kSortItems; j++) {
         const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
         const bool in = li < cnt;
-        key[j] = in ? *gp(kin + base + li) : 0u;
-        val[j] = in ? *gp(vin + base + li) : 0u;
+        if (PI) {
+            const uint2 pr = in ? static_cast<uint2>(*gp(pin + base + li)) : make_uint2(0u, 0u);
+            key[j] = pr.x;
+            val[j] = pr.y;
+        } else {
+            key[j] = in ? *gp(kin + base + li) : 0u;
+            val[j] = in ? *gp(vin + base + li) : 0u;
+        }
     }
 
     // digit offsets: global prefix over digits + this block's offset within each digit
@@ -268,8 +283,12 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
         const uint32_t k = S.skey[lp];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = S.gbase[d] + (uint32_t)lp - S.lpre[d];
-        *gp(kout + dst) = k;
-        *gp(vout + dst) = S.sval[lp];
+        if (PO) {
+            *gp(pout + dst) = make_uint2(k, S.sval[lp]);
+        } else {
+            *gp(kout + dst) = k;
+            *gp(vout + dst) = S.sval[lp];
+        }
         if (k >= sentinel) first_sentinel = min(first_sentinel, dst);
     }
     // last pass: every key >= sentinel (dropped / default rows) sorts after the
@@ -281,16 +300,20 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
     __syncthreads();
 }
 
+template <bool PI, bool PO>
 __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict__ kin,
                                                     const uint32_t *__restrict__ vin,
                                                     uint32_t *__restrict__ kout,
-                                                    uint32_t *__restrict__ vout, int64_t n,
+                                                    uint32_t *__restrict__ vout,
+                                                    const uint2 *__restrict__ pin,
+                                                    uint2 *__restrict__ pout, int64_t n,
                                                     int shift, const uint32_t *__restrict__ hist,
                                                     const uint32_t *__restrict__ dtot, int64_t nblk,
                                                     uint32_t sentinel, uint32_t *__restrict__ misc)
 {
     __shared__ SortLds S;
-    scatter_tile(kin, vin, kout, vout, n, shift, hist, dtot, nblk, sentinel, misc, blockIdx.x, S);
+    scatter_tile<PI, PO>(kin, vin, kout, vout, pin, pout, n, shift, hist, dtot, nblk, sentinel, misc,
+                         blockIdx.x, S);
 }
 
 // ------------------------------------------------ column-local sort in LDS
@@ -1862,15 +1885,33 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
         if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("col_sort launch: ") + hipGetErrorString(e));
         if (from_keys) return EMB_OK;
     } else {
+        // the first pass reads the forward's keys and values, the last writes the
+        // sorted keys and values into kf / vf; the passes between keep (key, value)
+        // pairs together in two ping-pong buffers
+        uint2 *pairs[2] = {reinterpret_cast<uint2 *>(ws + W.pairs),
+                           reinterpret_cast<uint2 *>(ws + W.pairs) + (W.pairs_n)};
+        const dim3 grid((unsigned)nblk), block(kBlock);
         for (int p = 0; p < passes; p++) {
             const int shift = p * kRadixBits;
-            hipLaunchKernelGGL(rs_hist, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, n, shift, hist, nblk, misc);
+            const bool pi = p > 0, po = p < passes - 1;
+            const uint2 *pin = pi ? pairs[(p - 1) & 1] : nullptr;
+            uint2 *pout = po ? pairs[p & 1] : nullptr;
+            uint32_t *lm = (from_keys && p == passes - 1) ? misc : nullptr;
+            if (pi) hipLaunchKernelGGL(rs_hist<true>, grid, block, 0, st, nullptr, pin, n, shift, hist, nblk, misc);
+            else hipLaunchKernelGGL(rs_hist<false>, grid, block, 0, st, k0, nullptr, n, shift, hist, nblk, misc);
             hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
-            hipLaunchKernelGGL(rs_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, st, k0, v0, k1, v1, n,
-                               shift, hist, dtot, nblk, plan->total_rows,
-                               (from_keys && p == passes - 1) ? misc : nullptr);
-            std::swap(k0, k1);
-            std::swap(v0, v1);
+            if (pi && po)
+                hipLaunchKernelGGL((rs_scatter<true, true>), grid, block, 0, st, nullptr, nullptr, nullptr,
+                                   nullptr, pin, pout, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+            else if (pi)
+                hipLaunchKernelGGL((rs_scatter<true, false>), grid, block, 0, st, nullptr, nullptr, kf, vf,
+                                   pin, nullptr, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+            else if (po)
+                hipLaunchKernelGGL((rs_scatter<false, true>), grid, block, 0, st, k0, v0, nullptr, nullptr,
+                                   nullptr, pout, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+            else
+                hipLaunchKernelGGL((rs_scatter<false, false>), grid, block, 0, st, k0, v0, kf, vf, nullptr,
+                                   nullptr, n, shift, hist, dtot, nblk, plan->total_rows, lm);
         }
         if (from_keys) {
             hipError_t e = hipGetLastError();

@@ -272,13 +272,14 @@ __device__ __forceinline__ void row_f32(const uint4 &v, float (&w)[8])
 // of two), V elements per lane: 16-byte loads for fp32 rows (BF false, V = 4),
 // 8-byte (V = 4) or 16-byte (V = 8) loads for bf16.  With 8 elements a lane
 // group pays its per-position work (row address, bag checks, counts) for twice
-// the elements; it keeps 4 loads in flight instead of 8, the same bytes.
+// the elements.  Eight loads stay in flight per lane either way (with 8
+// elements, four in flight made the long-sequence forward 6 % slower).
 template <bool BF, bool W, bool EXT, int V>
 __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
                                             int32_t &zero_bags)
 {
-    constexpr int U = V == 8 ? 4 : 8;          // row loads in flight per lane
+    constexpr int U = 8;                       // row loads in flight per lane
     constexpr int esz = BF ? 2 : 4;
     const int P = col.lanes, lp = __ffs(P) - 1;
     const int G = kWave >> lp;

@@ -69,6 +69,8 @@ struct WsLayout {
     size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
     size_t ccnt;                              // column sort -> compaction: valid keys per column, their prefix [2 (C + 1)]
     size_t fstat;                             // forward counters, one 8-word record per tile
+    size_t pairs;                             // radix passes between the first and the last:
+    size_t pairs_n;                           //   (key, value) pairs, two buffers of pairs_n
     size_t total;
 };
 
