@@ -109,17 +109,37 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
     for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
     __syncthreads();
     const int64_t base = tile * kSortTile;
+    // the tile's keys in 16-byte loads (4 keys, or 2 pairs, per load); a
+    // histogram does not depend on which thread counts which key
     uint32_t k[kSortItems];
+    bool kin[kSortItems];
+    if (PI) {
 #pragma unroll
-    for (int i = 0; i < kSortItems; i++) {
-        const int64_t idx = base + (int64_t)i * kBlock + t;
-        k[i] = idx < n ? (PI ? (*gp(pin + idx)).x : *gp(keys + idx)) : 0u;
+        for (int i = 0; i < kSortItems / 2; i++) {
+            const int64_t idx = base + 2 * ((int64_t)i * kBlock + t);   // first of two pairs
+            const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(pin + idx)))
+                                    : make_uint4(0u, 0u, 0u, 0u);
+            k[2 * i] = v.x;
+            k[2 * i + 1] = v.z;
+            kin[2 * i] = idx < n;
+            kin[2 * i + 1] = idx + 1 < n;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kSortItems / 4; i++) {
+            const int64_t idx = base + 4 * ((int64_t)i * kBlock + t);
+            const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(keys + idx)))
+                                    : make_uint4(0u, 0u, 0u, 0u);
+            k[4 * i] = v.x; k[4 * i + 1] = v.y; k[4 * i + 2] = v.z; k[4 * i + 3] = v.w;
+#pragma unroll
+            for (int j = 0; j < 4; j++) kin[4 * i + j] = idx + j < n;
+        }
     }
     // plain LDS atomics; a wavefront whose lanes all carry one digit (hot rows in
     // the high passes) adds once
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
-        const bool in = base + (int64_t)i * kBlock + t < n;
+        const bool in = kin[i];
         const uint32_t d = (k[i] >> shift) & (kRadix - 1);
         const uint64_t act = __ballot(in);
         const uint32_t d0 = uniform(d);
@@ -144,18 +164,31 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
     hist_tile<PI>(keys, pin, n, shift, hist, nblk, misc, blockIdx.x, h);
 }
 
-// exclusive scan of one digit's block counts hist[d][0..nblk) in place, total -> dtot[d]
+// exclusive scan of one digit's block counts hist[d][0..nblk) in place, total ->
+// dtot[d]: each thread takes a contiguous run of the counts (all its loads in
+// flight together), one block-wide scan of the run sums, then the runs
+constexpr int kScanRun = 16;       // counts per thread per round: 4096 blocks per round
 __device__ __forceinline__ void scan_digit(uint32_t *__restrict__ hist, int64_t nblk,
                                            uint32_t *__restrict__ dtot, int d, uint32_t *tmp)
 {
     uint32_t *h = hist + (int64_t)d * nblk;
     uint32_t carry = 0;
-    for (int64_t s = 0; s < nblk; s += kBlock) {
-        const int64_t i = s + threadIdx.x;
-        const uint32_t v = i < nblk ? h[i] : 0u;
+    for (int64_t s = 0; s < nblk; s += (int64_t)kBlock * kScanRun) {
+        const int64_t i0 = s + (int64_t)threadIdx.x * kScanRun;
+        uint32_t v[kScanRun], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            v[k] = i0 + k < nblk ? h[i0 + k] : 0u;
+            sum += v[k];
+        }
         uint32_t ex;
-        const uint32_t tot = block_exclusive_scan(v, tmp, ex);
-        if (i < nblk) h[i] = carry + ex;
+        const uint32_t tot = block_exclusive_scan(sum, tmp, ex);
+        uint32_t run = carry + ex;
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            if (i0 + k < nblk) h[i0 + k] = run;
+            run += v[k];
+        }
         carry += tot;
     }
     if (threadIdx.x == 0) dtot[d] = carry;
@@ -978,19 +1011,23 @@ constexpr int kSegShort = 64;
 constexpr int kSegSpan = kTileMax + kSegShort;
 constexpr int kKeyWin = kSegShort + kTileMax + 2 * kSegShort;   // keys [x0 - 64, x0 + 384)
 static_assert(kKeyWin % kWave == 0, "key window loads are unrolled per lane");
+static_assert(kWave * 4 * sizeof(float) + kOffCap * sizeof(int16_t) <= kKeyWin * sizeof(uint32_t),
+              "the pieces and the entries' segment starts fit the key window's space");
 
 struct BwdLds {
     int32_t bag[kSegSpan];      // bag of each contributor of the tile, then of each entry
     float wt[kSegSpan];         // pooling weight of each contributor, then each entry's sum
-    union {                     // the keys are read only before the walk, the pieces
-                                // only during it: sharing keeps a wave under 8 KB of
-                                // LDS, five waves per SIMD
+    union {                     // the keys are read only until the entries are built,
+                                // the pieces and the entries' segment starts only after:
+                                // sharing keeps a wave at 8 KB of LDS, five waves per SIMD
         uint32_t kw[kKeyWin];   // sorted keys x0 - 64 .. x0 + 383 (sentinels outside [0, nv))
-        float part[kWave][4];
+        struct {
+            float part[kWave][4];
+            int16_t eseg[kOffCap];  // first entry of each of the tile's segments (compact_entries)
+        };
     };
     uint32_t seg[kOffCap];      // window of segment starts
     uint32_t ukey[kOffCap];     // unique keys of the same segments
-    int16_t eseg[kOffCap];      // first entry of each of the tile's segments (see compact_entries)
     int32_t hseg[kWave], hpass[kWave];
     int32_t njob;                  // segments whose last piece arrived here: summed by the
     int32_t job_u[4], job_c[4];    //   whole wavefront once the walk is done
@@ -1356,38 +1393,55 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
     wave_sync();
 }
 
-// number of leading keys i < n with key[i] < k or key[i] >= hi: the start of the
-// run of k when every key before it is smaller or at least hi (a 64-ary search)
-__device__ __forceinline__ int64_t wave_count_before(const uint32_t *key, int64_t n, uint32_t k,
-                                                     uint32_t hi)
+// The two ends of the runs that cross a tile's edges, searched together: the
+// start of the run of k0 in key[0, t0) (the leading keys are smaller, or at
+// least hi: dropped / DEFAULT keys the column sort left at the end of earlier
+// columns) and the end of the run of kl in key[t1, nv) (the keys after it are
+// larger).  Each round every lane probes once for each search that still runs
+// and both loads are in flight together, so a tile inside a long run (a hot
+// row) waits for the longer search only, not for both one after the other.
+__device__ __forceinline__ void run_bounds(const uint32_t *key, bool need_s, int64_t t0, uint32_t k0,
+                                           uint32_t hi, bool need_e, int64_t t1, int64_t nv,
+                                           uint32_t kl, int64_t &start, int64_t &end)
 {
-    int64_t lo = 0, up = n;
     const int l = lane_id();
-    while (up - lo > 64) {
-        const int64_t step = (up - lo + 63) / 64;
-        const int64_t i = lo + (int64_t)l * step;
-        bool b = false;
-        if (i < up) {
-            const uint32_t x = *gp(key + i);
-            b = x < k || x >= hi;
+    int64_t loA = 0, upA = need_s ? t0 : 0;      // answer in [loA, upA]
+    int64_t loB = t1, upB = need_e ? nv : t1;    // first index with key > kl, in [loB, upB]
+    bool a = upA - loA > 64, b = upB - loB > 64;
+    while (a || b) {
+        const int64_t sA = (upA - loA + 63) / 64, iA = loA + (int64_t)l * sA;
+        const int64_t sB = (upB - loB + 63) / 64, iB = loB + (int64_t)l * sB;
+        const uint32_t vA = (a && iA < upA) ? *gp(key + iA) : 0u;
+        const uint32_t vB = (b && iB < upB) ? *gp(key + iB) : 0xFFFFFFFFu;
+        const int cA = __popcll(__ballot(a && iA < upA && (vA < k0 || vA >= hi)));
+        const int cB = __popcll(__ballot(b && iB < upB && vB <= kl));
+        if (a) {
+            if (cA == 0) {
+                upA = loA;
+            } else {
+                const int64_t nu = loA + (int64_t)cA * sA < upA ? loA + (int64_t)cA * sA : upA;
+                loA = loA + (int64_t)(cA - 1) * sA + 1;
+                upA = nu;
+            }
         }
-        const int cnt = __popcll(__ballot(b));
-        if (cnt == 0) { up = lo; break; }
-        const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;
-        const int64_t nup = (lo + (int64_t)cnt * step < up) ? lo + (int64_t)cnt * step : up;
-        lo = nlo;
-        up = nup;
-    }
-    if (up > lo) {
-        const int64_t i = lo + l;
-        bool b = false;
-        if (i < up) {
-            const uint32_t x = *gp(key + i);
-            b = x < k || x >= hi;
+        if (b) {
+            if (cB == 0) {
+                upB = loB;
+            } else {
+                const int64_t nu = loB + (int64_t)cB * sB < upB ? loB + (int64_t)cB * sB : upB;
+                loB = loB + (int64_t)(cB - 1) * sB + 1;
+                upB = nu;
+            }
         }
-        lo += __popcll(__ballot(b));
+        a = upA - loA > 64;
+        b = upB - loB > 64;
     }
-    return lo;
+    // the last round of both: at most 64 candidates each
+    const int64_t iA = loA + l, iB = loB + l;
+    const uint32_t vA = iA < upA ? *gp(key + iA) : 0u;
+    const uint32_t vB = iB < upB ? *gp(key + iB) : 0xFFFFFFFFu;
+    start = loA + __popcll(__ballot(iA < upA && (vA < k0 || vA >= hi)));
+    end = loB + __popcll(__ballot(iB < upB && vB <= kl));
 }
 
 // The segments of tile t from the sorted keys, without a unique list: heads
@@ -1423,8 +1477,13 @@ __device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L
     // only a long segment crosses a tile boundary: its ends come from a search.
     // Keys before the run are smaller, or dropped / DEFAULT keys (>= total_rows)
     // that the column sort left at the end of earlier columns.
-    if (kprev == k0) start = (int)wave_count_before(a.skeys, (int64_t)t.t0, k0, a.total_rows);
-    if (knext == kl) end = t.t1 + (int)wave_upper_bound(a.skeys + t.t1, (int64_t)(nv - t.t1), kl);
+    if (kprev == k0 || knext == kl) {
+        int64_t s64, e64;
+        run_bounds(a.skeys, kprev == k0, (int64_t)t.t0, k0, a.total_rows, knext == kl, (int64_t)t.t1,
+                   (int64_t)nv, kl, s64, e64);
+        if (kprev == k0) start = (int)s64;
+        if (knext == kl) end = (int)e64;
+    }
     if (lane == 0) {
         L.seg[0] = (uint32_t)start;
         L.seg[nseg] = (uint32_t)end;
