@@ -154,6 +154,10 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
     __syncthreads();
 }
 
+// Both per-tile kernels take their tiles in one contiguous range per XCD: the
+// histogram words of neighbouring tiles (hist[d][b], hist[d][b + 1]) and the
+// two halves of a digit run cut by a line boundary then meet in one L2 instead
+// of reaching memory as partial lines from two XCDs.
 template <bool PI>
 __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys,
                                                  const uint2 *__restrict__ pin, int64_t n,
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
                                                  int64_t nblk, uint32_t *__restrict__ misc)
 {
     __shared__ uint32_t h[kRadix];
-    hist_tile<PI>(keys, pin, n, shift, hist, nblk, misc, blockIdx.x, h);
+    hist_tile<PI>(keys, pin, n, shift, hist, nblk, misc, xcd_block(blockIdx.x, gridDim.x, 0), h);
 }
 
 // exclusive scan of one digit's block counts hist[d][0..nblk) in place, total ->
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict_
 {
     __shared__ SortLds S;
     scatter_tile<PI, PO>(kin, vin, kout, vout, pin, pout, n, shift, hist, dtot, nblk, sentinel, misc,
-                         blockIdx.x, S);
+                         xcd_block(blockIdx.x, gridDim.x, 0), S);
 }
 
 // ------------------------------------------------ column-local sort in LDS
