@@ -135,19 +135,26 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
             for (int j = 0; j < 4; j++) kin[4 * i + j] = idx + j < n;
         }
     }
-    // plain LDS atomics; a wavefront whose lanes all carry one digit (hot rows in
-    // the high passes) adds once
+    // LDS atomics.  Skewed keys put most of a wavefront's lanes on one digit (the
+    // hot rows' digit in the high passes), and same-address atomics of one
+    // instruction run one after another: the lanes that share the digit of the
+    // first remaining lane are counted with one atomic, twice over, and only the
+    // lanes left after that add one each.
 #pragma unroll
     for (int i = 0; i < kSortItems; i++) {
-        const bool in = kin[i];
+        bool left = kin[i];
         const uint32_t d = (k[i] >> shift) & (kRadix - 1);
-        const uint64_t act = __ballot(in);
-        const uint32_t d0 = uniform(d);
-        if (__ballot(in && d == d0) == act) {
-            if (lane == 0 && act) atomicAdd(&h[d0], (uint32_t)__popcll(act));
-        } else if (in) {
-            atomicAdd(&h[d], 1u);
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const uint64_t rem = __ballot(left);
+            if (rem == 0) break;
+            const int fl = __ffsll((long long)rem) - 1;
+            const uint32_t dr = (uint32_t)__builtin_amdgcn_readlane((int)d, fl);
+            const uint64_t m = __ballot(left && d == dr);
+            if (lane == fl) atomicAdd(&h[dr], (uint32_t)__popcll(m));
+            left = left && d != dr;
         }
+        if (left) atomicAdd(&h[d], 1u);
     }
     __syncthreads();
     for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + tile] = h[d];
@@ -169,49 +176,63 @@ __global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ k
 }
 
 // exclusive scan of one digit's block counts hist[d][0..nblk) in place, total ->
-// dtot[d]: each thread takes a contiguous run of the counts (all its loads in
-// flight together), one block-wide scan of the run sums, then the runs
-constexpr int kScanRun = 16;       // counts per thread per round: 4096 blocks per round
-__device__ __forceinline__ void scan_digit(uint32_t *__restrict__ hist, int64_t nblk,
-                                           uint32_t *__restrict__ dtot, int d, uint32_t *tmp)
-{
-    uint32_t *h = hist + (int64_t)d * nblk;
-    uint32_t carry = 0;
-    for (int64_t s = 0; s < nblk; s += (int64_t)kBlock * kScanRun) {
-        const int64_t i0 = s + (int64_t)threadIdx.x * kScanRun;
-        uint32_t v[kScanRun], sum = 0;
-#pragma unroll
-        for (int k = 0; k < kScanRun; k++) {
-            v[k] = i0 + k < nblk ? h[i0 + k] : 0u;
-            sum += v[k];
-        }
-        uint32_t ex;
-        const uint32_t tot = block_exclusive_scan(sum, tmp, ex);
-        uint32_t run = carry + ex;
-#pragma unroll
-        for (int k = 0; k < kScanRun; k++) {
-            if (i0 + k < nblk) h[i0 + k] = run;
-            run += v[k];
-        }
-        carry += tot;
-    }
-    if (threadIdx.x == 0) dtot[d] = carry;
-}
-
-// one block per digit
+// dtot[d], one block per digit.  Per round of kScanChunk counts: coalesced loads
+// into LDS, each thread sums a contiguous run of kScanRun counts there, one
+// block-wide scan of the run sums, the run prefixes back through LDS, coalesced
+// stores.  (Each thread loading its own run straight from memory put 64
+// different lines behind every load instruction.)
+constexpr int kScanRun = 16;
+constexpr int kScanChunk = kBlock * kScanRun;     // 4096 blocks per round
 __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t nblk,
                                                  uint32_t *__restrict__ dtot)
 {
+    __shared__ uint32_t buf[kScanChunk];
     __shared__ uint32_t tmp[kWavesPerBlock];
-    scan_digit(hist, nblk, dtot, blockIdx.x, tmp);
+    const int t = threadIdx.x;
+    uint32_t *h = hist + (int64_t)blockIdx.x * nblk;
+    uint32_t carry = 0;
+    for (int64_t s0 = 0; s0 < nblk; s0 += kScanChunk) {
+        const int m = (int)min<int64_t>(kScanChunk, nblk - s0);
+        uint32_t v[kScanRun];
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            const int i = k * kBlock + t;
+            v[k] = i < m ? h[s0 + i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) buf[k * kBlock + t] = v[k];
+        __syncthreads();
+        uint32_t sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            v[k] = buf[t * kScanRun + k];
+            sum += v[k];
+        }
+        uint32_t ex;
+        const uint32_t tot = block_exclusive_scan(sum, tmp, ex);   // ends with a barrier
+        uint32_t run = carry + ex;
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            buf[t * kScanRun + k] = run;
+            run += v[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kScanRun; k++) {
+            const int i = k * kBlock + t;
+            if (i < m) h[s0 + i] = buf[i];
+        }
+        carry += tot;
+        __syncthreads();
+    }
+    if (t == 0) dtot[blockIdx.x] = carry;
 }
 
 struct SortLds {
     uint32_t skey[kSortTile];
     uint32_t sval[kSortTile];
-    uint32_t run[kWavesPerBlock][kRadix];   // per-wave running digit counts
-    uint32_t lpre[kRadix];                  // block-local digit prefix
-    uint32_t gbase[kRadix];                 // global destination of digit runs
+    uint16_t run[kWavesPerBlock][kRadix];   // per-wave running digit counts (<= 4096)
+    uint32_t gdst[kRadix];                  // global destination of digit d's run minus its LDS start
     uint32_t tmp[kWavesPerBlock];
 };
 
@@ -250,17 +271,17 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
         }
     }
 
-    // digit offsets: global prefix over digits + this block's offset within each digit
+    // digit offsets: global prefix over digits + this block's offset within each
+    // digit (kept by the thread that owns digits t * kDigitsPerThread + i)
+    uint32_t gbase[kDigitsPerThread];
     {
-        uint32_t v[kDigitsPerThread], ex[kDigitsPerThread];
+        uint32_t v[kDigitsPerThread];
 #pragma unroll
         for (int i = 0; i < kDigitsPerThread; i++) v[i] = dtot[t * kDigitsPerThread + i];
-        digit_exclusive_scan(v, ex, S.tmp);
+        digit_exclusive_scan(v, gbase, S.tmp);
 #pragma unroll
-        for (int i = 0; i < kDigitsPerThread; i++) {
-            const int d = t * kDigitsPerThread + i;
-            S.gbase[d] = ex[i] + hist[(int64_t)d * nblk + tile];
-        }
+        for (int i = 0; i < kDigitsPerThread; i++)
+            gbase[i] += hist[(int64_t)(t * kDigitsPerThread + i) * nblk + tile];
         for (int d = t; d < kRadix; d += kBlock)
             for (int i = 0; i < kWavesPerBlock; i++) S.run[i][d] = 0;
     }
@@ -276,7 +297,7 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
         rank[j] = before + (uint32_t)__popcll(peers & lt_mask);
         const bool leader = in && (peers >> lane) == 1ull;   // highest lane of its digit group
         wave_sync();
-        if (leader) S.run[w][d] = before + (uint32_t)__popcll(peers);
+        if (leader) S.run[w][d] = (uint16_t)(before + (uint32_t)__popcll(peers));
         wave_sync();
     }
     __syncthreads();
@@ -297,9 +318,9 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
 #pragma unroll
         for (int i = 0; i < kDigitsPerThread; i++) {
             const int d = t * kDigitsPerThread + i;
-            S.lpre[d] = lex[i];
+            S.gdst[d] = gbase[i] - lex[i];      // wraps; gdst + LDS position is the destination
 #pragma unroll
-            for (int k = 0; k < kWavesPerBlock; k++) S.run[k][d] = lex[i] + woff[i][k];
+            for (int k = 0; k < kWavesPerBlock; k++) S.run[k][d] = (uint16_t)(lex[i] + woff[i][k]);
         }
     }
     __syncthreads();
@@ -319,7 +340,7 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
     for (int lp = t; lp < cnt; lp += kBlock) {
         const uint32_t k = S.skey[lp];
         const uint32_t d = (k >> shift) & (kRadix - 1);
-        const uint32_t dst = S.gbase[d] + (uint32_t)lp - S.lpre[d];
+        const uint32_t dst = S.gdst[d] + (uint32_t)lp;
         if (PO) {
             *gp(pout + dst) = make_uint2(k, S.sval[lp]);
         } else {

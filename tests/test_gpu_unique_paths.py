@@ -42,3 +42,12 @@ def test_sgd_unique_list_asked(ncols):
     w = W.config(2, n_cols=ncols, batch=2048 if ncols == 24 else 12000,
                  rows_range=(1e2, 1e4), opt=W.OPT_SGD)
     run_dense_case(w, seed=5830 + ncols, tile=128, ask_unique=True)
+
+
+def test_emit_global_passes_many_blocks():
+    # about 18 M positions: some 4400 radix blocks of 4096 keys, so the per-digit
+    # scan of the block counts (4096 counts per round) takes two rounds; long
+    # Zipf sequences as in the long-sequence workload, on smaller tables
+    w = W.config(4, rows=200_000, batch=4096, opt=W.OPT_EMIT)
+    out = run_dense_case(w, seed=5840, tile=256)
+    assert out["batch"].n > 4096 * 4096
