@@ -169,6 +169,12 @@ def run(args):
     # keyed: one rows buffer per step, read after the timed region for the counts
     krows = torch.empty(n_pool, max_ids, dtype=torch.int32, device=dev) if keyed else None
     kinds = {c.kind for c in w.cols}
+    # EMIT: the backward's output, the distinct rows' keys and gradients
+    emit = training and w.opt == 0
+    ukeys = torch.empty(max(max_ids, 1), dtype=torch.int32, device=dev) if emit else None
+    nuniq = torch.zeros(1, dtype=torch.int64, device=dev) if emit else None
+    ugrads = (torch.empty(max(max_ids, 1), max(c.dim for c in w.cols), dtype=torch.float32, device=dev)
+              if emit else None)
 
     # device counters only with --stats (their atomics cost time); they are then
     # reported summed over the timed steps
@@ -245,9 +251,44 @@ def run(args):
             E.emb_backward_atomic(plan.plan, G, plan.workspace)
             mark(ev, "apply")
         elif training:
-            E.emb_backward_dedup(plan.plan, plan.workspace, None, None, tstats)
+            E.emb_backward_dedup(plan.plan, plan.workspace, ukeys, nuniq, tstats)
             mark(ev, "dedup")
-            E.emb_backward_apply(plan.plan, G, plan.workspace)
+            E.emb_backward_apply(plan.plan, G, plan.workspace, ugrads)
+            mark(ev, "apply")
+
+    # --graph: each batch's forward, dedup and apply captured once as three HIP
+    # graphs (the library's calls are plain kernel launches on the caller's
+    # stream, with no allocation, copy or memset), then replayed: one host call
+    # per stage instead of one per kernel.  Events between the replays time the
+    # stages as in the eager loop.
+    graphs = []
+
+    def capture():
+        torch.cuda.synchronize()
+        for j, d in enumerate(dbat):
+            n = d["n"]
+            ids = d["ids"] if kinds & {0, 1} else None
+            fv = d["fv"] if 2 in kinds else None
+            gs = [torch.cuda.CUDAGraph() for _ in range(3 if training else 1)]
+            with torch.cuda.graph(gs[0]):
+                E.emb_forward(plan.plan, d["off"], ids, fv, None, n, Y, plan.workspace, training, tstats)
+            if training:
+                with torch.cuda.graph(gs[1]):
+                    E.emb_backward_dedup(plan.plan, plan.workspace, ukeys, nuniq, tstats)
+                with torch.cuda.graph(gs[2]):
+                    E.emb_backward_apply(plan.plan, G, plan.workspace, ugrads)
+            graphs.append(gs)
+        torch.cuda.synchronize()
+
+    def replay(i, ev=None):
+        gs = graphs[i % len(graphs)]
+        mark(ev, "start")
+        gs[0].replay()
+        mark(ev, "fwd")
+        if training:
+            gs[1].replay()
+            mark(ev, "dedup")
+            gs[2].replay()
             mark(ev, "apply")
 
     # per-batch algorithmic bytes (dense workloads: valid counts from the generator's
@@ -269,12 +310,17 @@ def run(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.graph:
+        capture()
+        run_step = replay
+    else:
+        run_step = step
     stats.zero_()
     evs = [dict() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        run_step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] {args.steps} timed steps in {wall * 1e3:.1f} ms")
@@ -375,7 +421,8 @@ def run(args):
                    "backward": ("atomic" if args.atomic_backward else "sorted") if training else "none",
                    "tile": plan.opts.tile or 256, "fwd_launches_per_step": 2 if pipe else 1,
                    "pipelined_transform": bool(pipe),
-                   "position_weights": bool(args.weights)},
+                   "position_weights": bool(args.weights),
+                   "hip_graph": bool(args.graph)},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_median_ms": round(float(np.median(step_ms)), 4),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
@@ -506,7 +553,14 @@ def main():
                     help="transform the next batch on a second stream during the backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) to scale HBM counters")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each batch's forward, dedup and apply as captured HIP graphs")
     args = ap.parse_args()
+    if args.graph and (WORKLOADS[args.workload] == 5 or args.pipeline or args.weights
+                       or args.atomic_backward):
+        print("--graph covers the plain forward and the sorted backward of the dense workloads",
+              file=sys.stderr)
+        sys.exit(2)
     keyed = WORKLOADS[args.workload] == 5
     if args.steps is None:
         args.steps = 20 if keyed else 100
