@@ -8,11 +8,12 @@
 // "Reduce-ID" of RecIS Fig. 3) in ascending order and a fixed summation order,
 // so gradients and updated weights are deterministic run to run.
 //
-//   pass p (ceil(key_bits / 8) passes):
+//   pass p (ceil(key_bits / 9) passes of 9-bit digits):
 //     rs_hist     per-block digit histograms
 //     rs_scan     per-digit exclusive scan over blocks (+ digit totals)
 //     rs_scatter  per-wavefront stable ranking by ballot matching, LDS-local
 //                 digit sort, coalesced scatter of each digit run
+//   (inputs whose columns fit a workgroup's LDS take the column sort instead)
 //   uq_count / uq_scan / uq_write   segment heads -> unique keys + segment starts
 //   seg_apply   one tile of sorted contributors per wavefront: gather fp32
 //               G slices scaled by the pooling weight, sum per segment in
@@ -92,10 +93,10 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDi
     return tot;
 }
 
-// digit histogram of one tile of kSortTile keys; equal digits within a
-// wavefront are added once.  PI: the keys are the first words of (key, value)
-// pairs (the passes between the first and the last keep the pairs together, so
-// that a scattered digit run is one contiguous write instead of two)
+// digit histogram of one tile of kSortTile keys.  PI: the keys are the first
+// words of (key, value) pairs (the passes between the first and the last keep
+// the pairs together, so that a scattered digit run is one contiguous write
+// instead of two)
 template <bool PI>
 __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
                                           const uint2 *__restrict__ pin, int64_t n, int shift,
