@@ -1420,54 +1420,98 @@ __device__ __forceinline__ void bwd_segment(const BwdArgs &a, BwdLds &L, const B
 }
 
 // The two ends of the runs that cross a tile's edges, searched together: the
-// start of the run of k0 in key[0, t0) (the leading keys are smaller, or at
-// least hi: dropped / DEFAULT keys the column sort left at the end of earlier
-// columns) and the end of the run of kl in key[t1, nv) (the keys after it are
-// larger).  Each round every lane probes once for each search that still runs
-// and both loads are in flight together, so a tile inside a long run (a hot
-// row) waits for the longer search only, not for both one after the other.
+// start of the run of k0 that holds t0 - 1 (the keys before the run are smaller,
+// or at least hi: dropped / DEFAULT keys the column sort left at the end of
+// earlier columns) and the end of the run of kl that holds t1 (the keys after it
+// are larger).  Each search first gallops away from the tile over multiples of
+// the step, 64 probes per round, the step starting at the nominal tile size T
+// and growing 64-fold while all 64 probes stay in the run; then 64-ary rounds
+// narrow the bracket that the gallop found (at most one step wide) down to the
+// answer.  The gallop's probes are multiples of T, so every tile of a long run
+// reads the same few lines, and the narrowing rounds read the lines around the
+// run's ends, again shared by those tiles.  (A 64-ary search over the whole key
+// range put every round's probes on different lines for every tile: about
+// 0.24 GB of reads per long-sequence apply.)  Both searches advance together, so
+// a tile waits for the longer one only.
 __device__ __forceinline__ void run_bounds(const uint32_t *key, bool need_s, int64_t t0, uint32_t k0,
                                            uint32_t hi, bool need_e, int64_t t1, int64_t nv,
-                                           uint32_t kl, int64_t &start, int64_t &end)
+                                           uint32_t kl, int64_t T, int64_t &start, int64_t &end)
 {
     const int l = lane_id();
-    int64_t loA = 0, upA = need_s ? t0 : 0;      // answer in [loA, upA]
-    int64_t loB = t1, upB = need_e ? nv : t1;    // first index with key > kl, in [loB, upB]
-    bool a = upA - loA > 64, b = upB - loB > 64;
-    while (a || b) {
-        const int64_t sA = (upA - loA + 63) / 64, iA = loA + (int64_t)l * sA;
-        const int64_t sB = (upB - loB + 63) / 64, iB = loB + (int64_t)l * sB;
-        const uint32_t vA = (a && iA < upA) ? *gp(key + iA) : 0u;
-        const uint32_t vB = (b && iB < upB) ? *gp(key + iB) : 0xFFFFFFFFu;
-        const int cA = __popcll(__ballot(a && iA < upA && (vA < k0 || vA >= hi)));
-        const int cB = __popcll(__ballot(b && iB < upB && vB <= kl));
-        if (a) {
-            if (cA == 0) {
-                upA = loA;
+    // phase per side: 0 gallop, 1 narrow, 2 done
+    int pa = need_s ? 0 : 2, pb = need_e ? 0 : 2;
+    // A: while galloping, inA holds k0; then the start is in [loA, upA]
+    int64_t inA = t0 - 1, sA = T, loA = 0, upA = 0;
+    // B: while galloping, inB holds kl; then the end (first index past the run) is in [loB, upB]
+    int64_t inB = t1, sB = T, loB = t1, upB = t1;
+    start = t0;
+    end = t1;
+    while (pa < 2 || pb < 2) {
+        int64_t iA = -1, iB = nv, stA = 1, stB = 1, baseA = 0, baseB = 0;
+        if (pa == 0) {
+            baseA = inA / sA * sA;
+            iA = baseA - (int64_t)l * sA;
+        } else if (pa == 1) {
+            stA = upA - loA > 64 ? (upA - loA + 63) / 64 : 1;
+            iA = loA + (int64_t)l * stA;
+        }
+        if (pb == 0) {
+            baseB = (inB / sB + 1) * sB;
+            iB = baseB + (int64_t)l * sB;
+        } else if (pb == 1) {
+            stB = upB - loB > 64 ? (upB - loB + 63) / 64 : 1;
+            iB = loB + (int64_t)l * stB;
+        }
+        const bool okA = (pa == 0 && iA >= 0) || (pa == 1 && iA < upA);
+        const bool okB = (pb == 0 && iB < nv) || (pb == 1 && iB < upB);
+        const uint32_t vA = okA ? *gp(key + iA) : 0u;
+        const uint32_t vB = okB ? *gp(key + iB) : 0xFFFFFFFFu;
+        const bool runA = okA && vA >= k0 && vA < hi;      // holds k0
+        const bool runB = okB && vB <= kl;                 // holds kl
+        const int inRunA = __popcll(__ballot(runA));       // a prefix of the lanes while galloping
+        const int outA = __popcll(__ballot(okA && !runA)); // a prefix of the lanes while narrowing
+        const int inRunB = __popcll(__ballot(runB));       // a prefix of the lanes in both phases
+        if (pa == 0) {
+            if (inRunA == kWave) {
+                inA = baseA - (int64_t)(kWave - 1) * sA;
+                sA *= kWave;
             } else {
-                const int64_t nu = loA + (int64_t)cA * sA < upA ? loA + (int64_t)cA * sA : upA;
-                loA = loA + (int64_t)(cA - 1) * sA + 1;
+                upA = inRunA > 0 ? baseA - (int64_t)(inRunA - 1) * sA : inA;
+                const int64_t out = baseA - (int64_t)inRunA * sA;     // outside the run, or < 0
+                loA = out + 1 > 0 ? out + 1 : 0;
+                pa = 1;
+            }
+        } else if (pa == 1) {
+            if (stA == 1 || outA == 0) {
+                start = loA + (stA == 1 ? outA : 0);
+                pa = 2;
+            } else {
+                const int64_t nu = loA + (int64_t)outA * stA < upA ? loA + (int64_t)outA * stA : upA;
+                loA = loA + (int64_t)(outA - 1) * stA + 1;
                 upA = nu;
             }
         }
-        if (b) {
-            if (cB == 0) {
-                upB = loB;
+        if (pb == 0) {
+            if (inRunB == kWave) {
+                inB = baseB + (int64_t)(kWave - 1) * sB;
+                sB *= kWave;
             } else {
-                const int64_t nu = loB + (int64_t)cB * sB < upB ? loB + (int64_t)cB * sB : upB;
-                loB = loB + (int64_t)(cB - 1) * sB + 1;
+                loB = (inRunB > 0 ? baseB + (int64_t)(inRunB - 1) * sB : inB) + 1;
+                const int64_t out = baseB + (int64_t)inRunB * sB;     // outside the run, or >= nv
+                upB = out < nv ? out : nv;
+                pb = 1;
+            }
+        } else if (pb == 1) {
+            if (stB == 1 || inRunB == 0) {
+                end = loB + (stB == 1 ? inRunB : 0);
+                pb = 2;
+            } else {
+                const int64_t nu = loB + (int64_t)inRunB * stB < upB ? loB + (int64_t)inRunB * stB : upB;
+                loB = loB + (int64_t)(inRunB - 1) * stB + 1;
                 upB = nu;
             }
         }
-        a = upA - loA > 64;
-        b = upB - loB > 64;
     }
-    // the last round of both: at most 64 candidates each
-    const int64_t iA = loA + l, iB = loB + l;
-    const uint32_t vA = iA < upA ? *gp(key + iA) : 0u;
-    const uint32_t vB = iB < upB ? *gp(key + iB) : 0xFFFFFFFFu;
-    start = loA + __popcll(__ballot(iA < upA && (vA < k0 || vA >= hi)));
-    end = loB + __popcll(__ballot(iB < upB && vB <= kl));
 }
 
 // The segments of tile t from the sorted keys, without a unique list: heads
@@ -1506,7 +1550,7 @@ __device__ __forceinline__ void seg_window_from_keys(const BwdArgs &a, BwdLds &L
     if (kprev == k0 || knext == kl) {
         int64_t s64, e64;
         run_bounds(a.skeys, kprev == k0, (int64_t)t.t0, k0, a.total_rows, knext == kl, (int64_t)t.t1,
-                   (int64_t)nv, kl, s64, e64);
+                   (int64_t)nv, kl, (int64_t)a.T, s64, e64);
         if (kprev == k0) start = (int)s64;
         if (knext == kl) end = (int)e64;
     }
