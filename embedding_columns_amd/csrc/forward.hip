@@ -56,6 +56,7 @@ struct FwdArgs {
                              // by fwd_stats afterwards (NULL: atomics on stats)
     uint32_t total_rows;
     uint32_t *cstart;        // training: first position of each column, [C + 1]
+    const char *zrow;        // kZeroRow bytes of zeros
 };
 
 constexpr int kColCache = 8;
@@ -289,7 +290,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
     const int len = s1 - s0, Lg = (len + G - 1) / G;
     const int ga = min(s0 + g * Lg, s1), ge = min(ga + Lg, s1);
     // lanes past the row's end read lane 0's slice and ignore it
-    const char *wbase = static_cast<const char *>(col.weights) + (int64_t)(qa ? q : 0) * V * esz;
+    const int64_t loff = (int64_t)(qa ? q : 0) * V * esz;
+    const char *wptr = static_cast<const char *>(col.weights);
+    // without per-position weights, positions that add nothing (dropped, DEFAULT,
+    // past the run) read zeros instead of row 0, so every loaded slice is added
+    // as it is (no select per element); with weights they read row 0 and the sum
+    // selects, since a weight may be infinite
     const int64_t rstride = (int64_t)D * esz;
 
     float acc[V], hacc[V];
@@ -315,7 +321,8 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
 #pragma unroll
             for (int u = 0; u < U; u++)
                 h[u] = *gp(reinterpret_cast<const RowRaw<BF, V> *>(
-                    wbase + (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
+                    ((!EXT && r[u] < 0) ? a.zrow : wptr) + loff +
+                    (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
 #pragma unroll
             for (int u = 0; u < U; u++) landed(h[u]);   // before the bag-end stores below
 #pragma unroll
@@ -350,7 +357,7 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const 
                     for (int v = 0; v < V; v++) acc[v] += use ? vw * w[v] : 0.f;
                 } else {
 #pragma unroll
-                    for (int v = 0; v < V; v++) acc[v] += use ? w[v] : 0.f;
+                    for (int v = 0; v < V; v++) acc[v] += w[v];   // zeros where !use
                 }
                 if (pp < ge) {
                     cnt += (r[u] != -1);
@@ -870,9 +877,11 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
         a.pcnt = reinterpret_cast<int32_t *>(ws + plan->ws.fcnt);
         a.tick = reinterpret_cast<uint32_t *>(ws + plan->ws.ftick);
         a.cstart = reinterpret_cast<uint32_t *>(ws + plan->ws.cstart);
+        a.zrow = ws + plan->ws.zrow;
     }
     if (ws) a.fstat = reinterpret_cast<int32_t *>(ws + plan->ws.fstat);
     if (sc) {
+        a.zrow = sc->zrow;
         a.part = sc->part;
         a.pcnt = sc->pcnt;
         a.tick = sc->tick;
@@ -962,14 +971,17 @@ size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout
     const size_t tick = a256(sizeof(uint32_t) * (size_t)tiles);
     const size_t fst = a256(sizeof(int32_t) * kFStat * (size_t)tiles);
     if (layout) {
+        // the zero row first: it sits at the same place for every batch size
         char *b = static_cast<char *>(base);
+        layout->zrow = b;
+        b += kZeroRow;
         layout->part = reinterpret_cast<float *>(b);
         layout->pcnt = reinterpret_cast<int32_t *>(b + part);
         layout->tick = reinterpret_cast<uint32_t *>(b + part + pcnt);
         layout->fstat = reinterpret_cast<int32_t *>(b + part + pcnt + tick);
         layout->tiles = tiles;
     }
-    return part + pcnt + tick + fst;
+    return kZeroRow + part + pcnt + tick + fst;
 }
 
 emb_status forward_with_scratch(emb_plan *plan, const int32_t *offsets, const int64_t *ids,

@@ -69,6 +69,9 @@ struct WsLayout {
     size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
     size_t ccnt;                              // column sort -> compaction: valid keys per column, their prefix [2 (C + 1)]
     size_t fstat;                             // forward counters, one 8-word record per tile
+    size_t zrow;                              // 1 KB never written: stays zero (the workspace is
+                                              //   zero-filled once); the plain forward's masked
+                                              //   positions load it
     size_t pairs;                             // radix passes between the first and the last:
     size_t pairs_n;                           //   (key, value) pairs, two buffers of pairs_n
     size_t total;
@@ -128,12 +131,14 @@ struct emb_table {
 namespace emb {
 // Split-bag partials and tickets of an inference forward held outside a workspace
 struct FwdScratch {
+    const char *zrow;    // kZeroRow bytes that hold zero
     float *part;
     int32_t *pcnt;
     uint32_t *tick;
     int32_t *fstat;
     int64_t tiles;
 };
+constexpr size_t kZeroRow = 1024;   // the widest row a lane group reads: 256 fp32
 // bytes an inference forward of n_ids positions needs for them; with layout, the
 // regions placed from base (forward.hip)
 size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout, void *base);

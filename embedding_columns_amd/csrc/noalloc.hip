@@ -10,9 +10,10 @@
 // device current) and kept; host code never passes the array's own name to a
 // kernel, since in host code that name is a host-side stand-in.
 //
-// Every call on one GPU shares that GPU's array.  Tickets must start at zero:
-// each call clears the tickets it uses with a fill kernel before the forward
-// (no memset node, so the pair can be captured into a graph).  Two calls that
+// Every call on one GPU shares that GPU's array.  Tickets must start at zero,
+// and the forward's zero row must hold zeros: each call clears both with one
+// fill kernel before the forward (no memset node, so the pair can be captured
+// into a graph).  Two calls that
 // overlap on one GPU (different streams, no ordering) race on the array.
 #include <mutex>
 #include <string>
@@ -28,10 +29,13 @@ constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static void *g_scratch_ptr[kMaxDevices];
 
-__global__ __launch_bounds__(kBlock) void zero_words(uint32_t *__restrict__ p, int64_t n)
+// clears n0 words at p0 and n1 words at p1
+__global__ __launch_bounds__(kBlock) void zero_words(uint32_t *__restrict__ p0, int64_t n0,
+                                                     uint32_t *__restrict__ p1, int64_t n1)
 {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i < n) p[i] = 0u;
+    if (i < n0) p0[i] = 0u;
+    else if (i < n0 + n1) p1[i - n0] = 0u;
 }
 
 // the device address of this GPU's array, looked up on the first call here
@@ -74,8 +78,12 @@ extern "C" emb_status emb_forward_noalloc(emb_plan *plan, const int32_t *offsets
     if (s != EMB_OK) return s;
     FwdScratch sc{};
     fwd_scratch_bytes(plan, n_ids, &sc, base);
-    hipLaunchKernelGGL(zero_words, dim3((unsigned)((sc.tiles + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), sc.tick, sc.tiles);
+    // the tickets, and the zero row (the forward only reads it; cleared anyway,
+    // the array's contents before the first call being the loader's)
+    const int64_t zw = (int64_t)(kZeroRow / 4);
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)((sc.tiles + zw + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), sc.tick, sc.tiles,
+                       reinterpret_cast<uint32_t *>(const_cast<char *>(sc.zrow)), zw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("zero_words launch: ") + hipGetErrorString(e));
     return forward_with_scratch(plan, offsets, ids, fvals, keyed_rows, n_ids, out, stats, stream, sc);

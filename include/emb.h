@@ -220,9 +220,10 @@ emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, const int32_
  * forbid hipMalloc.  It takes no workspace: the split-bag partials and tickets
  * live in a fixed 32 MiB array inside the library, one per GPU, held until the
  * process exits; the call allocates nothing.  A batch whose scratch would exceed
- * the array (about (8 max(dim) + 44) bytes per tile, tiles = ceil(n_ids / tile))
- * returns EMB_ERR_WORKSPACE before anything is enqueued.  Each call first clears
- * the tickets it uses with a fill kernel on `stream`.  All calls on one GPU share
+ * the array (1 KB plus about (8 max(dim) + 44) bytes per tile, tiles =
+ * ceil(n_ids / tile)) returns EMB_ERR_WORKSPACE before anything is enqueued.  Each
+ * call first clears the tickets it uses and a 1 KB zero row with a fill kernel on
+ * `stream`.  All calls on one GPU share
  * its array: calls that overlap on one GPU (unordered streams) race; order them.
  * Other arguments, layout and errors as emb_forward.
  */
