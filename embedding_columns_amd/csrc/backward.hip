@@ -821,15 +821,41 @@ __device__ __forceinline__ void col_sort_column(ColSortShared &SU, uint32_t *kin
 
 // Valid keys (below total_rows) of column blockIdx.x, counted in its sorted keys:
 // the dropped ones sort after the column's rows.
+// Each column's count of valid keys into vcnt[c]; the workgroup whose column
+// finishes last (a ticket) then writes their exclusive prefix vbase[0 .. C]
+// (vbase[C]: all valid keys) and resets the ticket for the next call.
 __device__ __forceinline__ void col_valid_count(const uint32_t *kout, const uint32_t *cstart,
-                                                uint32_t total_rows, uint32_t *vcnt)
+                                                uint32_t total_rows, uint32_t *vcnt, int C)
 {
     __syncthreads();   // every wave's sorted keys are written
     if (threadIdx.x >= kWave) return;
-    const int c = blockIdx.x;
+    const int c = blockIdx.x, lane = lane_id();
+    uint32_t *vbase = vcnt + C + 1, *vtick = vbase + C + 1;
     const int64_t P0 = cstart[c], cnt = (int64_t)cstart[c + 1] - P0;
     const int64_t nv = (cnt > 0 && total_rows > 0) ? wave_upper_bound(kout + P0, cnt, total_rows - 1u) : 0;
-    if (lane_id() == 0) vcnt[c] = (uint32_t)nv;
+    if (lane == 0) st_agent(vcnt + c, (uint32_t)nv);
+    wait_vm();                                   // the count is visible before the ticket
+    uint32_t old = 0;
+    if (lane == 0) old = ticket_add(vtick);
+    old = (uint32_t)__shfl((int)old, 0, kWave);
+    if (old != (uint32_t)(C - 1)) return;
+    uint32_t carry = 0;
+    for (int s = 0; s < C; s += kWave) {
+        const int i = s + lane;
+        const uint32_t v = i < C ? ld_agent(vcnt + i) : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, kWave);
+            if (lane >= o) x += y;
+        }
+        if (i < C) vbase[i] = carry + x - v;
+        carry += (uint32_t)__shfl((int)x, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+        vbase[C] = carry;
+        st_agent(vtick, 0u);                     // ready for the next call
+    }
 }
 
 // One workgroup per column.  With vcnt, it also records the column's number of
@@ -842,26 +868,10 @@ __global__ __launch_bounds__(kCSBlock) void col_sort(uint32_t *kin, uint32_t *vi
 {
     __shared__ ColSortShared SU;
     col_sort_column(SU, kin, vin, kspare, vspare, kout, vout, n, cstart, row_base, total_rows, misc);
-    if (vcnt) col_valid_count(kout, cstart, total_rows, vcnt);
+    if (vcnt) col_valid_count(kout, cstart, total_rows, vcnt, (int)gridDim.x);
 }
 
 // exclusive prefix of the columns' valid counts: vbase[c]; vbase[C] = all valid keys
-__global__ __launch_bounds__(kBlock) void cs_vscan(const uint32_t *__restrict__ vcnt, int C,
-                                                  uint32_t *__restrict__ vbase)
-{
-    __shared__ uint32_t tmp[kWavesPerBlock];
-    uint32_t carry = 0;
-    for (int s = 0; s < C; s += kBlock) {
-        const int i = s + threadIdx.x;
-        const uint32_t v = i < C ? vcnt[i] : 0u;
-        uint32_t ex;
-        const uint32_t tot = block_exclusive_scan(v, tmp, ex);
-        if (i < C) vbase[i] = carry + ex;
-        carry += tot;
-    }
-    if (threadIdx.x == 0) vbase[C] = carry;
-}
-
 // The column-sorted keys and values, moved so that the valid keys of all columns
 // come first, column after column (one ascending run: columns own disjoint,
 // increasing key ranges), then every column's dropped keys: the layout one
@@ -898,9 +908,9 @@ struct UqLds {
     uint32_t tmp[kWavesPerBlock];
 };
 
-__device__ __forceinline__ int uq_stage(UqLds &S, const uint32_t *k, int64_t n)
+__device__ __forceinline__ int uq_stage(UqLds &S, const uint32_t *k, int64_t n,
+                                        int64_t base = (int64_t)blockIdx.x * kUqTile)
 {
-    const int64_t base = (int64_t)blockIdx.x * kUqTile;
     const int cnt = (int)min<int64_t>(kUqTile, n - base);
     uint32_t x[kUqTile / kBlock];
 #pragma unroll
@@ -1002,6 +1012,59 @@ __global__ __launch_bounds__(kBlock) void uq_write(const uint32_t *__restrict__ 
     if (blockIdx.x == 0 && threadIdx.x == 0) seg[misc[1]] = misc[0];   // seg[U] = valid contributors
 }
 
+// The three kernels above in one workgroup, for inputs of at most kUqSmall keys
+// (the tiny EMIT step): rounds of kUqTile keys, a running count of heads, and the
+// valid count (the first sentinel position, or n) by a block minimum.
+constexpr int64_t kUqSmall = 4 * kUqTile;
+__global__ __launch_bounds__(kBlock) void uq_small(const uint32_t *__restrict__ k, int64_t n,
+                                                  uint32_t total_rows, uint32_t *__restrict__ misc,
+                                                  uint32_t *__restrict__ seg,
+                                                  uint32_t *__restrict__ ukeys,
+                                                  uint32_t *__restrict__ user_keys, int64_t *n_uniq,
+                                                  int64_t *stats)
+{
+    __shared__ UqLds S;
+    __shared__ uint32_t first_sent;
+    if (threadIdx.x == 0) first_sent = (uint32_t)n;
+    uint32_t carry = 0;
+    const int i0 = threadIdx.x * kUqItems;
+    for (int64_t base = 0; base < n; base += kUqTile) {
+        const int cnt = uq_stage(S, k, n, base);
+        uint32_t c = 0;
+        for (int j = 0; j < kUqItems; j++) {
+            const int i = i0 + j;
+            if (i < cnt) {
+                c += uq_head(S, i, total_rows, base + i == 0);
+                const uint32_t x = S.key[i + 1];
+                if (x >= total_rows && (base + i == 0 || S.key[i] < total_rows))
+                    atomicMin(&first_sent, (uint32_t)(base + i));
+            }
+        }
+        uint32_t ex;
+        const uint32_t tot = block_exclusive_scan(c, S.tmp, ex);   // ends with a barrier
+        uint32_t u = carry + ex;
+        for (int j = 0; j < kUqItems; j++) {
+            const int i = i0 + j;
+            if (i < cnt && uq_head(S, i, total_rows, base + i == 0)) {
+                const uint32_t x = S.key[i + 1];
+                *gp(seg + u) = (uint32_t)(base + i);
+                *gp(ukeys + u) = x;
+                if (user_keys) *gp(user_keys + u) = x;
+                u++;
+            }
+        }
+        carry += tot;
+        __syncthreads();                         // the staged keys are reused next round
+    }
+    if (threadIdx.x == 0) {
+        misc[0] = first_sent;
+        misc[1] = carry;
+        seg[carry] = first_sent;                 // seg[U] = valid contributors
+        if (n_uniq) *n_uniq = carry;
+        if (stats) atomicAdd((unsigned long long *)&stats[EMB_STAT_UNIQUE], (unsigned long long)carry);
+    }
+}
+
 // ------------------------------------------------------- segment-sum + apply
 
 struct BwdArgs {
@@ -1045,7 +1108,8 @@ struct BwdLds {
     float wt[kSegSpan];         // pooling weight of each contributor, then each entry's sum
     union {                     // the keys are read only until the entries are built,
                                 // the pieces and the entries' segment starts only after:
-                                // sharing keeps a wave at 8 KB of LDS, five waves per SIMD
+                                // sharing keeps a wave at 8 KB of LDS (room for five waves
+                                // per SIMD; its registers allow four)
         uint32_t kw[kKeyWin];   // sorted keys x0 - 64 .. x0 + 383 (sentinels outside [0, nv))
         struct {
             float part[kWave][4];
@@ -2001,12 +2065,12 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
         const uint32_t *cst = reinterpret_cast<const uint32_t *>(ws + W.cstart);
         uint32_t *kc = from_keys ? kf : (kf == k0 ? k1 : k0);
         uint32_t *vc = from_keys ? vf : (vf == v0 ? v1 : v0);
+        // valid counts [C + 1], their prefix [C + 1] (written by col_sort's last column), a ticket
         uint32_t *vcnt = reinterpret_cast<uint32_t *>(ws + W.ccnt), *vbase = vcnt + plan->n_cols + 1;
         hipLaunchKernelGGL(col_sort, dim3((unsigned)plan->n_cols), dim3(kCSBlock), 0, st, k0, v0, k1, v1,
                            kc, vc, n, cst, plan->drow_base, plan->total_rows, misc,
                            from_keys ? nullptr : vcnt);
         if (!from_keys) {
-            hipLaunchKernelGGL(cs_vscan, dim3(1), dim3(kBlock), 0, st, vcnt, plan->n_cols, vbase);
             hipLaunchKernelGGL(cs_compact, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                                kc, vc, kf, vf, n, cst, plan->n_cols, vcnt, vbase);
         }
@@ -2047,6 +2111,13 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
             if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
             return EMB_OK;
         }
+    }
+    if (n <= kUqSmall) {
+        hipLaunchKernelGGL(uq_small, dim3(1), dim3(kBlock), 0, st, kf, n, plan->total_rows, misc, seg, ukeys,
+                           uniq_keys, n_uniq, stats);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(EMB_ERR_HIP, std::string("backward dedup launch: ") + hipGetErrorString(e));
+        return EMB_OK;
     }
     hipLaunchKernelGGL(uq_count, dim3((unsigned)ublk), dim3(kBlock), 0, st, kf, n, plan->total_rows, ucnt, misc);
     hipLaunchKernelGGL(uq_scan, dim3(1), dim3(kBlock), 0, st, ucnt, ublk, uscan, misc, n_uniq, stats);

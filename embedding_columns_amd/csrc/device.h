@@ -76,6 +76,10 @@ __device__ __forceinline__ int32_t ld_agent(const int32_t *p)
 {
     return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // wait until this wavefront's outstanding memory operations (stores included)
 // have completed, i.e. reached their coherence point
 __device__ __forceinline__ void wait_vm()

@@ -67,7 +67,8 @@ struct WsLayout {
     size_t bpart, bcnt, btick;                // backward split-segment partials and tickets
     size_t cstart;                            // first position of each column [C + 1] (forward -> backward)
     size_t bw, posid;                         // weighted forward -> backward: (bag, weight) and index per position
-    size_t ccnt;                              // column sort -> compaction: valid keys per column, their prefix [2 (C + 1)]
+    size_t ccnt;                              // column sort -> compaction: valid keys per column, their
+                                              //   prefix [2 (C + 1)], and the ticket of the last column
     size_t fstat;                             // forward counters, one 8-word record per tile
     size_t zrow;                              // 1 KB never written: stays zero (the workspace is
                                               //   zero-filled once); the plain forward's masked

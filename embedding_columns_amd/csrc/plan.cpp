@@ -126,7 +126,7 @@ void plan_layout(emb_plan &P)
     L.cstart = take(4 * ((size_t)P.n_cols + 1));
     L.bw = take(8 * N);
     L.posid = take(4 * N);
-    L.ccnt = take(4 * 2 * ((size_t)P.n_cols + 1));
+    L.ccnt = take(4 * (2 * ((size_t)P.n_cols + 1) + 1));
     L.fstat = take(4 * 8 * P.max_tiles);
     L.zrow = take(kZeroRow);
     L.pairs_n = (size_t)((N + 31) / 32 * 32);
