@@ -10,9 +10,9 @@
  *
  * Sources of the definitions (the web pages this library implements):
  *  - RECom explainer, "Why this problem is worth solving": an embedding column
- *    maps a raw feature to an index by hashing or bucketing, drops out-of-range
- *    indices, fills a default when the feature is missing, looks up table rows
- *    and reduces them to one vector; one column owns one table.
+ *    turns a raw feature into an index with a hash or a bucket, discards indices
+ *    outside its table, substitutes a default for a missing feature, gathers the
+ *    table rows and reduces them to one vector; each column has its own table.
  *  - RecIS, Sec. 3.2 "Index-aware segment reduction" and Algorithm 1: CSR
  *    offsets define segments; forward Y[s,:] = sum_r w_r E[i_r,:] over segment s,
  *    empty segments produce zero; backward dE[u] = sum over contributors r with
@@ -55,7 +55,7 @@ typedef enum {
     EMB_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } emb_status;
 
-/* column kinds: how a raw input becomes a row index (RECom: "by hashing or bucketing") */
+/* column kinds: how a raw input becomes a row index (RECom explainer: a hash or a bucket) */
 #define EMB_COL_HASH     0  /* ids int64; valid iff id_lo <= id < id_hi; row = splitmix64(id) mod rows */
 #define EMB_COL_IDENTITY 1  /* ids int64; valid iff 0 <= id < rows;      row = id                    */
 #define EMB_COL_BUCKET   2  /* fvals fp32; valid iff not NaN;            row = #{j : boundaries[j] <= x} */

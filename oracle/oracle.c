@@ -7,9 +7,9 @@
  * HIP library.
  *
  * What it computes (one embedding column = one table; RECom explainer, the
- * paragraph "Why this problem is worth solving": an index by hashing or
- * bucketing, out-of-range indices dropped, a default when the feature is
- * missing, rows looked up and reduced to one vector):
+ * paragraph "Why this problem is worth solving": the index comes from a hash or
+ * a bucket, out-of-range indices are dropped, a default stands in for a
+ * missing feature, and the rows are looked up and reduced to one vector):
  *
  *   transform  HASH      valid iff id_lo <= id < id_hi, row = splitmix64(id) mod rows
  *              IDENTITY  valid iff 0 <= id < rows,      row = id
