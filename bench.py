@@ -162,7 +162,7 @@ def run(args):
     else:
         weights, states = W.make_tables(w, seed=cfg, device=dev)
     plan = E.EmbeddingColumns(w.cols, weights, states, batch=w.batch, max_ids=max_ids, opt=w.opt,
-                              lr=w.lr, eps=w.eps, tile=args.tile, device=dev)
+                              lr=w.lr, eps=w.eps, tile=args.tile, fwd_tile=args.fwd_tile, device=dev)
     G = W.make_grad(w, seed=cfg, device=dev)
     stats = torch.zeros(E.STAT_COUNT, dtype=torch.int64, device=dev)
     Y = torch.empty(w.batch, w.sum_dim, dtype=torch.float32, device=dev)
@@ -419,7 +419,8 @@ def run(args):
                    "valid_lookups_per_step": int(lookups / args.steps),
                    "optimizer": ["emit", "sgd", "adagrad"][w.opt] if training else "none",
                    "backward": ("atomic" if args.atomic_backward else "sorted") if training else "none",
-                   "tile": plan.opts.tile or 256, "fwd_launches_per_step": 2 if pipe else 1,
+                   "tile": plan.opts.tile or 256, "fwd_tile": plan.forward_tile(batches[idx[0]].n),
+                   "fwd_launches_per_step": 2 if pipe else 1,
                    "pipelined_transform": bool(pipe),
                    "position_weights": bool(args.weights),
                    "hip_graph": bool(args.graph)},
@@ -541,7 +542,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; 5 keyed)")
     ap.add_argument("--workload", default="long-seq", choices=sorted(WORKLOADS))
     ap.add_argument("--batches", type=int, default=4)
-    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=0, help="positions per tile (0: 256)")
+    ap.add_argument("--fwd-tile", type=int, default=0,
+                    help="positions per forward tile (0: --tile if given, else chosen per batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true", help="collect the device counters while timing")
     ap.add_argument("--atomic-backward", action="store_true",

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "EmbError", "lib", "library_path", "ColumnDesc", "PlanOpts",
-    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_forward", "emb_forward_ex", "emb_transform", "emb_forward_rows",
+    "emb_plan_query", "emb_plan_create", "emb_plan_destroy", "emb_plan_forward_tile", "emb_forward", "emb_forward_ex", "emb_transform", "emb_forward_rows",
     "emb_forward_noalloc", "emb_stream_copy",
     "emb_backward",
     "emb_backward_dedup", "emb_backward_apply", "emb_backward_atomic",
@@ -60,7 +60,8 @@ class ColumnDesc(C.Structure):
 
 
 class PlanOpts(C.Structure):
-    _fields_ = [("opt", C.c_int32), ("lr", C.c_float), ("eps", C.c_float), ("tile", C.c_int32)]
+    _fields_ = [("opt", C.c_int32), ("lr", C.c_float), ("eps", C.c_float), ("tile", C.c_int32),
+                ("fwd_tile", C.c_int32)]
 
 
 class WorkspaceView(C.Structure):
@@ -75,6 +76,7 @@ _SIGS = {
     "emb_plan_create": [C.POINTER(ColumnDesc), _I32, _I32, _I64, C.POINTER(PlanOpts), _VP, _VP,
                         C.POINTER(_VP)],
     "emb_plan_destroy": [_VP],
+    "emb_plan_forward_tile": [_VP, _I64, C.POINTER(_I32)],
     "emb_forward": [_VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_forward_ex": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _I32, _VP, _VP],
     "emb_transform": [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP],
@@ -169,6 +171,12 @@ def emb_plan_create(descs, batch, max_ids, opts, plan_mem, stream=None):
 
 def emb_plan_destroy(plan):
     _check(lib().emb_plan_destroy(plan))
+
+
+def emb_plan_forward_tile(plan, n_ids):
+    t = _I32()
+    _check(lib().emb_plan_forward_tile(plan, n_ids, C.byref(t)))
+    return t.value
 
 
 def emb_forward(plan, offsets, ids, fvals, keyed_rows, n_ids, out, workspace, training,
@@ -322,7 +330,7 @@ class EmbeddingColumns:
     KEYED column, the table's row pool); states[c]: fp32 Adagrad accumulator."""
 
     def __init__(self, cols, weights, states=None, batch=1, max_ids=0, opt=OPT_EMIT, lr=0.0,
-                 eps=0.0, tile=0, device="cuda"):
+                 eps=0.0, tile=0, fwd_tile=0, device="cuda"):
         self.device = torch.device(device)
         self.batch, self.max_ids = int(batch), int(max_ids)
         self.cols = list(cols)
@@ -343,7 +351,7 @@ class EmbeddingColumns:
                                   _ptr(s) if s is not None else None, getattr(c, "seq_max", 0),
                                   getattr(c, "seq_keep_last", 0), getattr(c, "default_row", -1))
         self.descs = descs
-        self.opts = PlanOpts(opt, lr, eps, tile)
+        self.opts = PlanOpts(opt, lr, eps, tile, fwd_tile)
         self.sum_dim = sum(c.dim for c in self.cols)
         self.max_dim = max(c.dim for c in self.cols)
         pb, wb = emb_plan_query(descs, self.batch, self.max_ids, self.opts)
@@ -430,6 +438,10 @@ class EmbeddingColumns:
     def backward_atomic(self, grad_out):
         """SGD by atomic scatter of every contribution (no sort; not bit-reproducible)."""
         emb_backward_atomic(self.plan, grad_out.contiguous(), self.workspace)
+
+    def forward_tile(self, n_ids):
+        """Positions per forward tile for a batch of n_ids positions."""
+        return emb_plan_forward_tile(self.plan, n_ids)
 
     def workspace_view(self, n_ids):
         v = emb_plan_workspace_view(self.plan, self.workspace)

@@ -73,16 +73,22 @@ enum FwdMode { kFused = 0, kTransform = 1, kFromRows = 2 };
 constexpr int kFeatFilter = 1;    // truncation or a mask: positions are removed
 constexpr int kFeatWeights = 2;   // per-position weights or default rows
 // A bag of at most kShort positions is never cut by a tile boundary: the tile
-// holding its start finishes it (tiles span at most kTileMax + kShort - 1
-// positions).  Only longer bags are split and combined through the workspace.
+// holding its start finishes it (tiles span at most T + kShort - 1 positions).
+// Only longer bags are split and combined through the workspace.
 constexpr int kShort = 64;
-constexpr int kSpan = kTileMax + kShort;
 
+// One wavefront's LDS for tiles of up to TM positions.  The kernel exists for two
+// capacities: kTileMax, and kFwdTileMax for batches of long bags, where a longer
+// tile cuts fewer bags (fewer pieces through the workspace) at the price of fewer
+// waves per SIMD.
+template <int TM>
 struct WaveLds {
+    static constexpr int kSpan = TM + kShort;
+    static constexpr int kOff = TM + 128;   // offsets window: kMargin bags before, the tile's after
     int32_t rows[kSpan];             // transformed row of each tile position
     int32_t pbag[kSpan];             // bag of each tile position (training)
     float wt[kSpan];                 // weight of each tile position (extended forward)
-    int32_t off[kOffCap];            // window of CSR offsets
+    int32_t off[kOff];               // window of CSR offsets
     union {
         float part[kWave][8];        // per-lane partial sum of each run's first bag
         float bnd[kBndCap];          // bucket boundaries of the current column
@@ -99,7 +105,8 @@ struct TileCtx {
     int wb, wn;      // LDS window: offsets[wb .. wb+wn)
 };
 
-__device__ __forceinline__ int offat(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+template <class LT>
+__device__ __forceinline__ int offat(const FwdArgs &a, const LT &L, const TileCtx &t, int b)
 {
     const unsigned i = (unsigned)(b - t.wb);
     return i < (unsigned)t.wn ? L.off[i] : *gp(a.off + b);
@@ -109,16 +116,16 @@ __device__ __forceinline__ int offat(const FwdArgs &a, const WaveLds &L, const T
 // covers them all (W, the usual case) the walk reads LDS only: a global
 // fallback inside the walk makes the compiler wait for every outstanding load
 // and store before each lookup.
-template <bool W>
-__device__ __forceinline__ int offw(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+template <bool W, class LT>
+__device__ __forceinline__ int offw(const FwdArgs &a, const LT &L, const TileCtx &t, int b)
 {
     if (W) return L.off[b - t.wb];
     return offat(a, L, t, b);
 }
 
 // the non-empty bag containing position p (p inside the tile)
-template <bool W>
-__device__ __forceinline__ int bag_of(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int p)
+template <bool W, class LT>
+__device__ __forceinline__ int bag_of(const FwdArgs &a, const LT &L, const TileCtx &t, int p)
 {
     int lo = t.bf, hi = t.bl + 1;   // off[lo] <= p < off[hi]
     while (hi - lo > 1) {
@@ -129,8 +136,8 @@ __device__ __forceinline__ int bag_of(const FwdArgs &a, const WaveLds &L, const 
 }
 
 // the next non-empty bag after b (a later position exists)
-template <bool W>
-__device__ __forceinline__ int next_bag(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int b)
+template <bool W, class LT>
+__device__ __forceinline__ int next_bag(const FwdArgs &a, const LT &L, const TileCtx &t, int b)
 {
     int nb = b + 1;
     while (offw<W>(a, L, t, nb + 1) == offw<W>(a, L, t, nb)) nb++;
@@ -196,8 +203,8 @@ __device__ __forceinline__ void bag_out(const FwdArgs &a, const DevCol &col, int
 
 // a piece of a bag that crosses a tile boundary: publish it, and if this is the
 // last piece to arrive, sum all pieces in tile order and write the bag
-template <int V, bool W, bool EXT>
-__device__ __forceinline__ void tile_piece(const FwdArgs &a, const WaveLds &L, const TileCtx &t,
+template <int V, bool W, bool EXT, class LT>
+__device__ __forceinline__ void tile_piece(const FwdArgs &a, const LT &L, const TileCtx &t,
                                            const DevCol &col, int c, int side, int bag,
                                            const float (&sum)[V], int n, int leader, int q, bool qa,
                                            int32_t &zero_bags)
@@ -275,8 +282,8 @@ __device__ __forceinline__ void row_f32(const uint4 &v, float (&w)[8])
 // group pays its per-position work (row address, bag checks, counts) for twice
 // the elements.  Eight loads stay in flight per lane either way (with 8
 // elements, four in flight made the long-sequence forward 6 % slower).
-template <bool BF, bool W, bool EXT, int V>
-__device__ __forceinline__ void fwd_segment(const FwdArgs &a, WaveLds &L, const TileCtx &t,
+template <bool BF, bool W, bool EXT, int V, class LT>
+__device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileCtx &t,
                                             const DevCol &col, int c, int s0, int s1,
                                             int32_t &zero_bags)
 {
@@ -442,11 +449,11 @@ __device__ __forceinline__ int bucket_count(B b, int nb, float x)
 
 constexpr int kMargin = 64;             // offsets staged before the tile's first bag
 
-constexpr int kPL = kSpan / kWave;     // tile positions per lane: p0 + lane + 64 i
-
 // The raw inputs of the tile's positions, loaded once at the start of the tile so
 // that they arrive while the offsets are searched.
+template <int TM>
 struct TileIn {
+    static constexpr int kPL = WaveLds<TM>::kSpan / kWave;   // per lane: p0 + lane + 64 i
     int64_t id[kPL];
     float fv[kPL];
     int32_t kr[kPL];
@@ -455,7 +462,8 @@ struct TileIn {
 // Sequence truncation and masking remove raw positions before the transform
 // (RecIS Sec. 3.1 / Figure 2: SeqTrunc precedes Hash).  A removed position
 // becomes a dropped one (-1): no row, not counted in a mean, no gradient.
-__device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L,
+template <class LT>
+__device__ __forceinline__ bool position_kept(const FwdArgs &a, const LT &L,
                                               const TileCtx &t, const DevCol &col, int p)
 {
     bool keep = true;
@@ -471,11 +479,12 @@ __device__ __forceinline__ bool position_kept(const FwdArgs &a, const WaveLds &L
 
 // FEAT: the extended forward's parts this launch needs, kFeatFilter (truncation
 // or the mask) and kFeatWeights (per-position weights or default rows)
-template <int FEAT, int MODE>
-__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, const TileCtx &t,
+template <int FEAT, int MODE, int TM>
+__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds<TM> &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
-                                              const TileIn &in, int32_t (&cnt)[5])
+                                              const TileIn<TM> &in, int32_t (&cnt)[5])
 {
+    constexpr int kPL = TileIn<TM>::kPL;
     const int lane = lane_id();
     const int nbd = col.n_bnd;
     const bool staged = col.kind == EMB_COL_BUCKET && nbd <= kBndCap;
@@ -532,14 +541,16 @@ __device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds &L, cons
 // Positions of column c inside the tile.  The first column starts at or before
 // t0 and the last ends at or after t1; the other boundaries are bags bf+1 .. bl,
 // inside the LDS window when it covers the walk (win).
-__device__ __forceinline__ int col_lo(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int c,
+template <class LT>
+__device__ __forceinline__ int col_lo(const FwdArgs &a, const LT &L, const TileCtx &t, int c,
                                       int c_first, bool win)
 {
     if (c == c_first) return t.t0;
     return max(t.t0, win ? offw<true>(a, L, t, c * a.B) : offat(a, L, t, c * a.B));
 }
 
-__device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const TileCtx &t, int c,
+template <class LT>
+__device__ __forceinline__ int col_hi(const FwdArgs &a, const LT &L, const TileCtx &t, int c,
                                       int c_last, bool win)
 {
     if (c == c_last) return t.t1;
@@ -549,14 +560,17 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const WaveLds &L, const 
 // FEAT: the parts of the extended forward this launch needs (kFeatFilter: a
 // column truncates or the call has a mask; kFeatWeights: per-position weights or
 // a column with a default row), each a separate instance so that the plain
-// forward carries none of that code.  MODE: FwdMode.
-template <int FEAT, int MODE>
-__global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
+// forward carries none of that code.  MODE: FwdMode.  TM: the tile capacity, T <= TM
+// (the larger one holds more inputs per lane in registers: three waves per SIMD
+// instead of four).
+template <int FEAT, int MODE, int TM>
+__global__ __launch_bounds__(kTileBlock, TM > kTileMax ? 3 : 4) void fwd_kernel(FwdArgs a)
 {
     constexpr bool EXT = (FEAT & kFeatWeights) != 0;
-    __shared__ WaveLds lds[kTileWaves];
+    constexpr int kPL = TileIn<TM>::kPL, kOff = WaveLds<TM>::kOff;
+    __shared__ WaveLds<TM> lds[kTileWaves];
     const int w = threadIdx.x / kWave, lane = lane_id();
-    WaveLds &L = lds[w];
+    WaveLds<TM> &L = lds[w];
     TileCtx t;
     t.k = xcd_block(blockIdx.x, gridDim.x, 0) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
@@ -566,7 +580,7 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     const int x0 = (int)min<int64_t>(t.k * T, N), x1 = (int)min<int64_t>((t.k + 1) * T, N);
     t.p0 = x0;
     const bool last = t.k == a.ntiles - 1;
-    TileIn in;
+    TileIn<TM> in;
 #pragma unroll
     for (int i = 0; i < kPL; i++) {
         const int p = x0 + lane + kWave * i;
@@ -589,17 +603,17 @@ __global__ __launch_bounds__(kTileBlock, 4) void fwd_kernel(FwdArgs a)
     } else {
         t.wb = 0;
     }
-    t.wn = min(nbag + 1 - t.wb, kOffCap);
+    t.wn = min(nbag + 1 - t.wb, kOff);
     {
         // all window loads in flight at once
-        int o[kOffCap / kWave];
+        int o[kOff / kWave];
 #pragma unroll
-        for (int j = 0; j < kOffCap / kWave; j++) {
+        for (int j = 0; j < kOff / kWave; j++) {
             const int i = lane + kWave * j;
             o[j] = i < t.wn ? *gp(a.off + t.wb + i) : 0;
         }
 #pragma unroll
-        for (int j = 0; j < kOffCap / kWave; j++) {
+        for (int j = 0; j < kOff / kWave; j++) {
             const int i = lane + kWave * j;
             if (i < t.wn) L.off[i] = o[j];
         }
@@ -815,8 +829,12 @@ using namespace emb;
 template <int FEAT, int MODE>
 static void launch_one(int64_t blocks, const FwdArgs &a, void *stream)
 {
-    hipLaunchKernelGGL((fwd_kernel<FEAT, MODE>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                       static_cast<hipStream_t>(stream), a);
+    if (a.T > kTileMax)
+        hipLaunchKernelGGL((fwd_kernel<FEAT, MODE, kFwdTileMax>), dim3((unsigned)blocks), dim3(kTileBlock),
+                           0, static_cast<hipStream_t>(stream), a);
+    else
+        hipLaunchKernelGGL((fwd_kernel<FEAT, MODE, kTileMax>), dim3((unsigned)blocks), dim3(kTileBlock),
+                           0, static_cast<hipStream_t>(stream), a);
 }
 
 // sc: the split-bag partials and tickets of an inference call come from there
@@ -854,10 +872,10 @@ static emb_status forward_impl(int mode, emb_plan *plan, const int32_t *offsets,
     a.B = plan->batch;
     a.sumD = plan->sum_dim;
     a.maxD = plan->max_dim;
-    a.T = plan->tile;
+    a.T = fwd_tile_for(plan, n_ids);
     a.training = training ? 1 : 0;
     a.N = n_ids;
-    a.ntiles = std::max<int64_t>(1, (n_ids + plan->tile - 1) / plan->tile);
+    a.ntiles = std::max<int64_t>(1, (n_ids + a.T - 1) / a.T);
     a.off = offsets;
     a.ids = ids;
     a.fvals = fvals;
@@ -964,7 +982,8 @@ extern "C" emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, c
 namespace emb {
 size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout, void *base)
 {
-    const int64_t tiles = std::max<int64_t>(1, (n_ids + plan->tile - 1) / plan->tile);
+    const int32_t T = fwd_tile_for(plan, n_ids);
+    const int64_t tiles = std::max<int64_t>(1, (n_ids + T - 1) / T);
     auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t part = a256(sizeof(float) * 2 * (size_t)tiles * (size_t)plan->max_dim);
     const size_t pcnt = a256(sizeof(int32_t) * 2 * (size_t)tiles);

@@ -22,6 +22,12 @@ constexpr int kTileWaves = EMB_TILE_WAVES;
 constexpr int kTileBlock = kWave * kTileWaves;
 constexpr int kTileMax = 256;        // positions (or sorted contributors) per wavefront tile
 constexpr int kTileDefault = 256;
+constexpr int kFwdTileMax = 512;     // forward tiles of a batch of long bags (a second instance)
+constexpr int kLongBag = 64;         // mean positions per bag from which a batch counts as long
+// ... and the long tiles a batch must fill: twice the waves of that instance the
+// chip holds at once (3 per SIMD, 1024 SIMDs).  Fewer tiles leave SIMDs idle, and
+// there shorter tiles, more of them, finish sooner.
+constexpr int64_t kLongTilesMin = 2 * 3 * 1024;
 constexpr int kOffCap = kTileMax + 128;  // LDS window of segment offsets per wavefront
 constexpr int kBndCap = 256;             // bucket boundaries staged in LDS (more: read from memory)
 constexpr int kMaxDimF32 = 256;
@@ -85,6 +91,7 @@ struct emb_plan {
     int64_t max_ids = 0;
     int32_t sum_dim = 0, max_dim = 0;
     int32_t tile = emb::kTileDefault;
+    int32_t fwd_tile = 0;          // positions per forward tile; 0: chosen per batch (fwd_tile_for)
     int32_t opt = EMB_OPT_EMIT;
     float lr = 0.f, eps = 0.f;
     uint32_t total_rows = 0;       // sum of rows: keys >= this are sentinels
@@ -143,6 +150,11 @@ constexpr size_t kZeroRow = 1024;   // the widest row a lane group reads: 256 fp
 // bytes an inference forward of n_ids positions needs for them; with layout, the
 // regions placed from base (forward.hip)
 size_t fwd_scratch_bytes(const emb_plan *plan, int64_t n_ids, FwdScratch *layout, void *base);
+// Positions per forward tile for a batch of n_ids positions: the plan's fixed size,
+// else kFwdTileMax when the batch's mean bag has kLongBag positions or more (bags
+// are then cut by tiles; a longer tile cuts fewer) and the batch makes at least
+// kLongTilesMin such tiles, else the plan's tile.
+int32_t fwd_tile_for(const emb_plan *plan, int64_t n_ids);
 emb_status forward_with_scratch(emb_plan *plan, const int32_t *offsets, const int64_t *ids,
                                 const float *fvals, const int32_t *keyed_rows, int64_t n_ids,
                                 float *out, int64_t *stats, void *stream, const FwdScratch &sc);

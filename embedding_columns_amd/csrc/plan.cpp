@@ -50,6 +50,9 @@ emb_status plan_validate(const emb_column_desc *cols, int32_t n_cols, int32_t ba
         return fail(EMB_ERR_INVALID_ARG, "unknown optimizer");
     if (opts->tile != 0 && (opts->tile % kWave != 0 || opts->tile < kWave || opts->tile > kTileMax))
         return fail(EMB_ERR_INVALID_ARG, "tile must be 0 or a multiple of 64 in [64, 256]");
+    if (opts->fwd_tile != 0 &&
+        (opts->fwd_tile % kWave != 0 || opts->fwd_tile < kWave || opts->fwd_tile > kFwdTileMax))
+        return fail(EMB_ERR_INVALID_ARG, "fwd_tile must be 0 or a multiple of 64 in [64, 512]");
     if (opts->opt != EMB_OPT_EMIT && !(opts->lr >= 0.f && std::isfinite(opts->lr)))
         return fail(EMB_ERR_INVALID_ARG, "lr must be finite and >= 0");
     if (opts->opt == EMB_OPT_ADAGRAD && !(opts->eps >= 0.f && std::isfinite(opts->eps)))
@@ -99,7 +102,9 @@ void plan_layout(emb_plan &P)
     const int64_t nb = (int64_t)P.n_cols * P.batch;
     // sort entries: the positions, plus one per bag when a column has a default row
     const int64_t N = std::max<int64_t>(P.max_ids, 1) + (P.has_default ? nb : 0);
-    P.max_tiles = std::max<int64_t>(1, (N + P.tile - 1) / P.tile);
+    // the forward's tiles are never shorter than the backward's unless fixed so
+    const int64_t tmin = P.fwd_tile ? std::min(P.tile, P.fwd_tile) : P.tile;
+    P.max_tiles = std::max<int64_t>(1, (N + tmin - 1) / tmin);
     P.sort_blocks = std::max<int64_t>(1, (N + kSortTile - 1) / kSortTile);
     P.uq_blocks = std::max<int64_t>(1, (N + kUqTile - 1) / kUqTile);
     WsLayout &L = P.ws;
@@ -134,6 +139,14 @@ void plan_layout(emb_plan &P)
     L.total = o;
 }
 
+int32_t fwd_tile_for(const emb_plan *P, int64_t n_ids)
+{
+    if (P->fwd_tile) return P->fwd_tile;
+    const bool long_bags = n_ids >= (int64_t)kLongBag * P->n_cols * P->batch;
+    const bool many = n_ids >= (int64_t)kFwdTileMax * kLongTilesMin;
+    return long_bags && many ? kFwdTileMax : P->tile;
+}
+
 }  // namespace emb
 
 using namespace emb;
@@ -156,6 +169,8 @@ static emb_status fill_plan(const emb_column_desc *cols, int32_t n_cols, int32_t
     P.batch = batch;
     P.max_ids = max_ids;
     P.tile = opts->tile ? opts->tile : kTileDefault;
+    // a fixed tile fixes the forward's too, unless fwd_tile sets that apart
+    P.fwd_tile = opts->fwd_tile ? opts->fwd_tile : opts->tile;
     P.opt = opts->opt;
     P.lr = opts->lr;
     P.eps = opts->eps;
@@ -269,6 +284,14 @@ emb_status emb_plan_destroy(emb_plan *plan)
     delete[] plan->hcols;
     delete[] plan->hrow_base;
     delete plan;
+    return EMB_OK;
+}
+
+emb_status emb_plan_forward_tile(const emb_plan *plan, int64_t n_ids, int32_t *tile)
+{
+    if (!plan || !tile) return fail(EMB_ERR_INVALID_ARG, "NULL argument");
+    if (n_ids < 0 || n_ids > plan->max_ids) return fail(EMB_ERR_WORKSPACE, "n_ids exceeds the plan's max_ids");
+    *tile = fwd_tile_for(plan, n_ids);
     return EMB_OK;
 }
 

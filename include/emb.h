@@ -122,6 +122,11 @@ typedef struct emb_plan_opts {
     float lr;                  /* learning rate (SGD, ADAGRAD)                          */
     float eps;                 /* ADAGRAD epsilon, outside the square root              */
     int32_t tile;              /* positions per wavefront tile: 0 = default (256), else a multiple of 64 <= 256 */
+    int32_t fwd_tile;          /* positions per forward tile: 0 = `tile` when that is set, else chosen */
+                               /* per call: 512 when the batch has at least 64 positions per bag on   */
+                               /* average (long sequences: a longer tile cuts fewer bags into pieces) */
+                               /* and at least 512 x 6144 positions (tiles enough to fill the chip    */
+                               /* twice), 256 otherwise.  Else a multiple of 64 <= 512.               */
 } emb_plan_opts;
 
 typedef struct emb_plan emb_plan;    /* host object owned by the library */
@@ -141,6 +146,12 @@ emb_status emb_plan_create(const emb_column_desc *cols, int32_t n_cols, int32_t 
                            void *stream, emb_plan **out /* host */);
 
 emb_status emb_plan_destroy(emb_plan *plan);
+
+/* Positions per tile of the forward kernels for a batch of `n_ids` positions: the
+ * plan's fixed size, or the one it chooses for that batch (emb_plan_opts.fwd_tile).
+ * Host only.  The allocation-free forward's scratch grows with ceil(n_ids / tile).
+ * n_ids outside [0, max_ids]: EMB_ERR_WORKSPACE. */
+emb_status emb_plan_forward_tile(const emb_plan *plan, int64_t n_ids, int32_t *tile /* host */);
 
 /*
  * Forward of all columns in ONE kernel launch.
@@ -221,7 +232,7 @@ emb_status emb_forward_rows(emb_plan *plan, const int32_t *offsets, const int32_
  * live in a fixed 32 MiB array inside the library, one per GPU, held until the
  * process exits; the call allocates nothing.  A batch whose scratch would exceed
  * the array (1 KB plus about (8 max(dim) + 44) bytes per tile, tiles =
- * ceil(n_ids / tile)) returns EMB_ERR_WORKSPACE before anything is enqueued.  Each
+ * ceil(n_ids / forward tile)) returns EMB_ERR_WORKSPACE before anything is enqueued.  Each
  * call first clears the tickets it uses and a 1 KB zero row with a fill kernel on
  * `stream`.  All calls on one GPU share
  * its array: calls that overlap on one GPU (unordered streams) race; order them.

@@ -35,7 +35,7 @@ class Step:
     """One training (or inference) step of the HIP path."""
 
     def __init__(self, w: W.Workload, batch: W.Batch, weights, states, tile=0, device="cuda",
-                 keyed_rows=None, keyed_pool=None):
+                 keyed_rows=None, keyed_pool=None, fwd_tile=0):
         self.dev = torch.device(device)
         self.w, self.b = w, batch
         self.gw = []
@@ -47,7 +47,7 @@ class Step:
         self.gs = [None if s is None else s.to(self.dev).contiguous() for s in (states or [None] * len(w.cols))]
         self.cols = E.EmbeddingColumns(w.cols, self.gw, self.gs, batch=w.batch,
                                        max_ids=max(batch.n, 1), opt=w.opt, lr=w.lr, eps=w.eps,
-                                       tile=tile, device=self.dev)
+                                       tile=tile, fwd_tile=fwd_tile, device=self.dev)
         self.off = torch.from_numpy(batch.offsets).to(self.dev)
         self.ids = torch.from_numpy(batch.ids).to(self.dev) if batch.n else torch.zeros(1, dtype=torch.int64, device=self.dev)
         self.fv = torch.from_numpy(batch.fvals).to(self.dev) if batch.n else torch.zeros(1, dtype=torch.float32, device=self.dev)
@@ -189,19 +189,20 @@ def check_rows_adagrad(col, before, st_before, after_gpu, st_gpu, g_ref, gbound,
 
 
 def run_dense_case(w, seed, tile=0, training=True, device="cuda", check_bwd=True, ask_unique=True,
-                   mask_keep=None, weighted=False, split=False):
+                   mask_keep=None, weighted=False, split=False, fwd_tile=0):
     """Full parity of one step for HASH / IDENTITY / BUCKET workloads.  With
     ask_unique=False the backward returns nothing (the benchmark's path) and only
     the updated rows are compared.  mask_keep: run the masked forward with a
     random mask that keeps each position with this probability.  weighted: pass
     random per-position weights.  split: the forward as emb_transform followed by
-    emb_forward_rows, whose row codes must equal the oracle's bit for bit."""
+    emb_forward_rows, whose row codes must equal the oracle's bit for bit.  fwd_tile:
+    the forward's own tile size (0: as the plan chooses)."""
     b = W.make_batch(w, seed=seed)
     mask = None if mask_keep is None else W.make_mask(b.n, seed, mask_keep)
     pw = W.make_position_weights(b.n, seed) if weighted else None
     wts, sts = W.make_tables(w, seed=seed, device="cpu")
     G = W.make_grad(w, seed=seed, device="cpu")
-    st = Step(w, b, wts, sts, tile=tile, device=device)
+    st = Step(w, b, wts, sts, tile=tile, device=device, fwd_tile=fwd_tile)
     Y = st.forward(training=training, mask=mask, pweights=pw, split=split)
     ws = st.cols.workspace_view(max(b.n, 1)) if training else None
     ws = (ws[0][:b.n], ws[1][:b.n], ws[2]) if ws is not None else None

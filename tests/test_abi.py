@@ -50,10 +50,10 @@ def _col(L, **kw):
     return L.ColumnDesc(**d)
 
 
-def _query(L, cols, batch=8, max_ids=100, opt=0, lr=0.0, eps=0.0, tile=0):
+def _query(L, cols, batch=8, max_ids=100, opt=0, lr=0.0, eps=0.0, tile=0, fwd_tile=0):
     arr = (L.ColumnDesc * max(len(cols), 1))(*cols)
     pb, wb = C.c_size_t(), C.c_size_t()
-    s = L.lib().emb_plan_query(arr, len(cols), batch, max_ids, C.byref(L.PlanOpts(opt, lr, eps, tile)),
+    s = L.lib().emb_plan_query(arr, len(cols), batch, max_ids, C.byref(L.PlanOpts(opt, lr, eps, tile, fwd_tile)),
                                C.byref(pb), C.byref(wb))
     return s, pb.value, wb.value, L.emb_last_error()
 
@@ -94,6 +94,12 @@ def test_plan_query_rejects_bad_plans(L):
     assert _query(L, [_col(L)], batch=0)[0] == 1
     assert _query(L, [_col(L)], max_ids=-1)[0] == 2
     assert _query(L, [_col(L)], tile=100)[0] == 1
+    assert _query(L, [_col(L)], tile=512)[0] == 1                        # the backward's tiles <= 256
+    for ft in (32, 100, 576, -64):
+        s, _, _, err = _query(L, [_col(L)], fwd_tile=ft)
+        assert s == 1 and "fwd_tile" in err, ft
+    assert _query(L, [_col(L)], fwd_tile=512)[0] == 0
+    assert _query(L, [_col(L)], tile=64, fwd_tile=448)[0] == 0
     assert _query(L, [_col(L)], opt=2, lr=0.05, eps=1e-8)[0] == 1          # Adagrad without state
     assert _query(L, [_col(L, opt_state=8192)], opt=2, lr=0.05, eps=1e-8)[0] == 0
     big = [_col(L, rows=(1 << 31) - 1) for _ in range(3)]
@@ -105,6 +111,14 @@ def test_workspace_grows_with_batch(L):
     _, _, w1, _ = _query(L, [_col(L)], batch=8, max_ids=1000)
     _, _, w2, _ = _query(L, [_col(L)], batch=8, max_ids=100000)
     assert w2 > w1
+
+
+def test_workspace_holds_the_shorter_tiles(L):
+    # per-tile partials and tickets are sized for the shorter of the two tile sizes
+    _, _, w256, _ = _query(L, [_col(L)], batch=8, max_ids=100000)
+    _, _, w64, _ = _query(L, [_col(L)], batch=8, max_ids=100000, fwd_tile=64)
+    _, _, w512, _ = _query(L, [_col(L)], batch=8, max_ids=100000, fwd_tile=512)
+    assert w64 > w256 and w512 == w256
 
 
 def test_table_query_validation(L):
