@@ -48,7 +48,9 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool in)
     return act & ~(((uint64_t)mis_hi << 32) | mis_lo);
 }
 
-// exclusive scan of 256 values held one per thread; returns the total
+// exclusive scan of one value per thread over a workgroup of NW wavefronts;
+// returns the total
+template <int NW = kWavesPerBlock>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t &excl)
 {
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
@@ -62,7 +64,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     __syncthreads();
     uint32_t wpre = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kWavesPerBlock; i++) {
+    for (int i = 0; i < NW; i++) {
         const uint32_t s = tmp[i];
         wpre += (i < w) ? s : 0u;
         tot += s;
@@ -72,68 +74,79 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     return tot;
 }
 
-// exclusive scan of kRadix values, kDigitsPerThread consecutive ones per thread
-constexpr int kDigitsPerThread = kRadix / kBlock;
-static_assert(kRadix % kBlock == 0, "digits per thread");
-
-__device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[kDigitsPerThread],
-                                                         uint32_t (&ex)[kDigitsPerThread],
+// exclusive scan of kRadix values, DPT = kRadix / (64 NW) consecutive ones per
+// thread of a workgroup of NW wavefronts
+template <int NW, int DPT>
+__device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[DPT], uint32_t (&ex)[DPT],
                                                          uint32_t *tmp)
 {
+    static_assert(DPT * kWave * NW == kRadix, "digits per thread");
     uint32_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < kDigitsPerThread; i++) sum += v[i];
+    for (int i = 0; i < DPT; i++) sum += v[i];
     uint32_t base;
-    const uint32_t tot = block_exclusive_scan(sum, tmp, base);
+    const uint32_t tot = block_exclusive_scan<NW>(sum, tmp, base);
 #pragma unroll
-    for (int i = 0; i < kDigitsPerThread; i++) {
+    for (int i = 0; i < DPT; i++) {
         ex[i] = base;
         base += v[i];
     }
     return tot;
 }
 
+// The histogram kernel's workgroup: kHistItems keys per thread of one kSortTile tile.
+constexpr int kHistBlock = 512;
+constexpr int kHistItems = kSortTile / kHistBlock;
+static_assert(kHistItems % 4 == 0, "keys are loaded four (or two pairs) at a time");
+
 // digit histogram of one tile of kSortTile keys.  PI: the keys are the first
 // words of (key, value) pairs (the passes between the first and the last keep
 // the pairs together, so that a scattered digit run is one contiguous write
 // instead of two)
+//
+// ndev: the passes after a first pass that left keys out sort the *ndev keys it
+// kept.  excl: the first pass leaves out keys >= excl (dropped and default-row
+// sentinels when nothing needs them sorted), so the later passes move fewer.
 template <bool PI>
 __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
-                                          const uint2 *__restrict__ pin, int64_t n, int shift,
+                                          const uint2 *__restrict__ pin, int64_t n,
+                                          const uint32_t *__restrict__ ndev, uint32_t excl, int shift,
                                           uint32_t *__restrict__ hist, int64_t nblk,
                                           uint32_t *__restrict__ misc, int64_t tile, uint32_t *h)
 {
     // the first pass starts the count of valid contributors at n; the last
-    // pass lowers it to the position of the first sentinel key
+    // pass lowers it to the position of the first sentinel key (or the first
+    // pass's scatter sets it to the keys it kept)
     if (shift == 0 && tile == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
+    if (ndev) n = min<int64_t>(n, (int64_t)*gp(ndev));
     const int t = threadIdx.x, lane = lane_id();
-    for (int d = t; d < kRadix; d += kBlock) h[d] = 0;
+    for (int d = t; d < kRadix; d += kHistBlock) h[d] = 0;
     __syncthreads();
     const int64_t base = tile * kSortTile;
     // the tile's keys in 16-byte loads (4 keys, or 2 pairs, per load); a
     // histogram does not depend on which thread counts which key
-    uint32_t k[kSortItems];
-    bool kin[kSortItems];
+    uint32_t k[kHistItems];
+    bool kin[kHistItems];
     if (PI) {
 #pragma unroll
-        for (int i = 0; i < kSortItems / 2; i++) {
-            const int64_t idx = base + 2 * ((int64_t)i * kBlock + t);   // first of two pairs
+        for (int i = 0; i < kHistItems / 2; i++) {
+            const int64_t idx = base + 2 * ((int64_t)i * kHistBlock + t);   // first of two pairs
             const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(pin + idx)))
                                     : make_uint4(0u, 0u, 0u, 0u);
             k[2 * i] = v.x;
             k[2 * i + 1] = v.z;
-            kin[2 * i] = idx < n;
-            kin[2 * i + 1] = idx + 1 < n;
+            kin[2 * i] = idx < n && v.x < excl;
+            kin[2 * i + 1] = idx + 1 < n && v.z < excl;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kSortItems / 4; i++) {
-            const int64_t idx = base + 4 * ((int64_t)i * kBlock + t);
+        for (int i = 0; i < kHistItems / 4; i++) {
+            const int64_t idx = base + 4 * ((int64_t)i * kHistBlock + t);
             const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(keys + idx)))
                                     : make_uint4(0u, 0u, 0u, 0u);
             k[4 * i] = v.x; k[4 * i + 1] = v.y; k[4 * i + 2] = v.z; k[4 * i + 3] = v.w;
 #pragma unroll
-            for (int j = 0; j < 4; j++) kin[4 * i + j] = idx + j < n;
+            for (int j = 0; j < 4; j++) kin[4 * i + j] = idx + j < n && k[4 * i + j] < excl;
         }
     }
     // LDS atomics.  Skewed keys put most of a wavefront's lanes on one digit (the
@@ -142,7 +155,7 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
     // first remaining lane are counted with one atomic, twice over, and only the
     // lanes left after that add one each.
 #pragma unroll
-    for (int i = 0; i < kSortItems; i++) {
+    for (int i = 0; i < kHistItems; i++) {
         bool left = kin[i];
         const uint32_t d = (k[i] >> shift) & (kRadix - 1);
 #pragma unroll
@@ -158,7 +171,7 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
         if (left) atomicAdd(&h[d], 1u);
     }
     __syncthreads();
-    for (int d = t; d < kRadix; d += kBlock) hist[(int64_t)d * nblk + tile] = h[d];
+    for (int d = t; d < kRadix; d += kHistBlock) hist[(int64_t)d * nblk + tile] = h[d];
     __syncthreads();
 }
 
@@ -167,13 +180,14 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
 // two halves of a digit run cut by a line boundary then meet in one L2 instead
 // of reaching memory as partial lines from two XCDs.
 template <bool PI>
-__global__ __launch_bounds__(kBlock) void rs_hist(const uint32_t *__restrict__ keys,
+__global__ __launch_bounds__(kHistBlock) void rs_hist(const uint32_t *__restrict__ keys,
                                                  const uint2 *__restrict__ pin, int64_t n,
+                                                 const uint32_t *__restrict__ ndev, uint32_t excl,
                                                  int shift, uint32_t *__restrict__ hist,
                                                  int64_t nblk, uint32_t *__restrict__ misc)
 {
     __shared__ uint32_t h[kRadix];
-    hist_tile<PI>(keys, pin, n, shift, hist, nblk, misc, xcd_block(blockIdx.x, gridDim.x, 0), h);
+    hist_tile<PI>(keys, pin, n, ndev, excl, shift, hist, nblk, misc, xcd_block(blockIdx.x, gridDim.x, 0), h);
 }
 
 // exclusive scan of one digit's block counts hist[d][0..nblk) in place, total ->
@@ -229,12 +243,18 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, i
     if (t == 0) dtot[blockIdx.x] = carry;
 }
 
+// The scatter kernel's workgroup: kScatWaves wavefronts over one kSortTile tile.
+constexpr int kScatWaves = 4;
+constexpr int kScatBlock = kWave * kScatWaves;
+constexpr int kScatItems = kSortTile / kScatBlock;     // keys per lane
+constexpr int kScatDigits = kRadix / kScatBlock;       // digits per thread in the offset scans
+
 struct SortLds {
     uint32_t skey[kSortTile];
     uint32_t sval[kSortTile];
-    uint16_t run[kWavesPerBlock][kRadix];   // per-wave running digit counts (<= 4096)
+    uint16_t run[kScatWaves][kRadix];       // per-wave running digit counts (<= 4096)
     uint32_t gdst[kRadix];                  // global destination of digit d's run minus its LDS start
-    uint32_t tmp[kWavesPerBlock];
+    uint32_t tmp[kScatWaves];
 };
 
 // PI / PO: the input / output is (key, value) pairs instead of two arrays
@@ -243,24 +263,30 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
                                              const uint32_t *__restrict__ vin,
                                              uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
                                              const uint2 *__restrict__ pin, uint2 *__restrict__ pout,
-                                             int64_t n, int shift, const uint32_t *__restrict__ hist,
+                                             int64_t n, const uint32_t *__restrict__ ndev, uint32_t excl,
+                                             uint32_t *__restrict__ nkept, int shift,
+                                             const uint32_t *__restrict__ hist,
                                              const uint32_t *__restrict__ dtot, int64_t nblk,
                                              uint32_t sentinel, uint32_t *__restrict__ misc,
                                              int64_t tile, SortLds &S)
 {
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int64_t base = tile * kSortTile;
+    if (ndev) n = min<int64_t>(n, (int64_t)*gp(ndev));
     const int cnt = (int)min<int64_t>(kSortTile, n - base);
+    if (cnt <= 0) return;                     // past the keys an excluding first pass kept
 
-    // each wavefront owns 1024 consecutive keys: item j of lane l is wave*1024 + j*64 + l,
-    // so (wave, j, lane) order is index order and the ranking below is stable.
+    // each wavefront owns W = kSortTile / kScatWaves consecutive keys: item j of lane l
+    // is wave*W + j*64 + l, so (wave, j, lane) order is index order and the ranking
+    // below is stable.
     // All loads are issued first: the barriers and fences below would otherwise
     // hold each load behind the previous step.
-    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    uint32_t key[kScatItems], val[kScatItems], rank[kScatItems];
+    bool inc[kScatItems];                     // loaded and not left out
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int j = 0; j < kSortItems; j++) {
-        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
+    for (int j = 0; j < kScatItems; j++) {
+        const int li = w * (kSortTile / kScatWaves) + j * kWave + lane;
         const bool in = li < cnt;
         if (PI) {
             const uint2 pr = in ? static_cast<uint2>(*gp(pin + base + li)) : make_uint2(0u, 0u);
@@ -270,28 +296,32 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
             key[j] = in ? *gp(kin + base + li) : 0u;
             val[j] = in ? *gp(vin + base + li) : 0u;
         }
+        inc[j] = in;
     }
+#pragma unroll
+    for (int j = 0; j < kScatItems; j++) inc[j] = inc[j] && key[j] < excl;
 
     // digit offsets: global prefix over digits + this block's offset within each
-    // digit (kept by the thread that owns digits t * kDigitsPerThread + i)
-    uint32_t gbase[kDigitsPerThread];
+    // digit (kept by the thread that owns digits t * kScatDigits + i)
+    uint32_t gbase[kScatDigits];
     {
-        uint32_t v[kDigitsPerThread];
+        uint32_t v[kScatDigits];
 #pragma unroll
-        for (int i = 0; i < kDigitsPerThread; i++) v[i] = dtot[t * kDigitsPerThread + i];
-        digit_exclusive_scan(v, gbase, S.tmp);
+        for (int i = 0; i < kScatDigits; i++) v[i] = dtot[t * kScatDigits + i];
+        const uint32_t kept = digit_exclusive_scan<kScatWaves>(v, gbase, S.tmp);
+        // an excluding first pass: the keys kept are the later passes' count
+        if (nkept && tile == 0 && t == 0) *gp(nkept) = kept;
 #pragma unroll
-        for (int i = 0; i < kDigitsPerThread; i++)
-            gbase[i] += hist[(int64_t)(t * kDigitsPerThread + i) * nblk + tile];
-        for (int d = t; d < kRadix; d += kBlock)
-            for (int i = 0; i < kWavesPerBlock; i++) S.run[i][d] = 0;
+        for (int i = 0; i < kScatDigits; i++)
+            gbase[i] += hist[(int64_t)(t * kScatDigits + i) * nblk + tile];
+        for (int d = t; d < kRadix; d += kScatBlock)
+            for (int i = 0; i < kScatWaves; i++) S.run[i][d] = 0;
     }
     __syncthreads();
 
 #pragma unroll
-    for (int j = 0; j < kSortItems; j++) {
-        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
-        const bool in = li < cnt;
+    for (int j = 0; j < kScatItems; j++) {
+        const bool in = inc[j];
         const uint32_t d = (key[j] >> shift) & (kRadix - 1);
         const uint64_t peers = match_digit(d, in);
         const uint32_t before = S.run[w][d];
@@ -303,32 +333,32 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
     }
     __syncthreads();
     // block-local digit histogram -> local prefix; per-wave offsets inside each digit
+    int nloc;                                  // keys of this tile that are sorted
     {
-        uint32_t tot[kDigitsPerThread], lex[kDigitsPerThread], woff[kDigitsPerThread][kWavesPerBlock];
+        uint32_t tot[kScatDigits], lex[kScatDigits], woff[kScatDigits][kScatWaves];
 #pragma unroll
-        for (int i = 0; i < kDigitsPerThread; i++) {
-            const int d = t * kDigitsPerThread + i;
+        for (int i = 0; i < kScatDigits; i++) {
+            const int d = t * kScatDigits + i;
             tot[i] = 0;
 #pragma unroll
-            for (int k = 0; k < kWavesPerBlock; k++) {
+            for (int k = 0; k < kScatWaves; k++) {
                 woff[i][k] = tot[i];
                 tot[i] += S.run[k][d];
             }
         }
-        digit_exclusive_scan(tot, lex, S.tmp);
+        nloc = (int)digit_exclusive_scan<kScatWaves>(tot, lex, S.tmp);
 #pragma unroll
-        for (int i = 0; i < kDigitsPerThread; i++) {
-            const int d = t * kDigitsPerThread + i;
+        for (int i = 0; i < kScatDigits; i++) {
+            const int d = t * kScatDigits + i;
             S.gdst[d] = gbase[i] - lex[i];      // wraps; gdst + LDS position is the destination
 #pragma unroll
-            for (int k = 0; k < kWavesPerBlock; k++) S.run[k][d] = (uint16_t)(lex[i] + woff[i][k]);
+            for (int k = 0; k < kScatWaves; k++) S.run[k][d] = (uint16_t)(lex[i] + woff[i][k]);
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSortItems; j++) {
-        const int li = w * (kSortTile / kWavesPerBlock) + j * kWave + lane;
-        if (li < cnt) {
+    for (int j = 0; j < kScatItems; j++) {
+        if (inc[j]) {
             const uint32_t d = (key[j] >> shift) & (kRadix - 1);
             const uint32_t lp = S.run[w][d] + rank[j];
             S.skey[lp] = key[j];
@@ -338,7 +368,7 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
     __syncthreads();
     // write each digit run contiguously
     uint32_t first_sentinel = 0xFFFFFFFFu;
-    for (int lp = t; lp < cnt; lp += kBlock) {
+    for (int lp = t; lp < nloc; lp += kScatBlock) {
         const uint32_t k = S.skey[lp];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = S.gdst[d] + (uint32_t)lp;
@@ -360,18 +390,21 @@ __device__ __forceinline__ void scatter_tile(const uint32_t *__restrict__ kin,
 }
 
 template <bool PI, bool PO>
-__global__ __launch_bounds__(kBlock) void rs_scatter(const uint32_t *__restrict__ kin,
+__global__ __launch_bounds__(kScatBlock) void rs_scatter(const uint32_t *__restrict__ kin,
                                                     const uint32_t *__restrict__ vin,
                                                     uint32_t *__restrict__ kout,
                                                     uint32_t *__restrict__ vout,
                                                     const uint2 *__restrict__ pin,
                                                     uint2 *__restrict__ pout, int64_t n,
-                                                    int shift, const uint32_t *__restrict__ hist,
+                                                    const uint32_t *__restrict__ ndev, uint32_t excl,
+                                                    uint32_t *__restrict__ nkept, int shift,
+                                                    const uint32_t *__restrict__ hist,
                                                     const uint32_t *__restrict__ dtot, int64_t nblk,
                                                     uint32_t sentinel, uint32_t *__restrict__ misc)
 {
     __shared__ SortLds S;
-    scatter_tile<PI, PO>(kin, vin, kout, vout, pin, pout, n, shift, hist, dtot, nblk, sentinel, misc,
+    scatter_tile<PI, PO>(kin, vin, kout, vout, pin, pout, n, ndev, excl, nkept, shift, hist, dtot, nblk,
+                         sentinel, misc,
                          xcd_block(blockIdx.x, gridDim.x, 0), S);
 }
 
@@ -2083,28 +2116,41 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
         // pairs together in two ping-pong buffers
         uint2 *pairs[2] = {reinterpret_cast<uint2 *>(ws + W.pairs),
                            reinterpret_cast<uint2 *>(ws + W.pairs) + (W.pairs_n)};
-        const dim3 grid((unsigned)nblk), block(kBlock);
+        const dim3 grid((unsigned)nblk);
+        // Segments found from the keys need only the valid keys sorted: the first
+        // pass leaves out the dropped and default-row sentinels and the later
+        // passes sort the keys it kept (their count, in misc[0], is the apply's).
+        const bool excl = from_keys;
         for (int p = 0; p < passes; p++) {
             const int shift = p * kRadixBits;
             const bool pi = p > 0, po = p < passes - 1;
             const uint2 *pin = pi ? pairs[(p - 1) & 1] : nullptr;
             uint2 *pout = po ? pairs[p & 1] : nullptr;
-            uint32_t *lm = (from_keys && p == passes - 1) ? misc : nullptr;
-            if (pi) hipLaunchKernelGGL(rs_hist<true>, grid, block, 0, st, nullptr, pin, n, shift, hist, nblk, misc);
-            else hipLaunchKernelGGL(rs_hist<false>, grid, block, 0, st, k0, nullptr, n, shift, hist, nblk, misc);
+            uint32_t *lm = (from_keys && !excl && p == passes - 1) ? misc : nullptr;
+            const uint32_t *ndev = (excl && p > 0) ? misc : nullptr;
+            const uint32_t lim = (excl && p == 0) ? plan->total_rows : 0xFFFFFFFFu;
+            uint32_t *nkept = (excl && p == 0) ? misc : nullptr;
+            if (pi) hipLaunchKernelGGL(rs_hist<true>, grid, dim3(kHistBlock), 0, st, nullptr, pin, n, ndev, lim,
+                                       shift, hist, nblk, misc);
+            else hipLaunchKernelGGL(rs_hist<false>, grid, dim3(kHistBlock), 0, st, k0, nullptr, n, ndev, lim,
+                                    shift, hist, nblk, misc);
             hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
             if (pi && po)
-                hipLaunchKernelGGL((rs_scatter<true, true>), grid, block, 0, st, nullptr, nullptr, nullptr,
-                                   nullptr, pin, pout, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+                hipLaunchKernelGGL((rs_scatter<true, true>), grid, dim3(kScatBlock), 0, st, nullptr, nullptr,
+                                   nullptr, nullptr, pin, pout, n, ndev, lim, nkept, shift, hist, dtot, nblk,
+                                   plan->total_rows, lm);
             else if (pi)
-                hipLaunchKernelGGL((rs_scatter<true, false>), grid, block, 0, st, nullptr, nullptr, kf, vf,
-                                   pin, nullptr, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+                hipLaunchKernelGGL((rs_scatter<true, false>), grid, dim3(kScatBlock), 0, st, nullptr, nullptr,
+                                   kf, vf, pin, nullptr, n, ndev, lim, nkept, shift, hist, dtot, nblk,
+                                   plan->total_rows, lm);
             else if (po)
-                hipLaunchKernelGGL((rs_scatter<false, true>), grid, block, 0, st, k0, v0, nullptr, nullptr,
-                                   nullptr, pout, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+                hipLaunchKernelGGL((rs_scatter<false, true>), grid, dim3(kScatBlock), 0, st, k0, v0, nullptr,
+                                   nullptr, nullptr, pout, n, ndev, lim, nkept, shift, hist, dtot, nblk,
+                                   plan->total_rows, lm);
             else
-                hipLaunchKernelGGL((rs_scatter<false, false>), grid, block, 0, st, k0, v0, kf, vf, nullptr,
-                                   nullptr, n, shift, hist, dtot, nblk, plan->total_rows, lm);
+                hipLaunchKernelGGL((rs_scatter<false, false>), grid, dim3(kScatBlock), 0, st, k0, v0, kf, vf,
+                                   nullptr, nullptr, n, ndev, lim, nkept, shift, hist, dtot, nblk,
+                                   plan->total_rows, lm);
         }
         if (from_keys) {
             hipError_t e = hipGetLastError();
