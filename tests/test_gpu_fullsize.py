@@ -2,10 +2,11 @@
 (default tile; the benchmark's first batch, tables, upstream gradient and
 prepopulated keyed table, from the same seeds).
 
-The CPU oracle is fast enough to recompute every pooled output and every
-touched row of the training front end; for the long-sequence workload the
-Adagrad rows are checked on a seeded sample of touched and untouched rows, and
-the keyed workload runs one step on the full prepopulated table."""
+The CPU oracle recomputes every pooled output and every touched row: the
+training front end's SGD rows, all of the long sequences' touched Adagrad rows
+and accumulators (a seeded sample of untouched rows must stay bit-identical),
+and every row the keyed workload's step updated, on the full prepopulated
+table."""
 import numpy as np
 import pytest
 import torch
@@ -76,7 +77,7 @@ def test_many_tiny_columns_full():
     check_forward(w, b, r["Y"], None, ref, training=False)
 
 
-def test_long_sequences_full_sampled_rows():
+def test_long_sequences_full():
     w = W.config(4)
     b = W.make_batch(w, seed=4000)
     wts, sts = W.make_tables(w, seed=4, device=DEV)
@@ -89,26 +90,22 @@ def test_long_sequences_full_sampled_rows():
     check_forward(w, b, r["Y"], r["ws"], ref)
     ucol, urow, ug, ub = oracle.backward(oc, w.batch, b.offsets, to_np(G), b.ids, b.fvals,
                                          opt=w.opt, lr=w.lr, eps=w.eps)
-    assert int(r["nu"].item()) == ucol.size
+    check_unique(w, r["ukeys"], r["nu"], ucol, urow)
     rng = np.random.default_rng(44)
     for c, col in enumerate(w.cols):
         sel = np.flatnonzero(ucol == c)
-        pick = rng.choice(sel, size=min(4000, sel.size), replace=False)
-        # the hottest rows (many contributors, pieces from many tiles) are always checked
-        hot = sel[np.argsort(-ub[sel][:, 0])[:64]]
-        pick = np.unique(np.concatenate([pick, hot]))
-        rows = urow[pick]
+        rows = urow[sel]
         gw = to_np(wts[c][torch.from_numpy(rows).to(DEV)])
         gs = to_np(sts[c][torch.from_numpy(rows).to(DEV)])
-        # compare the sampled rows as a small table whose touched set is all of them
+        # every touched row and accumulator, compared as a table whose rows are all touched
         sub = W.Column(col.kind, col.pool, col.dtype, rows.size, col.dim)
-        check_rows_adagrad(sub, host_w[c][rows], host_s[c][rows], gw, gs, ug[pick][:, :col.dim],
-                           ub[pick][:, :col.dim], np.arange(rows.size), w.lr, w.eps)
+        check_rows_adagrad(sub, host_w[c][rows], host_s[c][rows], gw, gs, ug[sel][:, :col.dim],
+                           ub[sel][:, :col.dim], np.arange(rows.size), w.lr, w.eps)
         # a sample of untouched rows stays bit-identical
         touched = np.zeros(col.rows, bool)
-        touched[urow[sel]] = True
-        r_ = rng.integers(0, col.rows, 20000)
-        un = np.unique(r_[~touched[r_]])[:5000]
+        touched[rows] = True
+        r_ = rng.integers(0, col.rows, 200000)
+        un = np.unique(r_[~touched[r_]])
         assert np.array_equal(to_np(wts[c][torch.from_numpy(un).to(DEV)]), host_w[c][un])
         assert np.array_equal(to_np(sts[c][torch.from_numpy(un).to(DEV)]), host_s[c][un])
 
@@ -153,9 +150,8 @@ def test_keyed_table_full_one_step():
     assert np.unique(pairs[0]).size == pairs.shape[1] == np.unique(pairs[1]).size
     err = np.abs(to_np(Y).astype(np.float64) - Yr)
     assert np.all(err <= RTOL_F32 * Yb), "pooled outputs differ"
-    # updated rows of a sample of the step's admitted keys, found by key
-    rng = np.random.default_rng(55)
-    pick = np.sort(rng.choice(urow.size, size=min(5000, urow.size), replace=False))
+    # every updated row, found by its key
+    pick = np.arange(urow.size)
     sk = pool_keys[urow[pick]]
     grow, gcnt = T.find(torch.from_numpy(sk).to(DEV))
     grow = to_np(grow)
