@@ -84,6 +84,7 @@ constexpr int kShort = 64;
 template <int TM>
 struct WaveLds {
     static constexpr int kSpan = TM + kShort;
+    static_assert(kSpan >= 8, "the walk's row reads run up to 7 entries past rows[] into pbag[]");
     static constexpr int kOff = TM + 128;   // offsets window: kMargin bags before, the tile's after
     int32_t rows[kSpan];             // transformed row of each tile position
     int32_t pbag[kSpan];             // bag of each tile position (training)
@@ -320,9 +321,13 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileC
             // row 0), so that the single wait below covers exactly these loads
             int r[U];
             RowRaw<BF, V> h[U];
+            // unconditional LDS reads from one base (immediate offsets): a read past
+            // the run's end (at most U - 1 past the tile span) stays inside the wave's
+            // LDS (pbag follows rows) and its value is replaced below
+            const int32_t *rp = L.rows + (p - t.t0);
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const int x = L.rows[min(p + u, ge - 1) - t.t0];   // unconditional LDS reads
+                const int x = rp[u];
                 r[u] = (p + u < ge) ? x : -1;
             }
 #pragma unroll
