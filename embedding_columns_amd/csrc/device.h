@@ -222,6 +222,36 @@ __device__ __forceinline__ void landed(float v)
     asm volatile("" ::"v"(v) : "memory");
 }
 
+// Structured buffer loads (the buffer_load "idxen offen" form): the address is
+// base + index * stride + offset, formed by the load itself, and an index at or
+// past the descriptor's record count reads zeros without touching memory.  The
+// compiler has builtins for the raw form only, so the intrinsic is named
+// directly.  Flags word: a 32-bit data format, as gfx9 buffer loads need.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+__device__ i32x4_t struct_buffer_load_x4(__amdgpu_buffer_rsrc_t rsrc, int32_t vindex, int32_t voffset,
+                                         int32_t soffset, int32_t aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+__device__ i32x2_t struct_buffer_load_x2(__amdgpu_buffer_rsrc_t rsrc, int32_t vindex, int32_t voffset,
+                                         int32_t soffset, int32_t aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+constexpr int32_t kBufFlags = 0x00020000;
+constexpr int kBufStrideMax = 16383;          // the descriptor's 14-bit stride field
+
+// A descriptor over `rows` records of `stride` bytes at `base`; the arguments
+// are the same in every lane, and are read from the first so that the
+// descriptor sits in scalar registers (a descriptor the compiler must assume
+// to vary is looped over lane by lane at every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *base, int stride, int32_t rows)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)__builtin_amdgcn_readfirstlane(stride),
+                                             __builtin_amdgcn_readfirstlane(rows), kBufFlags);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

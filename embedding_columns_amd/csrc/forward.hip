@@ -81,14 +81,14 @@ constexpr int kShort = 64;
 // capacities: kTileMax, and kFwdTileMax for batches of long bags, where a longer
 // tile cuts fewer bags (fewer pieces through the workspace) at the price of fewer
 // waves per SIMD.
-template <int TM>
+template <int TM, bool WT>
 struct WaveLds {
     static constexpr int kSpan = TM + kShort;
     static_assert(kSpan >= 8, "the walk's row reads run up to 7 entries past rows[] into pbag[]");
     static constexpr int kOff = TM + 128;   // offsets window: kMargin bags before, the tile's after
     int32_t rows[kSpan];             // transformed row of each tile position
     int32_t pbag[kSpan];             // bag of each tile position (training)
-    float wt[kSpan];                 // weight of each tile position (extended forward)
+    float wt[WT ? kSpan : 1];        // weight of each tile position (weighted instances)
     int32_t off[kOff];               // window of CSR offsets
     union {
         float part[kWave][8];        // per-lane partial sum of each run's first bag
@@ -277,16 +277,40 @@ __device__ __forceinline__ void row_f32(const uint4 &v, float (&w)[8])
     w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
 }
 
+// one lane's slice of row r through a structured buffer descriptor over the
+// table (r outside the table's rows: zeros)
+template <bool BF, int V> __device__ __forceinline__ RowRaw<BF, V> row_load(__amdgpu_buffer_rsrc_t rs, int r, int off);
+template <> __device__ __forceinline__ float4 row_load<false, 4>(__amdgpu_buffer_rsrc_t rs, int r, int off)
+{
+    const i32x4_t v = struct_buffer_load_x4(rs, r, off, 0, 0);
+    return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z), __int_as_float(v.w));
+}
+template <> __device__ __forceinline__ uint4 row_load<true, 8>(__amdgpu_buffer_rsrc_t rs, int r, int off)
+{
+    const i32x4_t v = struct_buffer_load_x4(rs, r, off, 0, 0);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+template <> __device__ __forceinline__ uint2 row_load<true, 4>(__amdgpu_buffer_rsrc_t rs, int r, int off)
+{
+    const i32x2_t v = struct_buffer_load_x2(rs, r, off, 0, 0);
+    return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+
 // one column segment [s0, s1) of the tile.  A row is read by P lanes (a power
 // of two), V elements per lane: 16-byte loads for fp32 rows (BF false, V = 4),
 // 8-byte (V = 4) or 16-byte (V = 8) loads for bf16.  With 8 elements a lane
 // group pays its per-position work (row address, bag checks, counts) for twice
 // the elements.  Eight loads stay in flight per lane either way (with 8
-// elements, four in flight made the long-sequence forward 6 % slower).
-template <bool BF, bool W, bool EXT, int V, class LT>
-__device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileCtx &t,
-                                            const DevCol &col, int c, int s0, int s1,
-                                            int32_t &zero_bags)
+// elements, four in flight made the long-sequence forward 6 % slower, and
+// twelve gained nothing).
+// SB: tables below 4 GB are read through a structured buffer descriptor (row
+// index and lane offset go to the load as they are, and the dropped and default
+// codes, negative, fall outside the descriptor's rows and read zeros); larger
+// tables form each 64-bit row address in the loop.
+template <bool BF, bool W, bool EXT, int V, bool SB, class LT>
+__device__ __forceinline__ void fwd_walk(const FwdArgs &a, LT &L, const TileCtx &t,
+                                         const DevCol &col, int c, int s0, int s1,
+                                         int32_t &zero_bags)
 {
     constexpr int U = 8;                       // row loads in flight per lane
     constexpr int esz = BF ? 2 : 4;
@@ -302,9 +326,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileC
     const char *wptr = static_cast<const char *>(col.weights);
     // without per-position weights, positions that add nothing (dropped, DEFAULT,
     // past the run) read zeros instead of row 0, so every loaded slice is added
-    // as it is (no select per element); with weights they read row 0 and the sum
-    // selects, since a weight may be infinite
+    // as it is (no select per element); with weights the sum still selects, since
+    // a weight may be infinite (those positions read zeros through the buffer
+    // descriptor, row 0 otherwise)
     const int64_t rstride = (int64_t)D * esz;
+    const __amdgpu_buffer_rsrc_t rsrc = row_buffer(col.weights, SB ? (int)rstride : 0,
+                                                   SB ? (int32_t)col.rows : 0);
 
     float acc[V], hacc[V];
 #pragma unroll
@@ -331,10 +358,12 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileC
                 r[u] = (p + u < ge) ? x : -1;
             }
 #pragma unroll
-            for (int u = 0; u < U; u++)
-                h[u] = *gp(reinterpret_cast<const RowRaw<BF, V> *>(
-                    ((!EXT && r[u] < 0) ? a.zrow : wptr) + loff +
-                    (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
+            for (int u = 0; u < U; u++) {
+                if (SB) h[u] = row_load<BF, V>(rsrc, r[u], (int)loff);
+                else h[u] = *gp(reinterpret_cast<const RowRaw<BF, V> *>(
+                         ((!EXT && r[u] < 0) ? a.zrow : wptr) + loff +
+                         (uint64_t)(uint32_t)max(r[u], 0) * (uint32_t)rstride));
+            }
 #pragma unroll
             for (int u = 0; u < U; u++) landed(h[u]);   // before the bag-end stores below
 #pragma unroll
@@ -441,6 +470,18 @@ __device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileC
     wave_sync();
 }
 
+template <bool BF, bool W, bool EXT, int V, class LT>
+__device__ __forceinline__ void fwd_segment(const FwdArgs &a, LT &L, const TileCtx &t,
+                                            const DevCol &col, int c, int s0, int s1,
+                                            int32_t &zero_bags)
+{
+    const uint64_t bytes = (uint64_t)col.rows * (uint64_t)(col.dim * (BF ? 2 : 4));
+    if (bytes <= 0xFFFFFFFFull && col.rows <= INT32_MAX && col.dim * (BF ? 2 : 4) <= kBufStrideMax)
+        fwd_walk<BF, W, EXT, V, true>(a, L, t, col, c, s0, s1, zero_bags);
+    else
+        fwd_walk<BF, W, EXT, V, false>(a, L, t, col, c, s0, s1, zero_bags);
+}
+
 // #{j : b[j] <= x} for sorted b, by binary lifting (B is an LDS or a global array)
 template <typename B>
 __device__ __forceinline__ int bucket_count(B b, int nb, float x)
@@ -458,7 +499,7 @@ constexpr int kMargin = 64;             // offsets staged before the tile's firs
 // that they arrive while the offsets are searched.
 template <int TM>
 struct TileIn {
-    static constexpr int kPL = WaveLds<TM>::kSpan / kWave;   // per lane: p0 + lane + 64 i
+    static constexpr int kPL = (TM + kShort) / kWave;   // per lane: p0 + lane + 64 i
     int64_t id[kPL];
     float fv[kPL];
     int32_t kr[kPL];
@@ -484,8 +525,8 @@ __device__ __forceinline__ bool position_kept(const FwdArgs &a, const LT &L,
 
 // FEAT: the extended forward's parts this launch needs, kFeatFilter (truncation
 // or the mask) and kFeatWeights (per-position weights or default rows)
-template <int FEAT, int MODE, int TM>
-__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds<TM> &L, const TileCtx &t,
+template <int FEAT, int MODE, int TM, bool WT>
+__device__ __forceinline__ void fwd_transform(const FwdArgs &a, WaveLds<TM, WT> &L, const TileCtx &t,
                                               const DevCol &col, int s0, int s1,
                                               const TileIn<TM> &in, int32_t (&cnt)[5])
 {
@@ -567,15 +608,18 @@ __device__ __forceinline__ int col_hi(const FwdArgs &a, const LT &L, const TileC
 // a column with a default row), each a separate instance so that the plain
 // forward carries none of that code.  MODE: FwdMode.  TM: the tile capacity, T <= TM
 // (the larger one holds more inputs per lane in registers: three waves per SIMD
-// instead of four).
+// instead of four; four waves at the larger capacity spill in every tile's set-up:
+// long sequences 234 against 208 us).  Only the weighted instances keep per-position
+// weights in LDS.
 template <int FEAT, int MODE, int TM>
 __global__ __launch_bounds__(kTileBlock, TM > kTileMax ? 3 : 4) void fwd_kernel(FwdArgs a)
 {
     constexpr bool EXT = (FEAT & kFeatWeights) != 0;
-    constexpr int kPL = TileIn<TM>::kPL, kOff = WaveLds<TM>::kOff;
-    __shared__ WaveLds<TM> lds[kTileWaves];
+    using Lds = WaveLds<TM, EXT>;
+    constexpr int kPL = TileIn<TM>::kPL, kOff = Lds::kOff;
+    __shared__ Lds lds[kTileWaves];
     const int w = threadIdx.x / kWave, lane = lane_id();
-    WaveLds<TM> &L = lds[w];
+    Lds &L = lds[w];
     TileCtx t;
     t.k = xcd_block(blockIdx.x, gridDim.x, 0) * kTileWaves + w;
     if (t.k >= a.ntiles) return;
