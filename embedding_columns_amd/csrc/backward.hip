@@ -94,10 +94,15 @@ __device__ __forceinline__ uint32_t digit_exclusive_scan(const uint32_t (&v)[DPT
     return tot;
 }
 
-// The histogram kernel's workgroup: kHistItems keys per thread of one kSortTile tile.
+// The histogram kernel's workgroup: HB threads, kSortTile / HB keys each, for one
+// kSortTile tile.  512 threads in general; 1024 when every tile's workgroup is
+// resident at once (at most 512 tiles: each workgroup is then the whole kernel's
+// time, and fewer keys per thread shorten it).  Long sequences, 2,184 tiles: 512
+// threads 180.8 us of dedup, 1024 190.5 us; the keyed step's 200 tiles: 62.7 ->
+// 60.0 us with 1024.
 constexpr int kHistBlock = 512;
-constexpr int kHistItems = kSortTile / kHistBlock;
-static_assert(kHistItems % 4 == 0, "keys are loaded four (or two pairs) at a time");
+constexpr int kHistBlockSmall = 1024;
+constexpr int64_t kHistSmallTiles = 512;
 
 // digit histogram of one tile of kSortTile keys.  PI: the keys are the first
 // words of (key, value) pairs (the passes between the first and the last keep
@@ -107,7 +112,7 @@ static_assert(kHistItems % 4 == 0, "keys are loaded four (or two pairs) at a tim
 // ndev: the passes after a first pass that left keys out sort the *ndev keys it
 // kept.  excl: the first pass leaves out keys >= excl (dropped and default-row
 // sentinels when nothing needs them sorted), so the later passes move fewer.
-template <bool PI>
+template <bool PI, int HB>
 __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
                                           const uint2 *__restrict__ pin, int64_t n,
                                           const uint32_t *__restrict__ ndev, uint32_t excl, int shift,
@@ -119,18 +124,20 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
     // pass's scatter sets it to the keys it kept)
     if (shift == 0 && tile == 0 && threadIdx.x == 0) *gp(misc) = (uint32_t)n;
     if (ndev) n = min<int64_t>(n, (int64_t)*gp(ndev));
+    constexpr int kItems = kSortTile / HB;
+    static_assert(kItems % 4 == 0, "keys are loaded four (or two pairs) at a time");
     const int t = threadIdx.x, lane = lane_id();
-    for (int d = t; d < kRadix; d += kHistBlock) h[d] = 0;
+    for (int d = t; d < kRadix; d += HB) h[d] = 0;
     __syncthreads();
     const int64_t base = tile * kSortTile;
     // the tile's keys in 16-byte loads (4 keys, or 2 pairs, per load); a
     // histogram does not depend on which thread counts which key
-    uint32_t k[kHistItems];
-    bool kin[kHistItems];
+    uint32_t k[kItems];
+    bool kin[kItems];
     if (PI) {
 #pragma unroll
-        for (int i = 0; i < kHistItems / 2; i++) {
-            const int64_t idx = base + 2 * ((int64_t)i * kHistBlock + t);   // first of two pairs
+        for (int i = 0; i < kItems / 2; i++) {
+            const int64_t idx = base + 2 * ((int64_t)i * HB + t);   // first of two pairs
             const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(pin + idx)))
                                     : make_uint4(0u, 0u, 0u, 0u);
             k[2 * i] = v.x;
@@ -140,8 +147,8 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kHistItems / 4; i++) {
-            const int64_t idx = base + 4 * ((int64_t)i * kHistBlock + t);
+        for (int i = 0; i < kItems / 4; i++) {
+            const int64_t idx = base + 4 * ((int64_t)i * HB + t);
             const uint4 v = idx < n ? static_cast<uint4>(*gp(reinterpret_cast<const uint4 *>(keys + idx)))
                                     : make_uint4(0u, 0u, 0u, 0u);
             k[4 * i] = v.x; k[4 * i + 1] = v.y; k[4 * i + 2] = v.z; k[4 * i + 3] = v.w;
@@ -155,7 +162,7 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
     // first remaining lane are counted with one atomic, twice over, and only the
     // lanes left after that add one each.
 #pragma unroll
-    for (int i = 0; i < kHistItems; i++) {
+    for (int i = 0; i < kItems; i++) {
         bool left = kin[i];
         const uint32_t d = (k[i] >> shift) & (kRadix - 1);
 #pragma unroll
@@ -171,7 +178,7 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
         if (left) atomicAdd(&h[d], 1u);
     }
     __syncthreads();
-    for (int d = t; d < kRadix; d += kHistBlock) hist[(int64_t)d * nblk + tile] = h[d];
+    for (int d = t; d < kRadix; d += HB) hist[(int64_t)d * nblk + tile] = h[d];
     __syncthreads();
 }
 
@@ -179,15 +186,15 @@ __device__ __forceinline__ void hist_tile(const uint32_t *__restrict__ keys,
 // histogram words of neighbouring tiles (hist[d][b], hist[d][b + 1]) and the
 // two halves of a digit run cut by a line boundary then meet in one L2 instead
 // of reaching memory as partial lines from two XCDs.
-template <bool PI>
-__global__ __launch_bounds__(kHistBlock) void rs_hist(const uint32_t *__restrict__ keys,
+template <bool PI, int HB>
+__global__ __launch_bounds__(HB) void rs_hist(const uint32_t *__restrict__ keys,
                                                  const uint2 *__restrict__ pin, int64_t n,
                                                  const uint32_t *__restrict__ ndev, uint32_t excl,
                                                  int shift, uint32_t *__restrict__ hist,
                                                  int64_t nblk, uint32_t *__restrict__ misc)
 {
     __shared__ uint32_t h[kRadix];
-    hist_tile<PI>(keys, pin, n, ndev, excl, shift, hist, nblk, misc, xcd_block(blockIdx.x, gridDim.x, 0), h);
+    hist_tile<PI, HB>(keys, pin, n, ndev, excl, shift, hist, nblk, misc, xcd_block(blockIdx.x, gridDim.x, 0), h);
 }
 
 // exclusive scan of one digit's block counts hist[d][0..nblk) in place, total ->
@@ -2130,10 +2137,17 @@ extern "C" emb_status emb_backward_dedup(emb_plan *plan, void *workspace, uint32
             const uint32_t *ndev = (excl && p > 0) ? misc : nullptr;
             const uint32_t lim = (excl && p == 0) ? plan->total_rows : 0xFFFFFFFFu;
             uint32_t *nkept = (excl && p == 0) ? misc : nullptr;
-            if (pi) hipLaunchKernelGGL(rs_hist<true>, grid, dim3(kHistBlock), 0, st, nullptr, pin, n, ndev, lim,
-                                       shift, hist, nblk, misc);
-            else hipLaunchKernelGGL(rs_hist<false>, grid, dim3(kHistBlock), 0, st, k0, nullptr, n, ndev, lim,
-                                    shift, hist, nblk, misc);
+            if (nblk <= kHistSmallTiles) {
+                if (pi) hipLaunchKernelGGL((rs_hist<true, kHistBlockSmall>), grid, dim3(kHistBlockSmall), 0, st,
+                                           nullptr, pin, n, ndev, lim, shift, hist, nblk, misc);
+                else hipLaunchKernelGGL((rs_hist<false, kHistBlockSmall>), grid, dim3(kHistBlockSmall), 0, st,
+                                        k0, nullptr, n, ndev, lim, shift, hist, nblk, misc);
+            } else {
+                if (pi) hipLaunchKernelGGL((rs_hist<true, kHistBlock>), grid, dim3(kHistBlock), 0, st, nullptr,
+                                           pin, n, ndev, lim, shift, hist, nblk, misc);
+                else hipLaunchKernelGGL((rs_hist<false, kHistBlock>), grid, dim3(kHistBlock), 0, st, k0, nullptr,
+                                        n, ndev, lim, shift, hist, nblk, misc);
+            }
             hipLaunchKernelGGL(rs_scan, dim3(kRadix), dim3(kBlock), 0, st, hist, nblk, dtot);
             if (pi && po)
                 hipLaunchKernelGGL((rs_scatter<true, true>), grid, dim3(kScatBlock), 0, st, nullptr, nullptr,
